@@ -1,0 +1,208 @@
+/*
+ * CPU oracle for the decode path of Lookahead Sparse Attention (LSA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark do.  It shares no code with the HIP library.
+ *
+ * Each function is the plain definition of one step, in exact integers or in
+ * IEEE double, with no blocking, fusion or reordering beyond the definition:
+ *
+ *  1. Indexer logits: the dot product of the indexer query with each chunk's
+ *     compressed indexer key ("FlashMemory-DeepSeek-V4 ... Lookahead Sparse
+ *     Attention", paperlayer.ai summary, 2 Methodology / 2.1 Architecture and
+ *     3 Experiments / Limitations, which name a dot-product interaction; the
+ *     Korean review, 1. Key Terms & Definitions, "Neural Memory Indexer").
+ *     Exact in int64.
+ *  2. Indexer score: a sigmoid of the logit (same 2.1 Architecture bullet and
+ *     the review's definition).  The argument is alpha*logit formed as one
+ *     IEEE single-precision product, then 1/(1+exp(-x)) in double.
+ *  3. Chunk selection: a fixed budget of k chunks, the first k of the order
+ *     "key descending, then chunk index ascending", returned in ascending
+ *     chunk order.  Written as a rank count: chunk c is kept iff fewer than k
+ *     chunks precede it in that order.
+ *  4. Gathered GQA decode attention: softmax(q K^T / sqrt(d_k)) V over the
+ *     tokens of the kept chunks (sergiiob.dev handbook "DeepSeek-V4:
+ *     Architecting for Ultra-Long Contexts", section "Grouped Query Attention
+ *     (GQA) vs. Multi-Head Attention (MHA)", the attention formula; the same
+ *     section: 64 query heads share 8 KV heads, every 8 consecutive query
+ *     heads one KV head).  bf16 inputs widened exactly to double; every sum
+ *     in double; tokens at or past the request's context length are left out.
+ *  5. Host-tier fetch: a byte copy of each selected chunk into its pool slot
+ *     (paperlayer.ai summary, 2.1 Architecture: non-recalled entries are
+ *     evicted to CPU; 3 Experiments / Experimental Setup: recalled chunks are
+ *     retrieved from CPU cold storage every tau = 64 steps).
+ *
+ * Layouts (row-major):
+ *   q_idx  int8   [B][nq][d_idx]        K_idx int8 [B][C][d_idx]
+ *   logits int64  [B*nq][C]             ids   int32 [B][k]
+ *   q      bf16   [B][Hq][d]            kv    bf16 [B][C_store][2][Hkv][T][d]
+ *   out    double [B][Hq][d]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* 1. logits[b*nq + r][c] = sum_i q_idx[b][r][i] * K_idx[b][c][i]  (exact). */
+void oracle_index_logits(const int8_t* q_idx, const int8_t* k_idx, int64_t B, int64_t nq, int64_t C,
+                         int64_t d_idx, int64_t* logits) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c)
+            for (int64_t r = 0; r < nq; ++r) {
+                const int8_t* qv = q_idx + (b * nq + r) * d_idx;
+                const int8_t* kv = k_idx + (b * C + c) * d_idx;
+                int64_t acc = 0;
+                for (int64_t i = 0; i < d_idx; ++i) acc += (int64_t)qv[i] * (int64_t)kv[i];
+                logits[(b * nq + r) * C + c] = acc;
+            }
+}
+
+/* 2. scores[j] = 1 / (1 + exp(-x)),  x = alpha * (float)logit in IEEE fp32. */
+void oracle_index_scores(const int64_t* logits, int64_t n, float alpha, double* scores) {
+    for (int64_t j = 0; j < n; ++j) {
+        volatile float xl = (float)logits[j];
+        volatile float x = alpha * xl; /* one single-precision product */
+        scores[j] = 1.0 / (1.0 + exp(-(double)x));
+    }
+}
+
+/* 3. Budgeted selection.  Chunk c precedes chunk c' when key[c] > key[c'],
+ *    or key[c] == key[c'] and c < c'.  Chunk c is kept iff
+ *    #{c' : c' precedes c} < k.  Ids are written in ascending order.
+ *    Returns 0, or -1 if k is out of [1, C]. */
+int oracle_topk_i64(const int64_t* keys, int64_t R, int64_t C, int64_t k, int32_t* ids) {
+    if (k < 1 || k > C) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t* row = keys + r * C;
+        int64_t n_out = 0;
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t before = 0;
+            for (int64_t c2 = 0; c2 < C; ++c2)
+                if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;
+            if (before < k) ids[r * k + n_out++] = (int32_t)c;
+        }
+        if (n_out != k) return -2; /* cannot happen: the order is total */
+    }
+    return 0;
+}
+
+/* Same rule on double keys (used to compare selection by score with
+ * selection by logit). */
+int oracle_topk_f64(const double* keys, int64_t R, int64_t C, int64_t k, int32_t* ids) {
+    if (k < 1 || k > C) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        const double* row = keys + r * C;
+        int64_t n_out = 0;
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t before = 0;
+            for (int64_t c2 = 0; c2 < C; ++c2)
+                if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;
+            if (before < k) ids[r * k + n_out++] = (int32_t)c;
+        }
+        if (n_out != k) return -2;
+    }
+    return 0;
+}
+
+/* 4. Gathered GQA decode attention.
+ *    For request b and query head h (KV head g = h / (Hq/Hkv)), the tokens
+ *    are those of the listed chunks: list entry j names chunk chunk_ids[b][j]
+ *    stored at position slots[b][j] of the store (slots == NULL: the chunk's
+ *    own index); token t of that chunk is at context position
+ *    chunk_ids[b][j]*T + t and is used iff that position < ctx_len[b].
+ *      z  = (q[b][h] . K[token]) * sm_scale
+ *      w  = exp(z - max z)
+ *      out[b][h] = sum_token w * V[token] / sum_token w
+ *    If `weights` is not NULL it receives the normalised softmax weight of
+ *    every (list entry, token) pair, [B][Hq][k*T], 0 for unused tokens.
+ *    Returns 0, -1 on bad arguments, -3 if a request has no usable token. */
+int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                         const int32_t* slots, const int32_t* ctx_len, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || k < 1 || T < 1) return -1;
+    const int64_t group = Hq / Hkv;
+    const int64_t tile = T * d;              /* one (K|V, head) tile        */
+    const int64_t chunk = 2 * Hkv * tile;    /* one chunk, K and V, all heads */
+    int status = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / group;
+            const uint16_t* qh = q + (b * Hq + h) * d;
+            double* z = (double*)malloc(sizeof(double) * (size_t)(k * T));
+            unsigned char* use = (unsigned char*)malloc((size_t)(k * T));
+            double m = -INFINITY;
+            int64_t n_used = 0;
+            for (int64_t j = 0; j < k; ++j) {
+                const int64_t c = chunk_ids[b * k + j];
+                const int64_t p = slots ? slots[b * k + j] : c;
+                const uint16_t* K = kv + (b * C_store + p) * chunk + (0 * Hkv + g) * tile;
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t e = j * T + t;
+                    use[e] = (c * T + t) < (int64_t)ctx_len[b];
+                    z[e] = 0.0;
+                    if (!use[e]) continue;
+                    double dot = 0.0;
+                    for (int64_t i = 0; i < d; ++i) dot += bf16_to_double(qh[i]) * bf16_to_double(K[t * d + i]);
+                    z[e] = dot * sm_scale;
+                    if (z[e] > m) m = z[e];
+                    ++n_used;
+                }
+            }
+            double* o = out + (b * Hq + h) * d;
+            for (int64_t i = 0; i < d; ++i) o[i] = 0.0;
+            if (n_used == 0) {
+#pragma omp atomic write
+                status = -3;
+            } else {
+                double l = 0.0;
+                for (int64_t e = 0; e < k * T; ++e) {
+                    if (!use[e]) continue;
+                    z[e] = exp(z[e] - m); /* z now holds the unnormalised weight */
+                    l += z[e];
+                }
+                for (int64_t j = 0; j < k; ++j) {
+                    const int64_t c = chunk_ids[b * k + j];
+                    const int64_t p = slots ? slots[b * k + j] : c;
+                    const uint16_t* V = kv + (b * C_store + p) * chunk + (1 * Hkv + g) * tile;
+                    for (int64_t t = 0; t < T; ++t) {
+                        const int64_t e = j * T + t;
+                        if (!use[e]) continue;
+                        for (int64_t i = 0; i < d; ++i) o[i] += z[e] * bf16_to_double(V[t * d + i]);
+                    }
+                }
+                for (int64_t i = 0; i < d; ++i) o[i] /= l;
+                if (weights) {
+                    double* wrow = weights + (b * Hq + h) * k * T;
+                    for (int64_t e = 0; e < k * T; ++e) wrow[e] = use[e] ? z[e] / l : 0.0;
+                }
+            }
+            free(z);
+            free(use);
+        }
+    return status;
+}
+
+/* 5. Host-tier fetch: pool[b][slots[b][j]] := host[b][chunk_ids[b][j]]
+ *    (whole chunk: K and V of every KV head).  slots == NULL means slot j. */
+int oracle_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* chunk_ids, const int32_t* slots,
+                        uint16_t* pool_kv, int64_t P, int64_t B, int64_t Hkv, int64_t d, int64_t k, int64_t T) {
+    const int64_t chunk = 2 * Hkv * T * d;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < k; ++j) {
+            const int64_t c = chunk_ids[b * k + j];
+            const int64_t p = slots ? slots[b * k + j] : j;
+            if (c < 0 || c >= C || p < 0 || p >= P) return -1;
+            memcpy(pool_kv + (b * P + p) * chunk, host_kv + (b * C + c) * chunk, sizeof(uint16_t) * (size_t)chunk);
+        }
+    return 0;
+}

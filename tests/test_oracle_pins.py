@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against things other than itself: brute force on
+tiny inputs, library routines (numpy integer matmul, scipy's expit, torch's
+dense scaled-dot-product attention in float64), closed forms worked out by hand
+(tests/golden/closed_forms.json) and invariants of the definitions."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def bf16(x):
+    """float array -> bf16 bits (round to nearest even); test inputs only."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def f32(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_store(K, V, Hkv=1, T=64):
+    """Tokens [n][d] of one request/head -> kv store [1][C][2][Hkv][T][d]."""
+    K = np.asarray(K, dtype=np.float32)
+    V = np.asarray(V, dtype=np.float32)
+    n, d = K.shape
+    C = (n + T - 1) // T
+    kv = np.zeros((1, C, 2, Hkv, T, d), dtype=np.uint16)
+    for j in range(n):
+        c, t = divmod(j, T)
+        for g in range(Hkv):
+            kv[0, c, 0, g, t] = bf16(K[j])
+            kv[0, c, 1, g, t] = bf16(V[j])
+    return kv
+
+
+# ---------------------------------------------------------------- indexer
+
+def test_logits_closed_form(oracle_lib):
+    g = _golden("closed_forms.json")["indexer_logits"]
+    q = np.array(g["q"], dtype=np.int8).reshape(1, 1, -1)
+    K = np.array(g["keys"], dtype=np.int8).reshape(1, len(g["keys"]), -1)
+    assert oracle_lib.index_logits(q, K)[0].tolist() == g["expected"]
+
+
+def test_logits_extreme_fits_int32(oracle_lib):
+    g = _golden("closed_forms.json")["indexer_logits_extreme"]
+    q = np.full((1, 1, g["d_idx"]), g["q_value"], dtype=np.int8)
+    K = np.full((1, 3, g["d_idx"]), g["key_value"], dtype=np.int8)
+    K[0, 1] = 127
+    out = oracle_lib.index_logits(q, K)[0]
+    assert out[0] == g["expected"] == 2 ** 21
+    assert out[1] == -128 * 127 * 128
+    assert out[2] == g["expected"]
+
+
+def test_logits_vs_numpy_integer_matmul(oracle_lib, synth_lib):
+    q = synth_lib.uniform_i8((3, 2, 128), 11, synth_lib.stream(synth_lib.TAG_MISC, 1), -128, 127)
+    K = synth_lib.uniform_i8((3, 50, 128), 11, synth_lib.stream(synth_lib.TAG_MISC, 2), -128, 127)
+    ref = np.einsum("brd,bcd->brc", q.astype(np.int64), K.astype(np.int64)).reshape(6, 50)
+    assert np.array_equal(oracle_lib.index_logits(q, K), ref)
+
+
+def test_logits_golden_key_closed_form(oracle_lib, synth_lib):
+    """A key equal to 8*sign(q) scores exactly 8*sum|q|."""
+    q = synth_lib.uniform_i8((2, 1, 64), 5, synth_lib.stream(synth_lib.TAG_MISC, 3), -16, 15)
+    K = (8 * np.sign(q.astype(np.int32))).astype(np.int8)  # [2][1][64] -> one chunk each
+    out = oracle_lib.index_logits(q, K)
+    assert out[:, 0].tolist() == [8 * int(np.abs(q[b, 0].astype(np.int64)).sum()) for b in range(2)]
+
+
+def test_scores_closed_form_and_expit(oracle_lib):
+    from scipy.special import expit
+    g = _golden("closed_forms.json")["sigmoid"]
+    logits = np.array([c["logit"] for c in g["cases"]], dtype=np.int64)
+    s = oracle_lib.index_scores(logits, g["alpha"])
+    assert s[0] == 0.5
+    for got, c in zip(s, g["cases"]):
+        assert abs(got - c["expected"]) <= 1e-15
+    # against scipy's logistic on the same fp32 argument, over a wide range
+    L = np.arange(-200000, 200001, 37, dtype=np.int64)
+    alpha = 2.0 ** -11
+    x = (np.float32(alpha) * L.astype(np.float32)).astype(np.float64)
+    np.testing.assert_allclose(oracle_lib.index_scores(L, alpha), expit(x), rtol=1e-14, atol=0)
+    # symmetry sigma(x) + sigma(-x) = 1
+    np.testing.assert_allclose(oracle_lib.index_scores(L, alpha) + oracle_lib.index_scores(-L, alpha), 1.0,
+                               rtol=0, atol=1e-15)
+
+
+def test_scores_argument_is_fp32_product(oracle_lib):
+    """A non-power-of-two alpha: the argument is rounded to fp32 before the sigmoid."""
+    alpha = 0.1
+    L = np.array([3, 7, 1234567], dtype=np.int64)
+    x32 = (np.float32(alpha) * L.astype(np.float32)).astype(np.float64)
+    want = 1.0 / (1.0 + np.exp(-x32))
+    assert np.array_equal(oracle_lib.index_scores(L, alpha), want)
+
+
+# ---------------------------------------------------------------- selection
+
+def brute_topk(row, k):
+    order = sorted(range(len(row)), key=lambda c: (-row[c], c))
+    return sorted(order[:k])
+
+
+def test_topk_closed_form(oracle_lib):
+    g = _golden("closed_forms.json")["topk"]
+    L = np.array([g["logits"]], dtype=np.int64)
+    for c in g["cases"]:
+        assert oracle_lib.topk_chunks(L, c["k"])[0].tolist() == c["expected"]
+
+
+@pytest.mark.parametrize("kind", ["random", "equal", "two_valued", "few_values", "descending"])
+def test_topk_vs_brute_force(oracle_lib, synth_lib, kind):
+    """T1: the rank-count selection equals a full sort on tiny inputs."""
+    for C in (1, 2, 3, 7, 16, 33, 64):
+        if kind == "random":
+            row = synth_lib.uniform_i32((C,), 1, synth_lib.stream(synth_lib.TAG_MISC, 10 + C), -1000, 1000)
+        elif kind == "equal":
+            row = np.full(C, 42, dtype=np.int32)
+        elif kind == "two_valued":
+            row = synth_lib.uniform_i32((C,), 2, synth_lib.stream(synth_lib.TAG_MISC, 100 + C), 0, 1) * 5 - 2
+        elif kind == "few_values":
+            row = synth_lib.uniform_i32((C,), 3, synth_lib.stream(synth_lib.TAG_MISC, 200 + C), -2, 2)
+        else:
+            row = np.arange(C, 0, -1, dtype=np.int32)
+        for k in sorted({1, C, max(1, C // 2), max(1, C - 1)}):
+            got = oracle_lib.topk_chunks(row.reshape(1, -1).astype(np.int64), k)[0].tolist()
+            assert got == brute_topk(row.tolist(), k), (kind, C, k)
+
+
+def test_topk_rejects_bad_k(oracle_lib):
+    L = np.zeros((1, 4), dtype=np.int64)
+    for k in (0, 5, -1):
+        with pytest.raises(ValueError):
+            oracle_lib.topk_chunks(L, k)
+
+
+def test_selection_by_score_equals_selection_by_logit(oracle_lib, synth_lib):
+    """T4: sigmoid is monotone, so selecting on sigma(alpha*l) picks the same
+    chunks as selecting on l; in the workloads' argument range distinct
+    logits give distinct fp64 scores, so ties are the same ties."""
+    from synth import workloads as W
+    for name in ("tiny", "32k", "128k"):
+        w = W.WORKLOADS[name]
+        K = W.indexer_keys(w)
+        for it in range(w.intervals if w.drift else 1):
+            q = W.indexer_query(w, it)
+            L = oracle_lib.index_logits(q, K)
+            S = oracle_lib.index_scores(L, w.alpha)
+            assert np.abs(L).max() * w.alpha <= 12.0
+            ids_l = oracle_lib.topk_chunks(L, w.k)
+            ids_s = oracle_lib.topk_chunks(S, w.k)
+            assert np.array_equal(ids_l, ids_s), (name, it)
+            for r in range(L.shape[0]):
+                u_l = np.unique(L[r])
+                u_s = np.unique(S[r])
+                assert u_l.size == u_s.size  # distinct logits -> distinct scores
+
+
+# ---------------------------------------------------------------- attention
+
+def _attend_one(oracle_lib, case, Hkv=1):
+    d = case["d"]
+    kv = make_store(case["K"], case["V"], Hkv=Hkv)
+    q = bf16(np.array(case["q"], dtype=np.float32)).reshape(1, 1, d)
+    ids = np.array([[0]], dtype=np.int32)
+    return oracle_lib.gather_attend(q, kv, ids, np.array([case["ctx_len"]]), Hkv, case["scale"])
+
+
+def test_attention_closed_forms(oracle_lib):
+    for case in _golden("closed_forms.json")["attention"]["cases"]:
+        out = _attend_one(oracle_lib, case)
+        np.testing.assert_allclose(out[0, 0], case["expected"], rtol=0, atol=1e-14, err_msg=case["name"])
+
+
+def test_attention_masks_tokens_past_context(oracle_lib):
+    """Tokens at or past ctx_len must not count, whatever they hold."""
+    case = _golden("closed_forms.json")["attention"]["cases"][0]
+    K = np.array(case["K"] + [[50.0, 0.0]] * 3, dtype=np.float32)
+    V = np.array(case["V"] + [[1000.0, -1000.0]] * 3, dtype=np.float32)
+    out = _attend_one(oracle_lib, dict(case, K=K.tolist(), V=V.tolist()))
+    np.testing.assert_allclose(out[0, 0], case["expected"], rtol=0, atol=1e-14)
+
+
+def _random_problem(synth_lib, B, Hq, Hkv, d, C, seed, T=64, qscale=1.0):
+    s = synth_lib.stream
+    q = synth_lib.normal_bf16((B, Hq, d), seed, s(synth_lib.TAG_MISC, 300), scale=qscale)
+    kv = synth_lib.normal_bf16((B, C, 2, Hkv, T, d), seed, s(synth_lib.TAG_MISC, 301))
+    return q, kv
+
+
+def _sdpa_dense(q, kv, ctx, Hkv, scale, T=64):
+    """Dense attention over the first ctx[b] tokens with torch's float64 SDPA."""
+    import torch
+    B, Hq, d = q.shape
+    outs = []
+    for b in range(B):
+        C = kv.shape[1]
+        K = f32(kv[b, :, 0]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, : ctx[b]]
+        V = f32(kv[b, :, 1]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, : ctx[b]]
+        Q = torch.from_numpy(f32(q[b]).astype(np.float64)).reshape(1, Hq, 1, d)
+        Kt = torch.from_numpy(K.astype(np.float64)).reshape(1, Hkv, -1, d)
+        Vt = torch.from_numpy(V.astype(np.float64)).reshape(1, Hkv, -1, d)
+        o = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, scale=scale, enable_gqa=True)
+        outs.append(o.reshape(Hq, d).numpy())
+    return np.stack(outs)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,C,ctx", [
+    (1, 8, 1, 64, 4, [256]),
+    (2, 16, 2, 128, 3, [192, 150]),       # second request: partial last chunk
+    (2, 64, 8, 128, 2, [128, 65]),        # DeepSeek-V4 GQA shape, one token in last chunk
+    (1, 4, 4, 32, 3, [130]),              # MHA special case
+])
+def test_all_chunks_equals_dense_sdpa(oracle_lib, synth_lib, B, Hq, Hkv, d, C, ctx):
+    """T2: with every chunk kept, sparse attention is dense attention."""
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=7)
+    ctx = np.array(ctx, dtype=np.int32)
+    ids = np.tile(np.arange(C, dtype=np.int32), (B, 1))
+    scale = 1.0 / math.sqrt(d)
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, scale)
+    ref = _sdpa_dense(q, kv, ctx, Hkv, scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_equals_sdpa_over_selected_tokens(oracle_lib, synth_lib):
+    """A strict subset of chunks: dense SDPA on the gathered tokens only."""
+    import torch
+    B, Hq, Hkv, d, C, T = 2, 16, 2, 64, 6, 64
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=8, qscale=4.0)
+    ids = np.array([[1, 4, 5], [0, 2, 3]], dtype=np.int32)
+    ctx = np.array([C * T - 10, C * T], dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d))
+    for b in range(B):
+        toks = [c * T + t for c in ids[b] for t in range(T) if c * T + t < ctx[b]]
+        Kall = f32(kv[b, :, 0]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, toks]
+        Vall = f32(kv[b, :, 1]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, toks]
+        Q = torch.from_numpy(f32(q[b]).astype(np.float64)).reshape(1, Hq, 1, d)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q, torch.from_numpy(Kall.astype(np.float64))[None], torch.from_numpy(Vall.astype(np.float64))[None],
+            scale=1 / math.sqrt(d), enable_gqa=True)
+        np.testing.assert_allclose(out[b], o.reshape(Hq, d).numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_softmax_weights_sum_to_one(oracle_lib, synth_lib):
+    """T3."""
+    B, Hq, Hkv, d, C = 2, 16, 2, 128, 5
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=9, qscale=8.0)
+    ids = np.array([[0, 2, 4], [1, 3, 4]], dtype=np.int32)
+    ctx = np.array([C * 64 - 40, C * 64], dtype=np.int32)
+    _, w = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d), want_weights=True)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+    assert (w >= 0).all()
+    # the masked tail of request 0 (chunk 4, tokens 24..63) has zero weight
+    assert (w[0, :, 2 * 64 + 24:] == 0).all()
+
+
+def test_single_token_returns_its_value(oracle_lib, synth_lib):
+    B, Hq, Hkv, d, C = 1, 8, 1, 64, 3
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=10, qscale=3.0)
+    ids = np.array([[2]], dtype=np.int32)
+    ctx = np.array([2 * 64 + 1], dtype=np.int32)  # only token 128 (chunk 2, t = 0) is valid
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125)
+    v = f32(kv[0, 2, 1, 0, 0]).astype(np.float64)
+    assert np.array_equal(out[0], np.tile(v, (Hq, 1)))
+
+
+def test_identical_keys_give_mean_of_values(oracle_lib, synth_lib):
+    B, Hq, Hkv, d, C = 1, 8, 1, 64, 2
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=11)
+    kv[:, :, 0] = kv[0, 0, 0, 0, 0]  # every key the same vector
+    ids = np.array([[0, 1]], dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, ids, np.array([128]), Hkv, 0.125)
+    V = f32(kv[0, :, 1, 0]).reshape(128, d).astype(np.float64)
+    np.testing.assert_allclose(out[0], np.tile(V.mean(axis=0), (Hq, 1)), rtol=1e-13, atol=1e-15)
+
+
+def test_convex_hull_and_gqa_as_mha(oracle_lib, synth_lib):
+    B, Hq, Hkv, d, C = 2, 16, 2, 64, 4
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=12, qscale=5.0)
+    ids = np.array([[0, 3], [1, 2]], dtype=np.int32)
+    ctx = np.array([C * 64, C * 64 - 5], dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / 8)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            V = np.concatenate([f32(kv[b, c, 1, g]) for c in ids[b]])
+            assert (out[b, h] >= V.min(axis=0) - 1e-12).all() and (out[b, h] <= V.max(axis=0) + 1e-12).all()
+    # MHA with each KV head repeated Hq/Hkv times gives the same result
+    kv_mha = np.repeat(kv, Hq // Hkv, axis=3)
+    out_mha = oracle_lib.gather_attend(q, kv_mha, ids, ctx, Hq, 1 / 8)
+    np.testing.assert_allclose(out, out_mha, rtol=0, atol=0)
+
+
+def test_chunk_order_and_slots(oracle_lib, synth_lib):
+    """Listing chunks in another order, or storing them at other slots, does
+    not change the result beyond summation order."""
+    B, Hq, Hkv, d, C = 1, 16, 2, 64, 6
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=13, qscale=2.0)
+    ctx = np.array([C * 64 - 7], dtype=np.int32)
+    ids = np.array([[0, 2, 5]], dtype=np.int32)
+    base = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / 8)
+    for perm in itertools.permutations(range(3)):
+        p = ids[:, list(perm)]
+        np.testing.assert_allclose(oracle_lib.gather_attend(q, kv, p, ctx, Hkv, 1 / 8), base, rtol=1e-12,
+                                   atol=1e-14)
+    pool = kv[:, [5, 0, 2]]  # compact pool holding chunks 5, 0, 2 in slots 0, 1, 2
+    out = oracle_lib.gather_attend(q, pool, ids, ctx, Hkv, 1 / 8, slots=np.array([[1, 2, 0]], dtype=np.int32))
+    np.testing.assert_allclose(out, base, rtol=0, atol=0)
+
+
+def test_attention_vs_python_loops(oracle_lib, synth_lib):
+    """Brute force with math.exp on a tiny case (independent of numpy/torch)."""
+    B, Hq, Hkv, d, C, T = 1, 4, 2, 8, 2, 64
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=14, qscale=2.0)
+    ids = np.array([[1, 0]], dtype=np.int32)
+    ctx = np.array([100], dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.3)
+    qf, kf = f32(q).astype(float), f32(kv).astype(float)
+    for h in range(Hq):
+        g = h // 2
+        toks = [(c, t) for c in (1, 0) for t in range(T) if c * T + t < 100]
+        z = [sum(qf[0, h, i] * kf[0, c, 0, g, t, i] for i in range(d)) * 0.3 for c, t in toks]
+        m = max(z)
+        w = [math.exp(x - m) for x in z]
+        o = [sum(w[j] * kf[0, c, 1, g, t, i] for j, (c, t) in enumerate(toks)) / sum(w) for i in range(d)]
+        np.testing.assert_allclose(out[0, h], o, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- fetch + schedule
+
+def test_fetch_is_a_byte_copy(oracle_lib, synth_lib):
+    host = synth_lib.normal_bf16((2, 9, 2, 2, 64, 16), 3, synth_lib.stream(synth_lib.TAG_MISC, 400))
+    ids = np.array([[0, 4, 8], [3, 4, 5]], dtype=np.int32)
+    slots = np.array([[2, 0, 1], [0, 1, 2]], dtype=np.int32)
+    pool = oracle_lib.fetch_chunks(host, ids, P=4, slots=slots)
+    for b in range(2):
+        for j in range(3):
+            assert np.array_equal(pool[b, slots[b, j]], host[b, ids[b, j]])
+        assert (pool[b, 3] == 0).all()
+    with pytest.raises(ValueError):
+        oracle_lib.fetch_chunks(host, np.array([[9]], dtype=np.int32), P=1)
+
+
+def test_schedule(oracle_lib):
+    tau = _golden("pages_figures.json")["tau_steps"]["value"]
+    assert [t for t in range(256) if oracle_lib.is_reselect_step(t, tau)] == [0, 64, 128, 192]
+    assert [oracle_lib.selection_for_step(t, tau, 0) for t in (0, 63, 64, 255)] == [0, 0, 1, 3]
+    assert [oracle_lib.selection_for_step(t, tau, 1) for t in (0, 63, 64, 127, 128, 255)] == [0, 0, 0, 0, 1, 2]
