@@ -1,0 +1,197 @@
+/*
+ * lsa.h -- C ABI of the MI355X (gfx950) library for the decode-time hot path
+ * of Lookahead Sparse Attention (LSA, "FlashMemory").
+ *
+ * The pages describe the problem as: keep on the GPU only the KV chunks the
+ * next decode window needs, predict them every tau = 64 steps with a neural
+ * memory indexer whose score is a sigmoid of a dot product between the
+ * current indexer query and each chunk's frozen compressed key, fetch them
+ * ahead of use, and attend over them (paperlayer.ai summary of
+ * "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via Lookahead
+ * Sparse Attention", Abstract, 1 Introduction and 2.1 Architecture; the
+ * sergiiob.dev handbook "DeepSeek-V4: Architecting for Ultra-Long Contexts",
+ * The Neural Memory Indexer).  The four calls below are those steps.
+ *
+ * Conventions shared by every call
+ *  - Pointers marked "device" must point to memory of the current HIP device;
+ *    "host" pointers to host memory.  The caller owns every buffer; the
+ *    library never allocates, frees, or keeps a pointer past the call.
+ *  - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *    outputs are valid once the stream has reached the call.
+ *  - Arguments are validated before any HIP call.  A rejected call enqueues
+ *    nothing and returns LSA_ERR_INVALID_ARGUMENT, LSA_ERR_UNSUPPORTED or
+ *    LSA_ERR_WORKSPACE; lsa_last_error() then holds a message (per thread).
+ *    A failed launch or copy returns LSA_ERR_HIP.  Faults inside a kernel
+ *    surface at the caller's next synchronisation, as with any HIP kernel.
+ *  - Chunk ids that are out of range, or duplicated, are caller errors the
+ *    kernels do not check (the ids produced by lsa_topk_chunks are always in
+ *    range and distinct).
+ *  - A chunk is LSA_CHUNK_TOKENS = 64 consecutive tokens.
+ *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *  - Calls keep no mutable global state and may be issued from several host
+ *    threads on different streams.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_CHUNK_TOKENS 64
+
+typedef enum lsa_status {
+    LSA_OK = 0,
+    LSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, size out of range, inconsistent shape */
+    LSA_ERR_UNSUPPORTED = 2,      /* well-formed but outside what the kernels implement */
+    LSA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
+    LSA_ERR_HIP = 4               /* a HIP launch or copy failed */
+} lsa_status;
+
+/* Static string naming a status code. */
+const char* lsa_status_string(lsa_status s);
+
+/* Message describing the last rejected call made by this host thread
+ * ("" if none).  Valid until the thread's next call into the library. */
+const char* lsa_last_error(void);
+
+/*
+ * lsa_index_score -- the memory indexer's score of every chunk.
+ *
+ * Defined by: the indexer scores chunks by a dot product between the indexer
+ * query (from the current hidden state) and each chunk's frozen compressed
+ * indexer key, passed through a sigmoid (paperlayer.ai summary, 2.1
+ * Architecture and 3 Experiments / Limitations; Korean review, 1. Key Terms &
+ * Definitions).  For request b, query row r < nq and chunk c:
+ *     logits[b][r][c] = sum_i q_idx[b][r][i] * k_idx[b][c][i]   exact int32
+ *     scores[b][r][c] = 1 / (1 + exp(-x)),  x = alpha * (float)logits[b][r][c]
+ * with x formed as one fp32 product; scores are fp32 within 1e-6 relative
+ * (plus 2^-126 absolute where the sigmoid underflows).
+ *
+ *  q_idx   device int8  [B][nq][d_idx]   indexer queries
+ *  k_idx   device int8  [B][C][d_idx]    indexer keys, one row per chunk
+ *  B, nq, C  >= 1 (nq rows share their request's keys; B*nq*C < 2^31)
+ *  d_idx   16, 32, 64, 128 or 256 (LSA_ERR_UNSUPPORTED otherwise)
+ *  alpha   scale of the sigmoid argument (finite)
+ *  logits  device int32 [B][nq][C]       required output
+ *  scores  device fp32  [B][nq][C]       optional output (NULL: not written)
+ *  stream  HIP stream
+ * Pointers to device buffers need 16-byte alignment for q_idx and k_idx,
+ * 4-byte for logits and scores.
+ */
+lsa_status lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, int32_t B, int32_t nq, int32_t C,
+                           int32_t d_idx, float alpha, int32_t* logits, float* scores, hipStream_t stream);
+
+/*
+ * lsa_topk_chunks -- the fixed-budget re-selection.
+ *
+ * Defined by: every tau steps LSA keeps only the chunks the indexer ranks
+ * highest (paperlayer.ai summary, 1 Introduction and 2.1 Architecture, where
+ * the native indexer's selection is a top-k).  For each row r the selected
+ * set is the first k chunks of the total order "logit descending, then chunk
+ * index ascending" (ties go to the lower chunk index), written in ascending
+ * chunk order.  The set is unique, so the output is bit-exact.
+ *
+ *  logits     device int32 [R][C]   (any int32 values)
+ *  R >= 1, 1 <= C <= 65536, 1 <= k <= C
+ *  chunk_ids  device int32 [R][k]   output, ascending within each row
+ *  stream     HIP stream
+ */
+lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t k, int32_t* chunk_ids,
+                           hipStream_t stream);
+
+/*
+ * Number of bytes of workspace lsa_gather_attend needs for these sizes and
+ * this split count (n_split = 0: the library's own choice).  Returns 0 when
+ * no workspace is needed, (size_t)-1 when the arguments are invalid.
+ */
+size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
+                                        int32_t n_split);
+
+/* The split count lsa_gather_attend uses for n_split = 0 (>= 1), or -1 when
+ * the arguments are invalid. */
+int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
+
+/*
+ * lsa_gather_attend -- GQA decode attention over the retained chunks only.
+ *
+ * Defined by: attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, with query
+ * heads in groups that share one KV head (sergiiob.dev handbook, "Grouped
+ * Query Attention (GQA) vs. Multi-Head Attention (MHA)": 64 query heads, 8 KV
+ * heads, d_k = 128, every 8 query heads one KV head), restricted to the
+ * tokens of the chunks LSA kept in GPU memory (paperlayer.ai summary,
+ * Abstract and 2.1 Architecture).  For request b and query head h, with KV
+ * head g = h / (Hq/Hkv):
+ *     tokens  = { chunk_ids[b][j]*64 + t : j < k, t < 64, that position < ctx_len[b] }
+ *     out[b][h] = sum_tok softmax_tok(sm_scale * q[b][h].K[tok]) * V[tok]
+ * where K/V of list entry j are read from store position slots[b][j]
+ * (slots == NULL: position chunk_ids[b][j]).  Products and sums in fp32
+ * (bf16 inputs are exact in fp32); the softmax weights enter the V product
+ * as a two-term bf16 split, about 16 significant bits.
+ *
+ *  q          device bf16 [B][Hq][d]
+ *  kv         device bf16 [B][C_store][2][Hkv][64][d]: chunk-major; index 2
+ *             selects K (0) or V (1); every stored chunk holds 64 token rows,
+ *             also past ctx_len (those rows are read, then ignored)
+ *  C_store    chunk positions per request in `kv` (>= 1)
+ *  chunk_ids  device int32 [B][k]: context chunk index of each list entry
+ *             (decides which tokens are < ctx_len)
+ *  slots      device int32 [B][k] store position of each entry, or NULL
+ *  ctx_len    device int32 [B]: valid tokens per request; a request whose
+ *             listed chunks hold no valid token gets out = 0
+ *  B >= 1; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16; d = 64 or 128; 1 <= k
+ *  sm_scale   softmax scale, normally 1/sqrt(d)
+ *  workspace  device buffer of at least
+ *             lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
+ *             bytes, 256-byte aligned (NULL allowed when that size is 0)
+ *  n_split    chunk-list splits per (request, KV head); 0 = library choice
+ *  out        device fp32 [B][Hq][d]
+ *  stream     HIP stream
+ * q, kv and out need 16-byte alignment.
+ */
+lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                             const int32_t* slots, const int32_t* ctx_len, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
+                             int32_t n_split, float* out, hipStream_t stream);
+
+/*
+ * lsa_fetch_chunks -- host-tier fetch of the selected chunks into HBM.
+ *
+ * Defined by: non-recalled entries live in CPU memory and the recalled
+ * chunks are brought back from that cold storage every tau = 64 steps,
+ * asynchronously, ahead of use (paperlayer.ai summary, 2.1 Architecture and
+ * 3 Experiments / Experimental Setup; sergiiob.dev handbook, The Neural Memory
+ * Indexer, item 3).  For every request b and entry j:
+ *     pool_kv[b][slot] := host_kv[b][chunk_ids[b][j]]   (K and V, all heads)
+ * with slot = host_slots[b][j] (NULL: slot j), as host-to-device copies
+ * enqueued on `side_stream`; entries whose chunk ids and slots both run on
+ * consecutively are merged into one copy.  If `done` is not NULL it is
+ * recorded on `side_stream` after the last copy, so a compute stream can
+ * wait on it (hipStreamWaitEvent) before attending over the pool.
+ *
+ *  host_kv         host bf16 [B][C][2][Hkv][64][d], pinned (hipHostMalloc);
+ *                  pageable memory is rejected with LSA_ERR_INVALID_ARGUMENT
+ *  C               chunks per request in host_kv
+ *  host_chunk_ids  host int32 [B][k], each in [0, C) (checked)
+ *  host_slots      host int32 [B][k], each in [0, P) (checked), or NULL
+ *  pool_kv         device bf16 [B][P][2][Hkv][64][d]
+ *  P               chunk slots per request in the pool (k <= P when slots is NULL)
+ *  B, Hkv, d, k    >= 1
+ *  side_stream     HIP stream the copies go on
+ *  done            HIP event or NULL
+ * The id and slot arrays are read during the call and may be reused at once.
+ */
+lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,
+                            const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
+                            int32_t d, int32_t k, hipStream_t side_stream, hipEvent_t done);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

@@ -1,0 +1,193 @@
+"""ctypes binding of liblsa.so (the C ABI in include/lsa.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+the library.  PyTorch supplies device memory and streams; outputs that the
+caller does not pass are allocated with ``torch.empty`` on the device of the
+inputs.  There is no fallback: if the library is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsa.so")
+_lib = None
+
+LSA_OK = 0
+STATUS_NAMES = {0: "LSA_OK", 1: "LSA_ERR_INVALID_ARGUMENT", 2: "LSA_ERR_UNSUPPORTED", 3: "LSA_ERR_WORKSPACE",
+                4: "LSA_ERR_HIP"}
+CHUNK_TOKENS = 64
+
+# Every symbol include/lsa.h declares.
+EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks",
+           "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits", "lsa_gather_attend",
+           "lsa_fetch_chunks")
+
+
+class LsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblsa.so (built by ``lookahead_chunk_sparse_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                          "or python lookahead_chunk_sparse_amd/build.py")
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.lsa_status_string.argtypes = [ctypes.c_int]
+    L.lsa_status_string.restype = ctypes.c_char_p
+    L.lsa_last_error.argtypes = []
+    L.lsa_last_error.restype = ctypes.c_char_p
+    L.lsa_index_score.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp]
+    L.lsa_index_score.restype = ctypes.c_int
+    L.lsa_topk_chunks.argtypes = [vp, i32, i32, i32, vp, vp]
+    L.lsa_topk_chunks.restype = ctypes.c_int
+    L.lsa_gather_attend_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.lsa_gather_attend_workspace_size.restype = sz
+    L.lsa_gather_attend_default_splits.argtypes = [i32, i32, i32]
+    L.lsa_gather_attend_default_splits.restype = i32
+    L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, sz, i32, vp, vp]
+    L.lsa_gather_attend.restype = ctypes.c_int
+    L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
+    L.lsa_fetch_chunks.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != LSA_OK:
+        raise LsaError(status, load_library().lsa_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def lsa_index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, alpha: float, logits=None, scores=None,
+                    want_scores: bool = True, stream=None):
+    """q_idx int8 [B][nq][d_idx], k_idx int8 [B][C][d_idx] (device).
+    Returns (logits int32 [B][nq][C], scores fp32 [B][nq][C] or None)."""
+    _need(q_idx, torch.int8, "q_idx", 3)
+    _need(k_idx, torch.int8, "k_idx", 3)
+    B, nq, d_idx = q_idx.shape
+    C = k_idx.shape[1]
+    if logits is None:
+        logits = torch.empty((B, nq, C), dtype=torch.int32, device=k_idx.device)
+    if scores is None and want_scores:
+        scores = torch.empty((B, nq, C), dtype=torch.float32, device=k_idx.device)
+    if k_idx.shape[0] != B or k_idx.shape[2] != d_idx:
+        raise ValueError(f"k_idx shape {tuple(k_idx.shape)} does not match q_idx {tuple(q_idx.shape)}")
+    _check(load_library().lsa_index_score(_ptr(q_idx), _ptr(k_idx), B, nq, C, d_idx, alpha, _ptr(logits),
+                                          _ptr(scores), _stream(stream)))
+    return logits, scores
+
+
+def lsa_topk_chunks(logits: torch.Tensor, k: int, chunk_ids=None, stream=None) -> torch.Tensor:
+    """logits int32 [..., C] (rows = all leading dims) -> int32 [..., k], ascending."""
+    _need(logits, torch.int32, "logits")
+    C = logits.shape[-1]
+    R = logits.numel() // C
+    if chunk_ids is None:
+        chunk_ids = torch.empty((*logits.shape[:-1], k), dtype=torch.int32, device=logits.device)
+    _check(load_library().lsa_topk_chunks(_ptr(logits), R, C, k, _ptr(chunk_ids), _stream(stream)))
+    return chunk_ids
+
+
+def lsa_gather_attend_workspace_size(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0) -> int:
+    n = load_library().lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
+    if n == ctypes.c_size_t(-1).value:
+        raise LsaError(1, load_library().lsa_last_error().decode())
+    return int(n)
+
+
+def lsa_gather_attend_default_splits(B: int, Hkv: int, k: int) -> int:
+    return int(load_library().lsa_gather_attend_default_splits(B, Hkv, k))
+
+
+def alloc_workspace(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0, device="cuda"):
+    """A workspace tensor for lsa_gather_attend (None when none is needed)."""
+    n = lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor,
+                      sm_scale: float | None = None, slots: torch.Tensor | None = None, workspace=None,
+                      n_split: int = 0, out=None, stream=None) -> torch.Tensor:
+    """q bf16 [B][Hq][d]; kv bf16 [B][C_store][2][Hkv][64][d]; chunk_ids int32 [B][k];
+    ctx_len int32 [B]; slots int32 [B][k] or None.  Returns fp32 [B][Hq][d]."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(kv, torch.bfloat16, "kv", 6)
+    _need(chunk_ids, torch.int32, "chunk_ids", 2)
+    _need(ctx_len, torch.int32, "ctx_len", 1)
+    B, Hq, d = q.shape
+    _, C_store, two, Hkv, T, dk = kv.shape
+    k = chunk_ids.shape[1]
+    if kv.shape[0] != B or two != 2 or T != CHUNK_TOKENS or dk != d:
+        raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
+    if chunk_ids.shape[0] != B or ctx_len.shape[0] != B:
+        raise ValueError("chunk_ids / ctx_len batch size mismatch")
+    if slots is not None:
+        _need(slots, torch.int32, "slots", 2)
+        if tuple(slots.shape) != tuple(chunk_ids.shape):
+            raise ValueError("slots must have the shape of chunk_ids")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, k, n_split, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().lsa_gather_attend(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
+                                            _ptr(ctx_len), B, Hq, Hkv, d, k, sm_scale, _ptr(workspace), ws_bytes,
+                                            n_split, _ptr(out), _stream(stream)))
+    return out
+
+
+def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_kv: torch.Tensor,
+                     host_slots: torch.Tensor | None = None, stream=None, done=None):
+    """host_kv pinned bf16 [B][C][2][Hkv][64][d]; host ids int32 [B][k] (CPU);
+    pool_kv device bf16 [B][P][2][Hkv][64][d].  `done`: torch.cuda.Event or None."""
+    _need(host_kv, torch.bfloat16, "host_kv", 6)
+    _need(pool_kv, torch.bfloat16, "pool_kv", 6)
+    _need(host_chunk_ids, torch.int32, "host_chunk_ids", 2)
+    if host_chunk_ids.is_cuda or (host_slots is not None and host_slots.is_cuda):
+        raise ValueError("chunk ids and slots for the fetch must be host tensors")
+    B, C, _, Hkv, T, d = host_kv.shape
+    P = pool_kv.shape[1]
+    k = host_chunk_ids.shape[1]
+    if host_slots is not None:
+        _need(host_slots, torch.int32, "host_slots", 2)
+    ev = 0
+    if done is not None:
+        ev = done.cuda_event if hasattr(done, "cuda_event") else int(done)
+    _check(load_library().lsa_fetch_chunks(_ptr(host_kv), C, _ptr(host_chunk_ids), _ptr(host_slots),
+                                           _ptr(pool_kv), P, B, Hkv, d, k, _stream(stream), ev))

@@ -1,0 +1,317 @@
+// Gathered-chunk GQA decode attention for gfx950 (split-K flash decode).
+//
+// What it computes: for request b and query head h (KV head g = h / G),
+// softmax(q K^T * sm_scale) V over the 64-token chunks listed for b, leaving
+// out tokens at or past ctx_len[b] (attention formula and GQA grouping:
+// sergiiob.dev handbook "DeepSeek-V4: Architecting for Ultra-Long Contexts",
+// "Grouped Query Attention (GQA) vs. Multi-Head Attention (MHA)"; retained
+// chunks only: paperlayer.ai summary of "FlashMemory-DeepSeek-V4", Abstract
+// and 2.1 Architecture).
+//
+// How, on CDNA4:
+//  * One workgroup = (request b, KV head g, split s) owns a contiguous slice
+//    of b's chunk list; its 4 waves each take 16 of every chunk's 64 tokens.
+//    Every K/V byte of the group is read from HBM once and serves all G query
+//    heads of the group (G <= 16 fills the N side of a 16-wide MFMA tile).
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 token rows of K (each
+//    lane loads 16 contiguous bytes of a row), B = the group's queries, kept
+//    in registers for the whole loop.
+//  * O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: the S^T accumulator layout
+//    (lane = head + 16*(slot/4), element = slot%4) is exactly the B-operand
+//    layout P^T needs, so P never leaves registers.  V^T needs each lane to
+//    hold 4 tokens of one d column: lanes load 16 contiguous bytes of 4 rows
+//    (4 consecutive rows per load instruction, fully coalesced) and a v_perm
+//    per output dword transposes them in registers, so no LDS is used on the
+//    streaming path.  Which slot carries which token is a free choice; slot
+//    4i+r carries token 4r+i of the wave's 16, making each load instruction
+//    cover 4 whole consecutive rows.
+//  * P enters the V product as hi + lo bf16 parts (two MFMAs), keeping about
+//    16 significant bits of the softmax weights; all accumulation is fp32.
+//  * Online softmax per wave in the log2 domain; the 4 waves merge through
+//    LDS at the end; splits merge in a second small kernel.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "lsa_kernels.h"
+
+namespace lsa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSliceTokens = 16;
+
+template <int D>
+struct VRow;  // one lane's share of one V row: D/16 bf16 values
+template <>
+struct VRow<128> {
+    uint4 v;
+};
+template <>
+struct VRow<64> {
+    uint2 v;
+};
+
+template <int D>
+__device__ inline VRow<D> load_vrow(const uint16_t* p);
+template <>
+__device__ inline VRow<128> load_vrow<128>(const uint16_t* p) {
+    return VRow<128>{*reinterpret_cast<const uint4*>(p)};
+}
+template <>
+__device__ inline VRow<64> load_vrow<64>(const uint16_t* p) {
+    return VRow<64>{*reinterpret_cast<const uint2*>(p)};
+}
+
+__device__ inline uint32_t vrow_dword(const VRow<128>& r, int w) {
+    return w == 0 ? r.v.x : w == 1 ? r.v.y : w == 2 ? r.v.z : r.v.w;
+}
+__device__ inline uint32_t vrow_dword(const VRow<64>& r, int w) { return w == 0 ? r.v.x : r.v.y; }
+
+__device__ inline void vrow_zero(VRow<128>& r) { r.v = make_uint4(0, 0, 0, 0); }
+__device__ inline void vrow_zero(VRow<64>& r) { r.v = make_uint2(0, 0); }
+
+// Registers of one wave's 16-token slice of one chunk.
+template <int D>
+struct Slice {
+    uint4 k[D / 32];   // K: row pi(lane%16), 8 bf16 per MFMA step
+    VRow<D> v[4];      // V: rows 4r + lane/16, d range [D/16 * (lane%16), +D/16)
+};
+
+template <int D>
+__device__ inline void load_slice(Slice<D>& s, const uint16_t* ktile, const uint16_t* vtile, int wave, int lane) {
+    const int n = lane & 15, i = lane >> 4;
+    const int tk = wave * kSliceTokens + 4 * (n & 3) + (n >> 2);  // token of A row n
+    const uint16_t* kp = ktile + (size_t)tk * D + 8 * i;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) s.k[st] = *reinterpret_cast<const uint4*>(kp + 32 * st);
+    constexpr int DPL = D / 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tv = wave * kSliceTokens + 4 * r + i;
+        s.v[r] = load_vrow<D>(vtile + (size_t)tv * D + DPL * n);
+    }
+}
+
+__device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+__device__ inline float bf16_value(short b) { return (float)__builtin_bit_cast(__bf16, b); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
+    constexpr int KS = D / 32;   // QK MFMA steps over d
+    constexpr int DPL = D / 16;  // PV MFMAs (d values per lane per V row)
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = lane & 15, i = lane >> 4;
+
+    int blk = blockIdx.x;
+    const int s = blk % a.n_split;
+    blk /= a.n_split;
+    const int g = blk % a.Hkv;
+    const int b = blk / a.Hkv;
+    const int G = a.G;
+
+    const int64_t j0 = ((int64_t)s * a.k) / a.n_split;
+    const int64_t j1 = ((int64_t)(s + 1) * a.k) / a.n_split;
+    const int ctx = a.ctx[b];
+    const int32_t* ids = a.ids + (int64_t)b * a.k;
+    const int32_t* slots = a.slots ? a.slots + (int64_t)b * a.k : nullptr;
+
+    // B operand of S^T = K Q^T: lane (head n, group i) holds q[n][32*st + 8*i .. +8].
+    bf16x8 qb[KS];
+    {
+        const bool live = n < G;
+        const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + (live ? n : 0)) * D + 8 * i;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            uint4 v = live ? *reinterpret_cast<const uint4*>(qp + 32 * st) : make_uint4(0, 0, 0, 0);
+            qb[st] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+
+    const int64_t chunk_elems = (int64_t)2 * a.Hkv * kChunkTokens * D;
+    const int64_t tile_elems = (int64_t)kChunkTokens * D;
+    const uint16_t* kv_b = a.kv + (int64_t)b * a.C_store * chunk_elems + (int64_t)g * tile_elems;
+    const int64_t v_off = (int64_t)a.Hkv * tile_elems;
+
+    f32x4 oacc[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running max (log2 domain) of head n
+    float l_run = 0.f;        // this lane's share of the running sum of head n
+
+    Slice<D> cur, nxt;
+    if (j0 < j1) {
+        const int64_t p = slots ? slots[j0] : ids[j0];
+        const uint16_t* kt = kv_b + p * chunk_elems;
+        load_slice<D>(cur, kt, kt + v_off, wave, lane);
+    }
+    for (int64_t j = j0; j < j1; ++j) {
+        if (j + 1 < j1) {
+            const int64_t p = slots ? slots[j + 1] : ids[j + 1];
+            const uint16_t* kt = kv_b + p * chunk_elems;
+            load_slice<D>(nxt, kt, kt + v_off, wave, lane);
+        }
+        // valid tokens of this chunk (uniform across the workgroup)
+        const int64_t c = ids[j];
+        const int64_t nvalid64 = (int64_t)ctx - c * kChunkTokens;
+        const int nvalid = nvalid64 < 0 ? 0 : nvalid64 > kChunkTokens ? kChunkTokens : (int)nvalid64;
+        const int first_tok = wave * kSliceTokens;
+        if (nvalid > first_tok) {
+            // S^T[slot][head] for this wave's 16 tokens
+            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[st]), qb[st], sacc,
+                                                               0, 0, 0);
+            // lane holds head n, slots 4i+r = tokens first_tok + 4r + i
+            float sv[4];
+            const bool partial = nvalid < first_tok + kSliceTokens;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sv[r] = sacc[r] * a.scale_log2;
+                if (partial && first_tok + 4 * r + i >= nvalid) {
+                    sv[r] = -INFINITY;
+                    vrow_zero(cur.v[r]);
+                }
+            }
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
+            l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            m_run = m_new;
+#pragma unroll
+            for (int j2 = 0; j2 < DPL; ++j2) oacc[j2] *= alpha;
+            i16x4 phi, plo;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const short h = bf16_bits(p[r]);
+                phi[r] = h;
+                plo[r] = bf16_bits(p[r] - bf16_value(h));
+            }
+            // A operand of O^T += V^T P^T: element r = V[token 4r+i][DPL*n + jj]
+#pragma unroll
+            for (int jj = 0; jj < DPL; ++jj) {
+                const int w = jj >> 1;
+                const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t lo = __builtin_amdgcn_perm(vrow_dword(cur.v[1], w), vrow_dword(cur.v[0], w), sel);
+                const uint32_t hi = __builtin_amdgcn_perm(vrow_dword(cur.v[3], w), vrow_dword(cur.v[2], w), sel);
+                const i16x4 av = __builtin_bit_cast(i16x4, make_uint2(lo, hi));
+                oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, phi, oacc[jj], 0, 0, 0);
+                oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, plo, oacc[jj], 0, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+
+    // ---- merge the 4 waves of the workgroup through LDS ----
+    __shared__ float sm_m[kWaves][16];
+    __shared__ float sm_l[kWaves][16];
+    __shared__ float sm_o[kWaves][16 * D];
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (n < G) {
+        if (i == 0) {
+            sm_m[wave][n] = m_run;
+            sm_l[wave][n] = l_tot;
+        }
+        // lane holds O[n][DPL*(4i + r) + jj]
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jj = 0; jj < DPL; ++jj) sm_o[wave][n * D + DPL * (4 * i + r) + jj] = oacc[jj][r];
+    }
+    __syncthreads();
+
+    const int64_t grp = (int64_t)b * a.Hkv + g;
+    for (int e = threadIdx.x; e < G * D; e += kThreads) {
+        const int h = e / D, dd = e % D;
+        float mstar = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm_m[w][h]);
+        float o = 0.f, l = 0.f;
+        if (mstar != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - mstar);
+                o += sc * sm_o[w][h * D + dd];
+                l += sc * sm_l[w][h];
+            }
+        }
+        if (a.n_split == 1) {
+            a.out[((int64_t)b * a.Hq + (int64_t)g * G + h) * D + dd] = l > 0.f ? o / l : 0.f;
+        } else {
+            const int64_t part = grp * a.n_split + s;
+            a.part_o[(part * G + h) * D + dd] = o;
+            if (dd == 0) {
+                a.part_ml[(part * G + h) * 2 + 0] = mstar;
+                a.part_ml[(part * G + h) * 2 + 1] = l;
+            }
+        }
+    }
+}
+
+// Merge the n_split partial (m, l, o) triples of every (request, head):
+// m* = max m_s, o = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
+__global__ void attend_combine_kernel(AttendArgs a) {
+    const int bh = blockIdx.x;  // b * Hq + h
+    const int b = bh / a.Hq, h = bh % a.Hq;
+    const int g = h / a.G, hh = h % a.G;
+    const int dd = threadIdx.x;
+    const int64_t base = ((int64_t)b * a.Hkv + g) * a.n_split;
+    float mstar = -INFINITY;
+    for (int s = 0; s < a.n_split; ++s) mstar = fmaxf(mstar, a.part_ml[((base + s) * a.G + hh) * 2]);
+    float o = 0.f, l = 0.f;
+    if (mstar != -INFINITY) {
+        for (int s = 0; s < a.n_split; ++s) {
+            const int64_t ps = (base + s) * a.G + hh;
+            const float sc = __builtin_amdgcn_exp2f(a.part_ml[ps * 2] - mstar);
+            l += sc * a.part_ml[ps * 2 + 1];
+            o += sc * a.part_o[ps * a.d + dd];
+        }
+    }
+    a.out[(int64_t)bh * a.d + dd] = l > 0.f ? o / l : 0.f;
+}
+
+}  // namespace
+
+int attend_default_splits(int B, int Hkv, int k) {
+    // Aim at one full wave of workgroups: 256 CUs x 2 resident workgroups.
+    const int64_t groups = (int64_t)B * Hkv;
+    int64_t s = (512 + groups / 2) / groups;
+    if (s < 1) s = 1;
+    if (s > k) s = k;
+    return (int)s;
+}
+
+size_t attend_workspace_bytes(int B, int Hkv, int G, int d, int n_split) {
+    if (n_split <= 1) return 0;
+    const size_t parts = (size_t)B * Hkv * n_split * G;
+    const size_t o_bytes = parts * d * sizeof(float);
+    const size_t o_round = (o_bytes + 255) & ~(size_t)255;
+    return o_round + parts * 2 * sizeof(float);
+}
+
+hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * a.n_split));
+    if (a.d == 128)
+        hipLaunchKernelGGL(attend_split_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attend_split_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_split == 1) return e;
+    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(a.d), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

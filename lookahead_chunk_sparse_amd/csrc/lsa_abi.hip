@@ -1,0 +1,211 @@
+// C-ABI entry points (include/lsa.h): argument validation, workspace
+// layout and kernel launches; plus the host-tier fetch, which is pure
+// host-to-device DMA on a side stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/lsa.h"
+#include "lsa_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lsa_status fail(lsa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lsa_status fail(lsa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+lsa_status ok() {
+    g_last_error.clear();
+    return LSA_OK;
+}
+
+lsa_status hip_fail(hipError_t e, const char* what) {
+    return fail(LSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_status_string(lsa_status s) {
+    switch (s) {
+        case LSA_OK: return "LSA_OK";
+        case LSA_ERR_INVALID_ARGUMENT: return "LSA_ERR_INVALID_ARGUMENT";
+        case LSA_ERR_UNSUPPORTED: return "LSA_ERR_UNSUPPORTED";
+        case LSA_ERR_WORKSPACE: return "LSA_ERR_WORKSPACE";
+        case LSA_ERR_HIP: return "LSA_ERR_HIP";
+    }
+    return "LSA_ERR_UNKNOWN";
+}
+
+const char* lsa_last_error(void) { return g_last_error.c_str(); }
+
+lsa_status lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, int32_t B, int32_t nq, int32_t C,
+                           int32_t d_idx, float alpha, int32_t* logits, float* scores, hipStream_t stream) {
+    if (!q_idx || !k_idx || !logits) return fail(LSA_ERR_INVALID_ARGUMENT, "q_idx, k_idx and logits are required");
+    if (B < 1 || nq < 1 || C < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B=%d nq=%d C=%d must all be >= 1", B, nq, C);
+    if ((int64_t)B * nq * C >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B*nq*C=%lld must be < 2^31", (long long)B * nq * C);
+    if (!std::isfinite(alpha)) return fail(LSA_ERR_INVALID_ARGUMENT, "alpha must be finite");
+    if (d_idx != 16 && d_idx != 32 && d_idx != 64 && d_idx != 128 && d_idx != 256)
+        return fail(LSA_ERR_UNSUPPORTED, "d_idx=%d: supported are 16, 32, 64, 128, 256", d_idx);
+    if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(logits, 4) || (scores && !aligned(scores, 4)))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "q_idx/k_idx need 16-byte, logits/scores 4-byte alignment");
+    hipError_t e = lsa::launch_index_score(q_idx, k_idx, B, nq, C, d_idx, alpha, logits, scores, stream);
+    if (e != hipSuccess) return hip_fail(e, "index score launch");
+    return ok();
+}
+
+lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t k, int32_t* chunk_ids,
+                           hipStream_t stream) {
+    if (!logits || !chunk_ids) return fail(LSA_ERR_INVALID_ARGUMENT, "logits and chunk_ids are required");
+    if (R < 1 || C < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "R=%d C=%d must be >= 1", R, C);
+    if (k < 1 || k > C) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d must be in [1, C=%d]", k, C);
+    if (C > lsa::kTopkMaxC) return fail(LSA_ERR_UNSUPPORTED, "C=%d exceeds %d", C, lsa::kTopkMaxC);
+    if (!aligned(logits, 4) || !aligned(chunk_ids, 4))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "logits and chunk_ids need 4-byte alignment");
+    hipError_t e = lsa::launch_topk(logits, R, C, k, chunk_ids, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return ok();
+}
+
+static lsa_status check_attend_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || k < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B=%d Hq=%d Hkv=%d k=%d must all be >= 1", B, Hq, Hkv, k);
+    if (Hq % Hkv != 0) return fail(LSA_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(LSA_ERR_UNSUPPORTED, "Hq/Hkv=%d: at most 16 query heads per KV head", Hq / Hkv);
+    if (d != 64 && d != 128) return fail(LSA_ERR_UNSUPPORTED, "d=%d: supported head dims are 64 and 128", d);
+    if ((int64_t)B * Hq >= ((int64_t)1 << 31) || (int64_t)B * k >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B*Hq and B*k must be < 2^31");
+    return LSA_OK;
+}
+
+int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k) {
+    if (B < 1 || Hkv < 1 || k < 1) return -1;
+    return lsa::attend_default_splits(B, Hkv, k);
+}
+
+size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k, int32_t n_split) {
+    if (check_attend_shape(B, Hq, Hkv, d, k) != LSA_OK || n_split < 0) return (size_t)-1;
+    if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
+    if (n_split > k) n_split = k;
+    return lsa::attend_workspace_bytes(B, Hkv, Hq / Hkv, d, n_split);
+}
+
+lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                             const int32_t* slots, const int32_t* ctx_len, int32_t B, int32_t Hq, int32_t Hkv,
+                             int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
+                             int32_t n_split, float* out, hipStream_t stream) {
+    if (!q || !kv || !chunk_ids || !ctx_len || !out)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "q, kv, chunk_ids, ctx_len and out are required");
+    lsa_status st = check_attend_shape(B, Hq, Hkv, d, k);
+    if (st != LSA_OK) return st;
+    if (C_store < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "C_store=%lld must be >= 1", (long long)C_store);
+    if (!std::isfinite(sm_scale)) return fail(LSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+    if (n_split < 0) return fail(LSA_ERR_INVALID_ARGUMENT, "n_split=%d must be >= 0", n_split);
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "q, kv and out need 16-byte alignment");
+    if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
+    if (n_split > k) n_split = k;
+    const int G = Hq / Hkv;
+    const size_t need = lsa::attend_workspace_bytes(B, Hkv, G, d, n_split);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (need > 0 && !aligned(workspace, 256)) return fail(LSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    lsa::AttendArgs a;
+    a.q = q;
+    a.kv = kv;
+    a.C_store = C_store;
+    a.ids = chunk_ids;
+    a.slots = slots;
+    a.ctx = ctx_len;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.d = d;
+    a.k = k;
+    a.n_split = n_split;
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.out = out;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    if (need > 0) {
+        const size_t parts = (size_t)B * Hkv * n_split * G;
+        const size_t o_round = (parts * d * sizeof(float) + 255) & ~(size_t)255;
+        a.part_o = static_cast<float*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_round);
+    }
+    hipError_t e = lsa::launch_gather_attend(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "gather-attend launch");
+    return ok();
+}
+
+lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,
+                            const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
+                            int32_t d, int32_t k, hipStream_t side_stream, hipEvent_t done) {
+    if (!host_kv || !host_chunk_ids || !pool_kv)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv, host_chunk_ids and pool_kv are required");
+    if (C < 1 || P < 1 || B < 1 || Hkv < 1 || d < 1 || k < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, d, k must all be >= 1");
+    if (!host_slots && k > P) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d > P=%lld with default slots", k, (long long)P);
+    for (int64_t e = 0; e < (int64_t)B * k; ++e) {
+        if (host_chunk_ids[e] < 0 || host_chunk_ids[e] >= C)
+            return fail(LSA_ERR_INVALID_ARGUMENT, "chunk id %d at entry %lld outside [0, %lld)", host_chunk_ids[e],
+                        (long long)e, (long long)C);
+        if (host_slots && (host_slots[e] < 0 || host_slots[e] >= P))
+            return fail(LSA_ERR_INVALID_ARGUMENT, "slot %d at entry %lld outside [0, %lld)", host_slots[e],
+                        (long long)e, (long long)P);
+    }
+    // The copies must come from pinned memory to be asynchronous DMA.
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof attr);
+    hipError_t pe = hipPointerGetAttributes(&attr, host_kv);
+    if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();  // clear the error a pageable pointer leaves behind
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv is not pinned host memory (allocate it with hipHostMalloc)");
+    }
+    const size_t chunk_bytes = (size_t)2 * Hkv * lsa::kChunkTokens * d * sizeof(uint16_t);
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t* ids = host_chunk_ids + (int64_t)b * k;
+        const int32_t* sl = host_slots ? host_slots + (int64_t)b * k : nullptr;
+        int32_t j = 0;
+        while (j < k) {
+            const int64_t c0 = ids[j];
+            const int64_t p0 = sl ? sl[j] : j;
+            int32_t run = 1;
+            while (j + run < k && ids[j + run] == c0 + run && (sl ? sl[j + run] : j + run) == p0 + run) ++run;
+            const char* src = reinterpret_cast<const char*>(host_kv) + ((int64_t)b * C + c0) * chunk_bytes;
+            char* dst = reinterpret_cast<char*>(pool_kv) + ((int64_t)b * P + p0) * chunk_bytes;
+            hipError_t e = hipMemcpyAsync(dst, src, run * chunk_bytes, hipMemcpyHostToDevice, side_stream);
+            if (e != hipSuccess) return hip_fail(e, "fetch copy");
+            j += run;
+        }
+    }
+    if (done) {
+        hipError_t e = hipEventRecord(done, side_stream);
+        if (e != hipSuccess) return hip_fail(e, "fetch event record");
+    }
+    return ok();
+}
+
+}  // extern "C"

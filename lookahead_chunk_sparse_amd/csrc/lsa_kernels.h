@@ -1,0 +1,39 @@
+// Internal launch interface of the HIP kernels behind the C ABI (include/lsa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+constexpr int kChunkTokens = 64;
+
+// ---- index score (indexer dot product + sigmoid) ----
+hipError_t launch_index_score(const int8_t* q_idx, const int8_t* k_idx, int B, int nq, int C, int d_idx,
+                              float alpha, int32_t* logits, float* scores, hipStream_t stream);
+
+// ---- top-k chunk selection ----
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkMaxC = 65536;
+hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, hipStream_t stream);
+
+// ---- gathered GQA decode attention ----
+struct AttendArgs {
+    const uint16_t* q;      // [B][Hq][d] bf16
+    const uint16_t* kv;     // [B][C_store][2][Hkv][64][d] bf16
+    int64_t C_store;
+    const int32_t* ids;     // [B][k]
+    const int32_t* slots;   // [B][k] or nullptr
+    const int32_t* ctx;     // [B]
+    int B, Hq, Hkv, G, d, k, n_split;
+    float scale_log2;       // sm_scale * log2(e)
+    float* part_o;          // [B][Hkv][n_split][G][d]      (n_split > 1)
+    float* part_ml;         // [B][Hkv][n_split][G][2]      (n_split > 1)
+    float* out;             // [B][Hq][d]
+};
+
+int attend_default_splits(int B, int Hkv, int k);
+size_t attend_workspace_bytes(int B, int Hkv, int G, int d, int n_split);
+hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream);
+
+}  // namespace lsa

@@ -1,0 +1,134 @@
+"""Decode schedule for one attention layer on one GPU.
+
+Every tau = 64 decode steps the memory indexer scores all chunks against the
+current indexer query and the top-k chunks are re-selected; every step
+attends over the selected chunks only (paperlayer.ai summary of
+"FlashMemory-DeepSeek-V4", 1 Introduction and 2.1 Architecture: the indexer
+runs every tau steps and predicts what the upcoming tau-step window needs;
+3 Experiments / Experimental Setup: tau = 64).
+
+Two placements of the K/V:
+  * HBM-resident store (lag 0): interval i attends with the selection made at
+    its own first step.
+  * Host tier (lag 1): the whole K/V lives in pinned host memory; the chunks
+    of selection i are copied into an HBM pool on a side stream while interval
+    i decodes with selection i-1 (the handbook page's asynchronous prefetch;
+    the summary's eviction of non-recalled entries to CPU), so the copy
+    overlaps attention.  Two pool buffers alternate; the first interval waits
+    for its own fetch.
+
+This module only orders calls into liblsa.so on HIP streams and records
+events; it computes nothing itself.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._binding import (alloc_workspace, lsa_fetch_chunks, lsa_gather_attend, lsa_index_score, lsa_topk_chunks)
+
+TAU = 64
+
+
+def selection_for_step(t: int, tau: int = TAU, lag: int = 0) -> int:
+    """Re-selection whose chunks step t attends over (interval t//tau, minus lag, at least 0)."""
+    return max(t // tau - lag, 0)
+
+
+class LsaDecoder:
+    """Decode state of one layer: indexer keys, K/V placement, selection buffers.
+
+    k_idx    device int8 [B][C][d_idx]
+    ctx_len  device int32 [B]
+    kv       device bf16 [B][C][2][Hkv][64][d]        (HBM-resident store), or
+    host_kv  pinned bf16 [B][C][2][Hkv][64][d]        (host tier; pool of k slots x 2)
+    """
+
+    def __init__(self, *, k_idx: torch.Tensor, ctx_len: torch.Tensor, Hq: int, k: int, alpha: float,
+                 kv: torch.Tensor | None = None, host_kv: torch.Tensor | None = None, tau: int = TAU,
+                 n_split: int = 0, sm_scale: float | None = None, device="cuda"):
+        if (kv is None) == (host_kv is None):
+            raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
+        self.k_idx = k_idx
+        self.ctx_len = ctx_len
+        self.kv = kv
+        self.host_kv = host_kv
+        store = kv if kv is not None else host_kv
+        self.B, self.C, _, self.Hkv, self.T, self.d = store.shape
+        self.Hq, self.k, self.alpha, self.tau = Hq, k, alpha, tau
+        self.d_idx = k_idx.shape[2]
+        self.lag = 1 if host_kv is not None else 0
+        self.n_split = n_split
+        self.sm_scale = 1.0 / math.sqrt(self.d) if sm_scale is None else sm_scale
+        dev = torch.device(device)
+        B = self.B
+        self.logits = torch.empty((B, 1, self.C), dtype=torch.int32, device=dev)
+        self.scores = torch.empty((B, 1, self.C), dtype=torch.float32, device=dev)
+        # selection buffers alternate by selection parity so a new selection
+        # never overwrites the one the current interval attends with
+        self.sel_ids = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
+        if self.lag:
+            self.pool = [torch.empty((B, k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
+                         for _ in range(2)]
+            self.slots = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+            self.host_ids = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)]
+            self.side = torch.cuda.Stream(device=dev)
+            self.ev_ids = torch.cuda.Event()
+            self.fetch_done = [torch.cuda.Event() for _ in range(2)]
+            self.attn_done = torch.cuda.Event()
+            self._attn_done_valid = False
+
+    # ---- single operations -------------------------------------------------
+    def reselect(self, q_idx: torch.Tensor, sel: int, stream=None) -> torch.Tensor:
+        """Score every chunk against q_idx (int8 [B][1][d_idx]) and keep the top k
+        into selection buffer sel % 2."""
+        lsa_index_score(q_idx, self.k_idx, self.alpha, logits=self.logits, scores=self.scores, stream=stream)
+        ids = self.sel_ids[sel % 2]
+        lsa_topk_chunks(self.logits.view(self.B, self.C), self.k, chunk_ids=ids, stream=stream)
+        return ids
+
+    def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """One decode step's attention with selection `sel`."""
+        ids = self.sel_ids[sel % 2]
+        if self.lag:
+            return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=self.slots,
+                                     workspace=self.workspace, n_split=self.n_split, out=out, stream=stream)
+        return lsa_gather_attend(q, self.kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
+                                 n_split=self.n_split, out=out, stream=stream)
+
+    # ---- one interval ------------------------------------------------------
+    def run_interval(self, i: int, q_idx: torch.Tensor, qs, outs) -> None:
+        """Enqueue interval i: its re-selection and len(qs) attention steps.
+        qs[j] is the bf16 [B][Hq][d] query of step i*tau + j; outs[j] receives
+        its fp32 output (the same tensor may be passed for every step)."""
+        if not self.lag:
+            self.reselect(q_idx, i)
+            for q, o in zip(qs, outs):
+                self.attend(q, i, o)
+            return
+        main = torch.cuda.current_stream()
+        self.reselect(q_idx, i)
+        self.host_ids[i % 2].copy_(self.sel_ids[i % 2], non_blocking=True)
+        self.ev_ids.record(main)
+        if i == 0:
+            self._fetch(0)
+        src = max(i - 1, 0)
+        main.wait_event(self.fetch_done[src % 2])
+        for q, o in zip(qs, outs):
+            self.attend(q, src, o)
+        if i >= 1:
+            self._fetch(i)  # overlaps the steps just enqueued
+        self.attn_done.record(main)
+        self._attn_done_valid = True
+
+    def _fetch(self, i: int) -> None:
+        """Copy selection i's chunks from host into pool buffer i % 2 on the side stream."""
+        self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
+        if self._attn_done_valid:
+            # pool buffer i % 2 was last read by the previous interval
+            self.side.wait_event(self.attn_done)
+        lsa_fetch_chunks(self.host_kv, self.host_ids[i % 2], self.pool[i % 2], host_slots=None,
+                         stream=self.side, done=None)
+        self.fetch_done[i % 2].record(self.side)

@@ -188,3 +188,29 @@ def attn_query(w: Workload, t: int, scale: float = 1.0) -> np.ndarray:
 
 def ctx_lens(w: Workload) -> np.ndarray:
     return np.full(w.B, w.N, dtype=np.int32)
+
+
+# ---- placing the K/V store (torch is used for memory only) ----------------
+
+def device_kv_store(w: Workload, device="cuda"):
+    """The K/V store in device memory: torch bf16 [B][C][2][Hkv][T][d],
+    generated request by request on the host and copied over."""
+    import torch
+    out = torch.empty((w.B, w.C, 2, w.Hkv, w.T, w.d), dtype=torch.bfloat16, device=device)
+    n = kv_elems_per_request(w)
+    host = torch.empty(n, dtype=torch.int16).pin_memory()
+    buf = host.numpy().view(np.uint16)
+    for b in range(w.B):
+        kv_fill_request(w, b, buf)
+        out[b].view(-1).view(torch.int16).copy_(host, non_blocking=False)
+    return out
+
+
+def pinned_kv_store(w: Workload):
+    """The K/V store in pinned host memory: torch bf16 [B][C][2][Hkv][T][d]."""
+    import torch
+    out = torch.empty((w.B, w.C, 2, w.Hkv, w.T, w.d), dtype=torch.bfloat16, pin_memory=True)
+    flat = out.view(torch.int16).numpy().view(np.uint16).reshape(w.B, -1)
+    for b in range(w.B):
+        kv_fill_request(w, b, flat[b])
+    return out

@@ -1,0 +1,238 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the same
+seeded inputs: logits and selections bit-exact, sigmoid scores within 1e-6
+relative, attention within max-abs 1e-2 / mean-abs 1e-3 of fp64."""
+import math
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from helpers import check_attention, check_scores, to_dev, to_dev_bf16
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    import lookahead_chunk_sparse_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def W():
+    from synth import workloads
+    return workloads
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ index score
+
+@pytest.mark.parametrize("B,nq,C,d_idx,lo,hi", [
+    (1, 1, 64, 64, -16, 15),
+    (3, 1, 65, 128, -16, 15),
+    (2, 3, 1, 128, -128, 127),
+    (2, 2, 1000, 16, -128, 127),
+    (1, 1, 777, 32, -128, 127),
+    (4, 1, 513, 256, -128, 127),
+    (1, 5, 129, 64, -128, 127),
+])
+def test_index_score_shapes(lsa, oracle_lib, synth_lib, B, nq, C, d_idx, lo, hi):
+    say("index_score", B, nq, C, d_idx)
+    s = synth_lib.stream
+    q = synth_lib.uniform_i8((B, nq, d_idx), 21, s(synth_lib.TAG_MISC, 500 + C), lo, hi)
+    K = synth_lib.uniform_i8((B, C, d_idx), 21, s(synth_lib.TAG_MISC, 600 + C), lo, hi)
+    alpha = 1.0 / (16 * d_idx)
+    logits, scores = lsa.lsa_index_score(to_dev(q), to_dev(K), alpha)
+    L_ref = oracle_lib.index_logits(q, K)
+    assert np.array_equal(logits.cpu().numpy().reshape(L_ref.shape), L_ref)
+    check_scores(scores.cpu().numpy().reshape(L_ref.shape), oracle_lib.index_scores(L_ref, alpha))
+
+
+def test_index_score_extremes(lsa, oracle_lib):
+    """Largest-magnitude logits (+-2^21) and a non-power-of-two alpha."""
+    q = np.full((1, 1, 128), -128, dtype=np.int8)
+    K = np.stack([np.full(128, -128), np.full(128, 127), np.zeros(128), np.full(128, 1)]).astype(np.int8)[None]
+    for alpha in (2.0 ** -11, 0.1, 3e-5):
+        logits, scores = lsa.lsa_index_score(to_dev(q), to_dev(K), alpha)
+        L_ref = oracle_lib.index_logits(q, K)
+        assert np.array_equal(logits.cpu().numpy().reshape(L_ref.shape), L_ref)
+        check_scores(scores.cpu().numpy().reshape(L_ref.shape), oracle_lib.index_scores(L_ref, alpha))
+
+
+@pytest.mark.parametrize("name", ["tiny", "32k", "128k", "500k", "1m_host"])
+def test_index_score_and_selection_workloads(lsa, oracle_lib, W, name):
+    """Every re-selection of every workload: logits and ids bit-exact."""
+    w = W.WORKLOADS[name]
+    K = W.indexer_keys(w)
+    Kd = to_dev(K)
+    for it in range(w.intervals if w.drift else 1):
+        say(name, "interval", it)
+        q = W.indexer_query(w, it)
+        logits, scores = lsa.lsa_index_score(to_dev(q), Kd, w.alpha)
+        ids = lsa.lsa_topk_chunks(logits.view(w.B, w.C), w.k)
+        L_ref, S_ref, ids_ref = oracle_lib.select(q, K, w.k, w.alpha)
+        assert np.array_equal(logits.cpu().numpy().reshape(L_ref.shape), L_ref)
+        check_scores(scores.cpu().numpy().reshape(S_ref.shape), S_ref)
+        got = ids.cpu().numpy()
+        assert np.array_equal(got, ids_ref), f"{name}: {np.sum(got != ids_ref)} ids differ"
+
+
+# ------------------------------------------------------------------ top-k
+
+def _rows(synth_lib, kind, R, C, seed):
+    s = synth_lib.stream(synth_lib.TAG_MISC, 700 + seed)
+    if kind == "random":
+        return synth_lib.uniform_i32((R, C), seed, s, -(2 ** 31), 2 ** 31 - 1)
+    if kind == "narrow":
+        return synth_lib.uniform_i32((R, C), seed, s, -3000, 3000)
+    if kind == "few":
+        return synth_lib.uniform_i32((R, C), seed, s, -2, 2)
+    if kind == "equal":
+        return np.full((R, C), 7, dtype=np.int32)
+    if kind == "extremes":
+        v = synth_lib.uniform_i32((R, C), seed, s, 0, 3)
+        return np.choose(v, [-(2 ** 31), 2 ** 31 - 1, 0, -1]).astype(np.int32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["random", "narrow", "few", "equal", "extremes"])
+@pytest.mark.parametrize("C", [1, 2, 63, 64, 65, 1000, 1024, 1025, 2048, 7813, 16384])
+def test_topk_parity(lsa, oracle_lib, synth_lib, kind, C):
+    R = 3 if C <= 2048 else 1
+    rows = _rows(synth_lib, kind, R, C, seed=C)
+    dl = to_dev(rows)
+    for k in sorted({1, C, max(1, C // 7), max(1, C - 1)}):
+        got = lsa.lsa_topk_chunks(dl, k).cpu().numpy()
+        ref = oracle_lib.topk_chunks(rows.astype(np.int64), k)
+        assert np.array_equal(got, ref), (kind, C, k)
+
+
+@pytest.mark.parametrize("C", [32768, 40000, 65536])
+def test_topk_large_rows(lsa, oracle_lib, synth_lib, C):
+    rows = _rows(synth_lib, "narrow", 1, C, seed=C)
+    for k in (1, C // 10, C):
+        got = lsa.lsa_topk_chunks(to_dev(rows), k).cpu().numpy()
+        assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (C, k)
+
+
+# ------------------------------------------------------------------ attention
+
+def _problem(synth_lib, B, Hq, Hkv, d, C, seed, qscale=1.0):
+    s = synth_lib.stream
+    q = synth_lib.normal_bf16((B, Hq, d), seed, s(synth_lib.TAG_MISC, 800), scale=qscale)
+    kv = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), seed, s(synth_lib.TAG_MISC, 801))
+    return q, kv
+
+
+def _ids(synth_lib, B, C, k, seed):
+    """Ascending distinct chunk ids per request; chunk 0 is always listed so a
+    request with a short context still has a valid token."""
+    out = np.empty((B, k), dtype=np.int32)
+    for b in range(B):
+        out[b] = np.sort(synth_lib.choose(k, C, seed, synth_lib.stream(synth_lib.TAG_MISC, 900 + b)))
+        out[b, 0] = 0
+    return out
+
+
+ATTEND_CASES = [
+    # B, Hq, Hkv, d, C, k, ctx (None = full), n_split, qscale
+    (1, 8, 1, 64, 64, 8, None, 0, 1.0),        # tiny workload shape
+    (4, 64, 8, 128, 40, 32, None, 0, 1.0),     # DeepSeek-V4 GQA shape
+    (4, 64, 8, 128, 40, 32, None, 1, 1.0),     # no split
+    (4, 64, 8, 128, 40, 32, None, 7, 1.0),     # ragged split
+    (4, 64, 8, 128, 40, 32, None, 32, 1.0),    # one chunk per split
+    (2, 64, 8, 128, 20, 20, [1270, 1281], 3, 1.0),  # partial last chunk in both requests
+    (2, 64, 8, 128, 20, 5, [1, 65], 2, 1.0),   # a single valid token / one token past a chunk
+    (3, 64, 8, 128, 30, 1, None, 0, 1.0),      # k = 1
+    (2, 64, 8, 128, 30, 12, None, 0, 8.0),     # sharpened softmax
+    (2, 16, 16, 128, 10, 6, None, 2, 2.0),     # MHA (one query head per KV head)
+    (2, 32, 2, 128, 10, 6, None, 2, 2.0),      # 16 query heads per KV head
+    (2, 12, 4, 64, 10, 6, [600, 333], 2, 2.0), # group of 3, d = 64, partial chunks
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,C,k,ctx,n_split,qscale", ATTEND_CASES)
+def test_attend_parity(lsa, oracle_lib, synth_lib, B, Hq, Hkv, d, C, k, ctx, n_split, qscale):
+    say("attend", B, Hq, Hkv, d, C, k, ctx, n_split, qscale)
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=31 + k, qscale=qscale)
+    ids = _ids(synth_lib, B, C, k, seed=41 + k)
+    ctx = np.full(B, C * 64, dtype=np.int32) if ctx is None else np.array(ctx, dtype=np.int32)
+    scale = 1.0 / math.sqrt(d)
+    out = lsa.lsa_gather_attend(to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx), scale, n_split=n_split)
+    ref = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, scale)
+    # requests without any valid token give 0 on the GPU; the oracle rejects them
+    stats = check_attention(out.cpu().numpy(), ref, "attend")
+    say("  ", stats)
+
+
+def test_attend_no_valid_token_gives_zero(lsa, synth_lib):
+    q, kv = _problem(synth_lib, 2, 8, 1, 64, 4, seed=3)
+    ids = np.array([[2, 3], [0, 1]], dtype=np.int32)
+    ctx = np.array([100, 0], dtype=np.int32)  # request 0: chunks 2,3 start at 128 > 100; request 1: empty
+    out = lsa.lsa_gather_attend(to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx), 0.125, n_split=2)
+    assert (out.cpu().numpy() == 0).all()
+
+
+def test_attend_slots_pool(lsa, oracle_lib, synth_lib):
+    """K/V read from a compact pool at explicit slots, masking by chunk id."""
+    B, Hq, Hkv, d, C, k = 2, 64, 8, 128, 30, 9
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=5)
+    ids = _ids(synth_lib, B, C, k, seed=6)
+    ids[0, -1] = C - 1
+    ctx = np.array([C * 64 - 20, C * 64], dtype=np.int32)
+    perm = np.array([[(j * 4) % k for j in range(k)]] * B, dtype=np.int32)  # slots, a permutation
+    pool = np.zeros((B, k, 2, Hkv, 64, d), dtype=np.uint16)
+    for b in range(B):
+        pool[b, perm[b]] = kv[b, ids[b]]
+    out = lsa.lsa_gather_attend(to_dev_bf16(q), to_dev_bf16(pool), to_dev(ids), to_dev(ctx), 1 / math.sqrt(d),
+                                slots=to_dev(perm))
+    ref = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d))
+    check_attention(out.cpu().numpy(), ref, "slots")
+
+
+def test_attend_deterministic(lsa, synth_lib):
+    """Same inputs, same bits (fixed reduction order)."""
+    B, Hq, Hkv, d, C, k = 4, 64, 8, 128, 40, 32
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=77)
+    ids = _ids(synth_lib, B, C, k, seed=78)
+    args = (to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(np.full(B, C * 64, dtype=np.int32)))
+    a = lsa.lsa_gather_attend(*args, n_split=5).cpu().numpy()
+    b = lsa.lsa_gather_attend(*args, n_split=5).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ fetch
+
+def test_fetch_byte_exact(lsa, oracle_lib, synth_lib):
+    import torch
+    B, C, Hkv, d, k, P = 2, 12, 2, 64, 5, 7
+    host = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), 9, synth_lib.stream(synth_lib.TAG_MISC, 950))
+    ids = np.array([[0, 1, 2, 7, 11], [3, 4, 6, 8, 9]], dtype=np.int32)
+    slots = np.array([[0, 1, 2, 5, 6], [6, 5, 4, 0, 1]], dtype=np.int32)
+    host_t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).pin_memory()
+    pool = torch.zeros((B, P, 2, Hkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    lsa.lsa_fetch_chunks(host_t, torch.from_numpy(ids), pool, host_slots=torch.from_numpy(slots), stream=side)
+    done.record(side)
+    done.synchronize()
+    ref = oracle_lib.fetch_chunks(host, ids, P, slots=slots)
+    assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), ref)
+    # default slots (entry j -> slot j) and the done event of the ABI
+    pool2 = torch.zeros((B, k, 2, Hkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    ev = torch.cuda.Event()
+    ev.record(side)  # create the event before handing it to the library
+    lsa.lsa_fetch_chunks(host_t, torch.from_numpy(ids), pool2, stream=side, done=ev)
+    ev.synchronize()
+    assert np.array_equal(pool2.cpu().view(torch.int16).numpy().view(np.uint16), oracle_lib.fetch_chunks(host, ids, k))
+
+
+def test_fetch_rejects_pageable(lsa):
+    import torch
+    host = torch.zeros((1, 4, 2, 1, 64, 64), dtype=torch.bfloat16)  # not pinned
+    pool = torch.zeros((1, 2, 2, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lsa.LsaError, match="pinned"):
+        lsa.lsa_fetch_chunks(host, torch.tensor([[0, 1]], dtype=torch.int32), pool)
