@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA decode hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: at t = 0 (mod 64) the
+memory-indexer scan and the top-k re-selection, then the gathered-chunk GQA
+decode attention; every step runs the attention.  The default workload is the
+128K-context one: batch 16, 64 query / 8 KV heads, head dim 128, 131,072
+tokens = 2,048 chunks of 64, 276 chunks (13.5%) retained, tau = 64.  Inputs
+are seeded synthetic data (synth/), resident in HBM before timing starts.
+
+Prints one JSON line (rank 0, N = 1):
+  value        decode steps/s over exactly --steps steps (hipGraph replay)
+  roofline     the attention kernel: algorithmic bytes per launch / its mean
+               launch time, timed with HIP events on its own stream, against
+               the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle (tests only otherwise) on a bounded sample of
+               the same workload, on this host's cores
+
+Other modes (used for profiling): --kernel-only (just the attention
+launches), --copy-calibration (a plain device copy of known size, to scale
+hardware byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+METRIC = "LSA decode steps/s + achieved HBM GB/s (fraction of peak), 128K ctx batch 16"
+KERNEL_SRC = os.path.join(ROOT, "lookahead_chunk_sparse_amd", "csrc", "gather_attend.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_128k_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attend_bytes_per_launch(w) -> int:
+    """Algorithmic HBM bytes of one attention launch: the retained K and V
+    tiles of every (request, KV head), the bf16 queries, the fp32 outputs and
+    the chunk ids."""
+    kv = w.B * w.Hkv * w.k * 2 * w.T * w.d * 2
+    q = w.B * w.Hq * w.d * 2
+    out = w.B * w.Hq * w.d * 4
+    ids = w.B * w.k * 4
+    return kv + q + out + ids
+
+
+def step_bytes(w) -> int:
+    """Algorithmic bytes of one decode step: the attention launch plus the
+    indexer scan (every key byte once) amortised over tau steps."""
+    return attend_bytes_per_launch(w) + (w.B * w.C * w.d_idx) // w.tau
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for_current_kernel(w):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_sha() or t.get("workload") != w.name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def setup(w, n_split: int):
+    import torch
+
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    K = torch.from_numpy(W.indexer_keys(w)).to(dev)
+    ctx = torch.from_numpy(W.ctx_lens(w)).to(dev)
+    kv = W.device_kv_store(w, dev)
+    dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split, device=dev)
+    log(f"[bench] inputs placed in HBM in {time.time() - t0:.1f}s (K/V {kv.numel() * 2 / 1e9:.2f} GB)")
+    return dec
+
+
+def make_queries(w, n_steps: int):
+    import torch
+
+    from synth import workloads as W
+    dev = torch.device("cuda:0")
+    q_all = torch.empty((n_steps, w.B, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    for t in range(n_steps):
+        q_all[t].view(torch.int16).copy_(torch.from_numpy(W.attn_query(w, t).view("int16")))
+    n_int = (n_steps + w.tau - 1) // w.tau
+    qidx = [torch.from_numpy(W.indexer_query(w, i)).to(dev) for i in range(n_int)]
+    return q_all, qidx
+
+
+def enqueue_steps(dec, w, q_all, qidx, n_steps, out):
+    for i in range((n_steps + w.tau - 1) // w.tau):
+        ts = range(i * w.tau, min((i + 1) * w.tau, n_steps))
+        dec.run_interval(i, qidx[i], [q_all[t] for t in ts], [out] * len(ts))
+
+
+def capture(dec, w, q_all, qidx, n_steps, out):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        enqueue_steps(dec, w, q_all, qidx, min(n_steps, w.tau), out)  # eager warm-up of every call
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        enqueue_steps(dec, w, q_all, qidx, n_steps, out)
+    return g
+
+
+def time_attention_launches(dec, w, q_all, n_launches: int):
+    """Mean duration of one attention launch, timed with HIP events recorded
+    on the stream the kernel runs on (torch's current stream)."""
+    import torch
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launches)]
+    torch.cuda.synchronize()
+    for j, (a, b) in enumerate(evs):
+        a.record(stream)
+        dec.attend(q_all[j % q_all.shape[0]], 0, out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return statistics.mean(ms), statistics.median(ms), ms
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle on a bounded sample of the same workload: one re-selection
+    (scan + top-k over every request) and as many full attention steps (all
+    requests, all heads) as fit in the time budget.  Returns steps/s scaled
+    from the sample, plus the sample's description."""
+    import numpy as np
+
+    import oracle
+    from synth import workloads as W
+
+    K = W.indexer_keys(w)
+    q_idx = W.indexer_query(w, 0)
+    t0 = time.perf_counter()
+    _, _, ids = oracle.select(q_idx, K, w.k, w.alpha)
+    t_sel = time.perf_counter() - t0
+    kv_sel = np.stack([W.kv_chunks(w, b, ids[b]) for b in range(w.B)])  # not timed: input placement
+    slots = np.tile(np.arange(w.k, dtype=np.int32), (w.B, 1))
+    ctx = W.ctx_lens(w)
+    t_att, n = 0.0, 0
+    while n < 64 and (n == 0 or t_sel + t_att < budget_s):
+        q = W.attn_query(w, n)
+        t0 = time.perf_counter()
+        oracle.gather_attend(q, kv_sel, ids, ctx, w.Hkv, w.sm_scale, slots=slots)
+        t_att += time.perf_counter() - t0
+        n += 1
+    per_step = t_att / n + t_sel / w.tau
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{w.name}: 1 re-selection (B={w.B}, C={w.C}) in {t_sel:.2f}s + {n} full attention "
+                       f"steps (B={w.B}, Hq={w.Hq}, k={w.k} chunks) in {t_att:.2f}s; steps/s = "
+                       f"1/(attention s/step + re-selection s/{w.tau})")}
+
+
+def copy_calibration(n_bytes: int, reps: int):
+    """A plain device-to-device copy of known size (for counter scaling)."""
+    import torch
+    a = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n_bytes, "copy_calibration_bytes_written": n_bytes,
+                      "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="128k")
+    ap.add_argument("--n-split", type=int, default=0, help="attention splits per (request, KV head); 0 = library")
+    ap.add_argument("--kernel-launches", type=int, default=200, help="event-timed attention launches")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 20)
+        return
+
+    import lookahead_chunk_sparse_amd  # noqa: F401  (fails loudly if liblsa.so is missing)
+    from synth import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if w.host_tier:
+        print("the headline bench runs HBM-resident workloads; see tests for the host tier", file=sys.stderr)
+        sys.exit(2)
+    dec = setup(w, args.n_split)
+    n_q = max(args.steps, args.warmup, w.tau)
+    q_all, qidx = make_queries(w, n_q)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
+    from lookahead_chunk_sparse_amd import lsa_gather_attend_default_splits
+    splits = args.n_split or lsa_gather_attend_default_splits(w.B, w.Hkv, w.k)
+
+    if args.kernel_only:
+        dec.reselect(qidx[0], 0)
+        mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
+        gbs = attend_bytes_per_launch(w) / (mean_ms * 1e-3) / 1e9
+        print(json.dumps({"kernel": "attend_split_kernel<128>+combine", "workload": w.name, "n_split": splits,
+                          "launches": args.kernel_launches, "mean_ms": mean_ms, "median_ms": med_ms,
+                          "achieved_GBs": gbs}))
+        return
+
+    # ---- warm-up: W untimed steps ----
+    if args.eager:
+        if args.warmup:
+            enqueue_steps(dec, w, q_all, qidx, args.warmup, out)
+    else:
+        if args.warmup:
+            g_w = capture(dec, w, q_all, qidx, args.warmup, out)
+            g_w.replay()
+        g = capture(dec, w, q_all, qidx, args.steps, out)
+    torch.cuda.synchronize()
+
+    # ---- timed: exactly K steps ----
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    if args.eager:
+        enqueue_steps(dec, w, q_all, qidx, args.steps, out)
+    else:
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    steps_s = 1000.0 / ms_per_step
+    log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {t_wall * 1e3:.2f} ms)")
+
+    # ---- the dominant kernel, event-timed on its own stream ----
+    mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
+    a_bytes = attend_bytes_per_launch(w)
+    achieved = a_bytes / (mean_ms * 1e-3) / 1e9
+    log(f"[bench] attention launch: mean {mean_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
+        f"{achieved:.0f} GB/s algorithmic")
+    traffic = traffic_for_current_kernel(w)
+
+    sb = step_bytes(w)
+    result = {
+        "metric": METRIC,
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name} context decode, one layer: batch {w.B}, {w.Hq} query / {w.Hkv} KV heads, "
+                         f"head dim {w.d}, {w.N} tokens = {w.C} chunks of {w.T}, top-{w.k} chunks "
+                         f"re-selected every {w.tau} steps, int8 indexer dim {w.d_idx}"),
+            "global_batch": w.B,
+            "seq_len": w.N,
+            "retained_chunks": w.k,
+            "n_split": splits,
+            "timing": "eager launches" if args.eager else "hipGraph replay of all steps",
+            "tokens_per_s": round(steps_s * w.B, 1),
+            "step_bytes": sb,
+            "step_GBs": round(sb * steps_s / 1e9, 1),
+            "step_frac_of_hbm_peak": round(sb * steps_s / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gather-attend (split kernel + combine)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": a_bytes,
+            "mean_launch_us": round(mean_ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

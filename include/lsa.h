@@ -148,7 +148,10 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *  sm_scale   softmax scale, normally 1/sqrt(d)
  *  workspace  device buffer of at least
  *             lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
- *             bytes, 256-byte aligned (NULL allowed when that size is 0)
+ *             bytes, 256-byte aligned (NULL allowed when that size is 0);
+ *             scratch for the per-split partial results, no state is kept
+ *             in it between calls.  Calls sharing a workspace must not
+ *             overlap in time (same stream, or otherwise ordered).
  *  n_split    chunk-list splits per (request, KV head); 0 = library choice
  *  out        device fp32 [B][Hq][d]
  *  stream     HIP stream

@@ -13,7 +13,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are kept out of the device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA results in VGPRs: the softmax rescale works on the accumulators
+                # with VALU ops, which cannot read AGPRs directly
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def build(verbose: bool = False) -> str:

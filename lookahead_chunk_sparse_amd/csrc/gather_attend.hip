@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "lsa_kernels.h"
 
@@ -45,6 +46,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSliceTokens = 16;
+constexpr int kListCache = 1024;  // list entries staged in LDS per segment
 
 template <int D>
 struct VRow;  // one lane's share of one V row: D/16 bf16 values
@@ -73,8 +75,6 @@ __device__ inline uint32_t vrow_dword(const VRow<128>& r, int w) {
 }
 __device__ inline uint32_t vrow_dword(const VRow<64>& r, int w) { return w == 0 ? r.v.x : r.v.y; }
 
-__device__ inline void vrow_zero(VRow<128>& r) { r.v = make_uint4(0, 0, 0, 0); }
-__device__ inline void vrow_zero(VRow<64>& r) { r.v = make_uint2(0, 0); }
 
 // Registers of one wave's 16-token slice of one chunk.
 template <int D>
@@ -101,7 +101,91 @@ __device__ inline void load_slice(Slice<D>& s, const uint16_t* ktile, const uint
 __device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 __device__ inline float bf16_value(short b) { return (float)__builtin_bit_cast(__bf16, b); }
 
+__device__ inline uint4 select4(bool ok, uint4 v) {
+    return ok ? v : make_uint4(0, 0, 0, 0);
+}
+__device__ inline void vrow_mask(VRow<128>& r, bool ok) { r.v = select4(ok, r.v); }
+__device__ inline void vrow_mask(VRow<64>& r, bool ok) { r.v = ok ? r.v : make_uint2(0, 0); }
+
+// Online-softmax update of one wave with one 16-token slice; tokens at or
+// past `nvalid` (chunk-relative) are masked.  Straight-line code except for
+// the rescale of O, which only runs when some head's running max grows and
+// issues no memory operation, so the loads in flight are never waited on
+// early.
 template <int D>
+__device__ inline void process_slice(Slice<D>& sl, int nvalid, int first_tok, int i, const bf16x8* qb,
+                                     float scale_log2, float& m_run, float& l_run, f32x4* oacc) {
+    constexpr int KS = D / 32;
+    constexpr int DPL = D / 16;
+    // S^T[slot][head] for this wave's 16 tokens
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sl.k[st]), qb[st], sacc, 0, 0, 0);
+    // lane holds head n, slots 4i+r = tokens first_tok + 4r + i; the K and V
+    // rows of masked tokens may hold anything, so S is replaced and V zeroed
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = first_tok + 4 * r + i < nvalid;
+        sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
+        vrow_mask(sl.v[r], ok);
+    }
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < DPL; ++jj) oacc[jj] *= alpha;
+        m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // nothing valid yet: every p is 0
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    i16x4 phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const short h = bf16_bits(p[r]);
+        phi[r] = h;
+        plo[r] = bf16_bits(p[r] - bf16_value(h));
+    }
+    // A operand of O^T += V^T P^T: element r = V[token 4r+i][DPL*n + jj]
+#pragma unroll
+    for (int jj = 0; jj < DPL; ++jj) {
+        const int w = jj >> 1;
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(vrow_dword(sl.v[1], w), vrow_dword(sl.v[0], w), sel);
+        const uint32_t hi = __builtin_amdgcn_perm(vrow_dword(sl.v[3], w), vrow_dword(sl.v[2], w), sel);
+        const i16x4 av = __builtin_bit_cast(i16x4, make_uint2(lo, hi));
+        oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, phi, oacc[jj], 0, 0, 0);
+        oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, plo, oacc[jj], 0, 0, 0);
+    }
+}
+
+// Merge the 4 waves' (m, l, o) of head h, column dd (log2-domain maxima).
+__device__ inline void merge_waves(const float (*sm_m)[16], const float (*sm_l)[16], const float* sm_o, int h, int dd,
+                                   int D, float& o, float& l, float& mstar) {
+    mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm_m[w][h]);
+    o = 0.f;
+    l = 0.f;
+    if (mstar != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - mstar);
+            o += sc * sm_o[w * 16 * D + h * D + dd];
+            l += sc * sm_l[w][h];
+        }
+    }
+}
+
+template <int D, int NBUF>
 __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     constexpr int KS = D / 32;   // QK MFMA steps over d
     constexpr int DPL = D / 16;  // PV MFMAs (d values per lane per V row)
@@ -120,104 +204,85 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     const int64_t j1 = ((int64_t)(s + 1) * a.k) / a.n_split;
     const int ctx = a.ctx[b];
     const int32_t* ids = a.ids + (int64_t)b * a.k;
-    const int32_t* slots = a.slots ? a.slots + (int64_t)b * a.k : nullptr;
 
     // B operand of S^T = K Q^T: lane (head n, group i) holds q[n][32*st + 8*i .. +8].
     bf16x8 qb[KS];
     {
-        const bool live = n < G;
+        const bool live = n < G;  // lanes of padding heads read head 0 and use zeros
         const uint16_t* qp = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + (live ? n : 0)) * D + 8 * i;
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-            uint4 v = live ? *reinterpret_cast<const uint4*>(qp + 32 * st) : make_uint4(0, 0, 0, 0);
-            qb[st] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int st = 0; st < KS; ++st)
+            qb[st] = __builtin_bit_cast(bf16x8, select4(live, *reinterpret_cast<const uint4*>(qp + 32 * st)));
     }
 
     const int64_t chunk_elems = (int64_t)2 * a.Hkv * kChunkTokens * D;
     const int64_t tile_elems = (int64_t)kChunkTokens * D;
     const uint16_t* kv_b = a.kv + (int64_t)b * a.C_store * chunk_elems + (int64_t)g * tile_elems;
     const int64_t v_off = (int64_t)a.Hkv * tile_elems;
+    const int first_tok = wave * kSliceTokens;
 
     f32x4 oacc[DPL];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < DPL; ++jj) oacc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;  // running max (log2 domain) of head n
     float l_run = 0.f;        // this lane's share of the running sum of head n
 
-    Slice<D> cur, nxt;
-    if (j0 < j1) {
-        const int64_t p = slots ? slots[j0] : ids[j0];
-        const uint16_t* kt = kv_b + p * chunk_elems;
-        load_slice<D>(cur, kt, kt + v_off, wave, lane);
-    }
-    for (int64_t j = j0; j < j1; ++j) {
-        if (j + 1 < j1) {
-            const int64_t p = slots ? slots[j + 1] : ids[j + 1];
-            const uint16_t* kt = kv_b + p * chunk_elems;
-            load_slice<D>(nxt, kt, kt + v_off, wave, lane);
+    // The workgroup's list entries (store position, valid tokens) are staged
+    // in LDS, a segment of up to kListCache entries at a time, so computing a
+    // prefetch address never waits behind the K/V loads in flight.
+    __shared__ int sm_pos[kListCache];
+    __shared__ int sm_nv[kListCache];
+    const int32_t* pos_src = a.slots ? a.slots + (int64_t)b * a.k : ids;
+
+    // Ring of NBUF register buffers: entry e of a segment lives in
+    // buf[e % NBUF]; NBUF - 1 entries are in flight while one is processed.
+    Slice<D> buf[NBUF];
+    int nv[NBUF];
+    // Loads are counted in issue order (vmcnt), so the groups of loads are
+    // kept in program order: a buffer's loads must be older than those of
+    // every buffer issued after it for the waits to stay partial.
+    auto issue = [&](int e, int bi) {
+        nv[bi] = sm_nv[e];
+        const uint16_t* kt = kv_b + (int64_t)sm_pos[e] * chunk_elems;
+        __builtin_amdgcn_sched_barrier(0);
+        load_slice<D>(buf[bi], kt, kt + v_off, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int64_t seg = j0; seg < j1; seg += kListCache) {
+        const int segn = (int)(j1 - seg < kListCache ? j1 - seg : kListCache);
+        __syncthreads();  // the previous segment's entries are no longer read
+        for (int e = threadIdx.x; e < segn; e += kThreads) {
+            const int64_t c = ids[seg + e];
+            const int64_t v = (int64_t)ctx - c * kChunkTokens;
+            sm_pos[e] = pos_src[seg + e];
+            sm_nv[e] = v < 0 ? 0 : v > kChunkTokens ? kChunkTokens : (int)v;
         }
-        // valid tokens of this chunk (uniform across the workgroup)
-        const int64_t c = ids[j];
-        const int64_t nvalid64 = (int64_t)ctx - c * kChunkTokens;
-        const int nvalid = nvalid64 < 0 ? 0 : nvalid64 > kChunkTokens ? kChunkTokens : (int)nvalid64;
-        const int first_tok = wave * kSliceTokens;
-        if (nvalid > first_tok) {
-            // S^T[slot][head] for this wave's 16 tokens
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        __syncthreads();
+        // Every step issues one prefetch (past the segment's end it re-reads
+        // the last entry, never used) and processes one buffer, so the
+        // compiler can count the loads in flight exactly.  Full rounds of
+        // NBUF steps run in a loop with no early exit; the remainder follows.
+        auto step = [&](int e, int u) {
+            const int ep = e + NBUF - 1;
+            issue(ep < segn ? ep : segn - 1, (u + NBUF - 1) % NBUF);
+            process_slice<D>(buf[u], nv[u], first_tok, i, qb, a.scale_log2, m_run, l_run, oacc);
+        };
 #pragma unroll
-            for (int st = 0; st < KS; ++st)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[st]), qb[st], sacc,
-                                                               0, 0, 0);
-            // lane holds head n, slots 4i+r = tokens first_tok + 4r + i
-            float sv[4];
-            const bool partial = nvalid < first_tok + kSliceTokens;
+        for (int u = 0; u < NBUF - 1; ++u) issue(u < segn ? u : segn - 1, u);
+        int e = 0;
+        for (; e + NBUF <= segn; e += NBUF) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sv[r] = sacc[r] * a.scale_log2;
-                if (partial && first_tok + 4 * r + i >= nvalid) {
-                    sv[r] = -INFINITY;
-                    vrow_zero(cur.v[r]);
-                }
-            }
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sv[r] - m_new);
-            l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            m_run = m_new;
-#pragma unroll
-            for (int j2 = 0; j2 < DPL; ++j2) oacc[j2] *= alpha;
-            i16x4 phi, plo;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const short h = bf16_bits(p[r]);
-                phi[r] = h;
-                plo[r] = bf16_bits(p[r] - bf16_value(h));
-            }
-            // A operand of O^T += V^T P^T: element r = V[token 4r+i][DPL*n + jj]
-#pragma unroll
-            for (int jj = 0; jj < DPL; ++jj) {
-                const int w = jj >> 1;
-                const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-                const uint32_t lo = __builtin_amdgcn_perm(vrow_dword(cur.v[1], w), vrow_dword(cur.v[0], w), sel);
-                const uint32_t hi = __builtin_amdgcn_perm(vrow_dword(cur.v[3], w), vrow_dword(cur.v[2], w), sel);
-                const i16x4 av = __builtin_bit_cast(i16x4, make_uint2(lo, hi));
-                oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, phi, oacc[jj], 0, 0, 0);
-                oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, plo, oacc[jj], 0, 0, 0);
-            }
+            for (int u = 0; u < NBUF; ++u) step(e + u, u);
         }
-        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < NBUF - 1; ++u)
+            if (e + u < segn) step(e + u, u);
     }
 
     // ---- merge the 4 waves of the workgroup through LDS ----
     __shared__ float sm_m[kWaves][16];
     __shared__ float sm_l[kWaves][16];
-    __shared__ float sm_o[kWaves][16 * D];
+    __shared__ float sm_o[kWaves * 16 * D];
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (n < G) {
@@ -229,55 +294,76 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int jj = 0; jj < DPL; ++jj) sm_o[wave][n * D + DPL * (4 * i + r) + jj] = oacc[jj][r];
+            for (int jj = 0; jj < DPL; ++jj) sm_o[wave * 16 * D + n * D + DPL * (4 * i + r) + jj] = oacc[jj][r];
     }
     __syncthreads();
 
     const int64_t grp = (int64_t)b * a.Hkv + g;
+    if (a.n_split == 1) {
+        for (int e = threadIdx.x; e < G * D; e += kThreads) {
+            const int h = e / D, dd = e % D;
+            float o, l, mstar;
+            merge_waves(sm_m, sm_l, sm_o, h, dd, D, o, l, mstar);
+            a.out[((int64_t)b * a.Hq + (int64_t)g * G + h) * D + dd] = l > 0.f ? o / l : 0.f;
+        }
+        return;
+    }
+    const int64_t part = grp * a.n_split + s;
     for (int e = threadIdx.x; e < G * D; e += kThreads) {
         const int h = e / D, dd = e % D;
-        float mstar = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mstar = fmaxf(mstar, sm_m[w][h]);
-        float o = 0.f, l = 0.f;
-        if (mstar != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - mstar);
-                o += sc * sm_o[w][h * D + dd];
-                l += sc * sm_l[w][h];
-            }
-        }
-        if (a.n_split == 1) {
-            a.out[((int64_t)b * a.Hq + (int64_t)g * G + h) * D + dd] = l > 0.f ? o / l : 0.f;
-        } else {
-            const int64_t part = grp * a.n_split + s;
-            a.part_o[(part * G + h) * D + dd] = o;
-            if (dd == 0) {
-                a.part_ml[(part * G + h) * 2 + 0] = mstar;
-                a.part_ml[(part * G + h) * 2 + 1] = l;
-            }
+        float o, l, mstar;
+        merge_waves(sm_m, sm_l, sm_o, h, dd, D, o, l, mstar);
+        a.part_o[(part * G + h) * D + dd] = o;
+        if (dd == 0) {
+            a.part_ml[(part * G + h) * 2 + 0] = mstar;
+            a.part_ml[(part * G + h) * 2 + 1] = l;
         }
     }
 }
 
 // Merge the n_split partial (m, l, o) triples of every (request, head):
 // m* = max m_s, o = sum_s 2^(m_s - m*) o_s / sum_s 2^(m_s - m*) l_s.
-__global__ void attend_combine_kernel(AttendArgs a) {
+// One workgroup of d threads per (request, query head).  For NS > 0 (the
+// split count known at compile time) every partial is loaded up front, so
+// the kernel costs one memory latency.  A separate launch: merging inside
+// the split kernel would need agent-scope fences across the XCDs' L2
+// caches, which measured far slower than this launch.
+template <int NS>
+__global__ __launch_bounds__(128) void attend_combine_kernel(AttendArgs a) {
     const int bh = blockIdx.x;  // b * Hq + h
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int g = h / a.G, hh = h % a.G;
     const int dd = threadIdx.x;
     const int64_t base = ((int64_t)b * a.Hkv + g) * a.n_split;
-    float mstar = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) mstar = fmaxf(mstar, a.part_ml[((base + s) * a.G + hh) * 2]);
-    float o = 0.f, l = 0.f;
-    if (mstar != -INFINITY) {
-        for (int s = 0; s < a.n_split; ++s) {
-            const int64_t ps = (base + s) * a.G + hh;
-            const float sc = __builtin_amdgcn_exp2f(a.part_ml[ps * 2] - mstar);
-            l += sc * a.part_ml[ps * 2 + 1];
-            o += sc * a.part_o[ps * a.d + dd];
+    float mstar = -INFINITY, o = 0.f, l = 0.f;
+    if constexpr (NS > 0) {
+        float pm[NS], pl[NS], po[NS];
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) {
+            const int64_t ps = (base + sp) * a.G + hh;
+            pm[sp] = a.part_ml[ps * 2];
+            pl[sp] = a.part_ml[ps * 2 + 1];
+            po[sp] = a.part_o[ps * a.d + dd];
+        }
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp) mstar = fmaxf(mstar, pm[sp]);
+        if (mstar != -INFINITY) {
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp) {
+                const float sc = __builtin_amdgcn_exp2f(pm[sp] - mstar);
+                l += sc * pl[sp];
+                o += sc * po[sp];
+            }
+        }
+    } else {
+        for (int sp = 0; sp < a.n_split; ++sp) mstar = fmaxf(mstar, a.part_ml[((base + sp) * a.G + hh) * 2]);
+        if (mstar != -INFINITY) {
+            for (int sp = 0; sp < a.n_split; ++sp) {
+                const int64_t ps = (base + sp) * a.G + hh;
+                const float sc = __builtin_amdgcn_exp2f(a.part_ml[ps * 2] - mstar);
+                l += sc * a.part_ml[ps * 2 + 1];
+                o += sc * a.part_o[ps * a.d + dd];
+            }
         }
     }
     a.out[(int64_t)bh * a.d + dd] = l > 0.f ? o / l : 0.f;
@@ -285,32 +371,74 @@ __global__ void attend_combine_kernel(AttendArgs a) {
 
 }  // namespace
 
+// Register-ring size of the split kernel: 3 unless LSA_ATTEND_DEPTH (2, 3
+// or 4) overrides it for tuning.  Read once per process.
+int attend_pipeline_depth() {
+    static const int depth = [] {
+        const char* e = getenv("LSA_ATTEND_DEPTH");
+        const int v = e ? atoi(e) : 3;
+        return (v >= 2 && v <= 4) ? v : 3;
+    }();
+    return depth;
+}
+
 int attend_default_splits(int B, int Hkv, int k) {
-    // Aim at one full wave of workgroups: 256 CUs x 2 resident workgroups.
+    // About one workgroup per CU (256): with every K/V byte read exactly once,
+    // fewer and longer streams keep HBM fuller than more and shorter ones
+    // (measured on the 128K workload: 256 workgroups beat 128 and 512+).
     const int64_t groups = (int64_t)B * Hkv;
-    int64_t s = (512 + groups / 2) / groups;
+    int64_t s = (256 + groups / 2) / groups;
     if (s < 1) s = 1;
     if (s > k) s = k;
     return (int)s;
 }
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: [partial O][partial (m, l)], the second region 256-byte
+// aligned; nothing when there is a single split.
 size_t attend_workspace_bytes(int B, int Hkv, int G, int d, int n_split) {
     if (n_split <= 1) return 0;
     const size_t parts = (size_t)B * Hkv * n_split * G;
-    const size_t o_bytes = parts * d * sizeof(float);
-    const size_t o_round = (o_bytes + 255) & ~(size_t)255;
-    return o_round + parts * 2 * sizeof(float);
+    return round256(parts * d * sizeof(float)) + parts * 2 * sizeof(float);
+}
+
+void attend_workspace_carve(AttendArgs& a, void* workspace) {
+    char* p = static_cast<char*>(workspace);
+    const size_t parts = (size_t)a.B * a.Hkv * a.n_split * a.G;
+    a.part_o = reinterpret_cast<float*>(p);
+    p += round256(parts * a.d * sizeof(float));
+    a.part_ml = reinterpret_cast<float*>(p);
+}
+
+template <int D>
+void launch_split(const AttendArgs& a, dim3 grid, hipStream_t stream) {
+    switch (a.depth) {
+        case 2: hipLaunchKernelGGL((attend_split_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((attend_split_kernel<D, 4>), grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((attend_split_kernel<D, 3>), grid, dim3(kThreads), 0, stream, a); break;
+    }
 }
 
 hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * a.n_split));
     if (a.d == 128)
-        hipLaunchKernelGGL(attend_split_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+        launch_split<128>(a, grid, stream);
     else
-        hipLaunchKernelGGL(attend_split_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+        launch_split<64>(a, grid, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(a.d), 0, stream, a);
+    const dim3 cgrid((unsigned)((int64_t)a.B * a.Hq)), cblock(a.d);
+    switch (a.n_split) {
+        case 2: hipLaunchKernelGGL(attend_combine_kernel<2>, cgrid, cblock, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(attend_combine_kernel<3>, cgrid, cblock, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL(attend_combine_kernel<4>, cgrid, cblock, 0, stream, a); break;
+        case 5: hipLaunchKernelGGL(attend_combine_kernel<5>, cgrid, cblock, 0, stream, a); break;
+        case 6: hipLaunchKernelGGL(attend_combine_kernel<6>, cgrid, cblock, 0, stream, a); break;
+        case 7: hipLaunchKernelGGL(attend_combine_kernel<7>, cgrid, cblock, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL(attend_combine_kernel<8>, cgrid, cblock, 0, stream, a); break;
+        default: hipLaunchKernelGGL(attend_combine_kernel<0>, cgrid, cblock, 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -145,16 +145,12 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     a.d = d;
     a.k = k;
     a.n_split = n_split;
+    a.depth = lsa::attend_pipeline_depth();
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     a.out = out;
     a.part_o = nullptr;
     a.part_ml = nullptr;
-    if (need > 0) {
-        const size_t parts = (size_t)B * Hkv * n_split * G;
-        const size_t o_round = (parts * d * sizeof(float) + 255) & ~(size_t)255;
-        a.part_o = static_cast<float*>(workspace);
-        a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_round);
-    }
+    if (need > 0) lsa::attend_workspace_carve(a, workspace);
     hipError_t e = lsa::launch_gather_attend(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gather-attend launch");
     return ok();

@@ -26,6 +26,7 @@ struct AttendArgs {
     const int32_t* slots;   // [B][k] or nullptr
     const int32_t* ctx;     // [B]
     int B, Hq, Hkv, G, d, k, n_split;
+    int depth;              // chunks in flight per wave + 1 (register ring size)
     float scale_log2;       // sm_scale * log2(e)
     float* part_o;          // [B][Hkv][n_split][G][d]      (n_split > 1)
     float* part_ml;         // [B][Hkv][n_split][G][2]      (n_split > 1)
@@ -33,7 +34,9 @@ struct AttendArgs {
 };
 
 int attend_default_splits(int B, int Hkv, int k);
+int attend_pipeline_depth();
 size_t attend_workspace_bytes(int B, int Hkv, int G, int d, int n_split);
+void attend_workspace_carve(AttendArgs& a, void* workspace);
 hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream);
 
 }  // namespace lsa

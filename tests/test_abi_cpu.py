@@ -110,9 +110,9 @@ def test_workspace_size_rules(lsa):
     a = lsa.lsa_gather_attend_workspace_size(16, 64, 8, 128, 276, 4)
     b = lsa.lsa_gather_attend_workspace_size(16, 64, 8, 128, 276, 8)
     assert 0 < a < b
-    # partial O (B*Hkv*splits*G*d fp32, rounded to 256 B) + (m, l) pairs
+    # partial O (B*Hkv*splits*G*d fp32, rounded to 256 B), then the (m, l) pairs
     parts = 16 * 8 * 4 * 8
-    assert a == ((parts * 128 * 4 + 255) // 256) * 256 + parts * 2 * 4
+    assert a == (parts * 128 * 4 + 255) // 256 * 256 + parts * 2 * 4
     # splits are capped at k
     assert lsa.lsa_gather_attend_workspace_size(1, 8, 1, 64, 3, 50) == lsa.lsa_gather_attend_workspace_size(
         1, 8, 1, 64, 3, 3)

@@ -1,0 +1,59 @@
+"""The decode interval captured as a HIP graph (the way the benchmark times
+it) gives, on every replay, the bits of the same work launched eagerly --
+with other eager work and synchronisations between replays."""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from helpers import to_dev, to_dev_bf16
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.mark.parametrize("n_split", [0, 3])
+def test_graph_replays_match_eager(n_split):
+    import torch
+
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"]
+    dev = torch.device("cuda")
+    K = to_dev(W.indexer_keys(w))
+    ctx = to_dev(W.ctx_lens(w))
+    kv = W.device_kv_store(w, dev)
+    dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split)
+    steps = 8
+    qs = [to_dev_bf16(W.attn_query(w, t)) for t in range(steps)]
+    qidx = to_dev(W.indexer_query(w, 0))
+    outs = [torch.zeros((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for _ in range(steps)]
+
+    dec.run_interval(0, qidx, qs, outs)  # eager
+    torch.cuda.synchronize()
+    eager = [o.cpu().numpy().copy() for o in outs]
+    ids_eager = dec.sel_ids[0].cpu().numpy().copy()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dec.run_interval(0, qidx, qs, outs)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device=dev)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        dec.sel_ids[0].fill_(-1)
+        junk.mul_(1.0001)            # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(dec.sel_ids[0].cpu().numpy(), ids_eager), f"replay {rep}: selection"
+        for t in range(steps):
+            assert np.array_equal(outs[t].cpu().numpy(), eager[t]), f"replay {rep}, step {t}"
+    # and eager again after the replays
+    dec.run_interval(0, qidx, qs, outs)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        assert np.array_equal(outs[t].cpu().numpy(), eager[t])
