@@ -192,6 +192,41 @@ def copy_calibration(n_bytes: int, reps: int):
                       "reps": reps}))
 
 
+def score_sweep(nqs, C: int, d_idx: int, launches: int):
+    """Batched indexer scoring: nq query rows sharing one key set of C chunks.
+    Times the int8-MFMA kernel and the GEMV kernel on the same shapes
+    (selected through the library's dispatch threshold)."""
+    import torch
+
+    import lookahead_chunk_sparse_amd as lsa
+    from synth import TAG_MISC, stream, uniform_i8
+    dev = torch.device("cuda:0")
+    K = torch.from_numpy(uniform_i8((1, C, d_idx), 0, stream(TAG_MISC, 1), -16, 15)).to(dev)
+    for nq in nqs:
+        q = torch.from_numpy(uniform_i8((1, nq, d_idx), 0, stream(TAG_MISC, 2), -16, 15)).to(dev)
+        logits = torch.empty((1, nq, C), dtype=torch.int32, device=dev)
+        scores = torch.empty((1, nq, C), dtype=torch.float32, device=dev)
+        row = {"nq": nq, "C": C, "d_idx": d_idx}
+        for path, thr in (("gemv", "1000000000"), ("mfma", "1")):
+            os.environ["LSA_SCORE_MFMA_MIN_NQ"] = thr
+            for _ in range(5):
+                lsa.lsa_index_score(q, K, 1.0 / (16 * d_idx), logits=logits, scores=scores)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(launches):
+                lsa.lsa_index_score(q, K, 1.0 / (16 * d_idx), logits=logits, scores=scores)
+            e.record()
+            torch.cuda.synchronize()
+            us = s.elapsed_time(e) * 1e3 / launches
+            ops = 2.0 * nq * C * d_idx
+            byts = C * d_idx + nq * d_idx + nq * C * 8
+            row[path] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 2), "GBs": round(byts / us / 1e3, 1)}
+        os.environ.pop("LSA_SCORE_MFMA_MIN_NQ", None)
+        row["int8_peak_TOPS"] = 5000.0
+        print(json.dumps(row), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +240,10 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--score-sweep", action="store_true",
+                    help="batched indexer scoring: MFMA vs GEMV kernel over nq (one key set)")
+    ap.add_argument("--score-nq", default="1,2,4,8,16,32,64,128,256,512",
+                    help="query rows for --score-sweep (comma list)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -218,6 +257,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 20)
+        return
+    if args.score_sweep:
+        import lookahead_chunk_sparse_amd  # noqa: F401
+        score_sweep([int(x) for x in args.score_nq.split(",")], 16384, 128, 50)
         return
 
     import lookahead_chunk_sparse_amd  # noqa: F401  (fails loudly if liblsa.so is missing)

@@ -80,6 +80,32 @@ def test_index_score_and_selection_workloads(lsa, oracle_lib, W, name):
         assert np.array_equal(got, ids_ref), f"{name}: {np.sum(got != ids_ref)} ids differ"
 
 
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+@pytest.mark.parametrize("B,nq,C,d_idx", [
+    (1, 16, 1, 128), (2, 17, 15, 128), (1, 64, 1000, 128), (3, 65, 17, 64), (1, 256, 16384, 128),
+    (2, 33, 513, 256), (1, 128, 2048, 64),
+])
+def test_batched_scoring(lsa, oracle_lib, synth_lib, monkeypatch, path, B, nq, C, d_idx):
+    """Many query rows sharing a request's keys: the int8-MFMA kernel and the
+    GEMV kernel (forced through the dispatch threshold) both match."""
+    monkeypatch.setenv("LSA_SCORE_MFMA_MIN_NQ", "1" if path == "mfma" else "1000000")
+    s = synth_lib.stream
+    q = synth_lib.uniform_i8((B, nq, d_idx), 23, s(synth_lib.TAG_MISC, 1500 + nq), -128, 127)
+    K = synth_lib.uniform_i8((B, C, d_idx), 23, s(synth_lib.TAG_MISC, 1600 + C), -128, 127)
+    K[0, 0] = -128
+    q[0, 0] = -128  # the largest logit, 2^21 at d_idx = 128
+    alpha = 0.1 / d_idx
+    logits, scores = lsa.lsa_index_score(to_dev(q), to_dev(K), alpha)
+    L_ref = oracle_lib.index_logits(q, K)
+    assert np.array_equal(logits.cpu().numpy().reshape(L_ref.shape), L_ref)
+    check_scores(scores.cpu().numpy().reshape(L_ref.shape), oracle_lib.index_scores(L_ref, alpha))
+    # each row's selection too (the oracle's rank-count top-k is quadratic in
+    # C: on the largest rows only the first 4 are compared)
+    ids = lsa.lsa_topk_chunks(logits, max(1, C // 10)).cpu().numpy().reshape(B * nq, -1)
+    rows = B * nq if C <= 2048 else 4
+    assert np.array_equal(ids[:rows], oracle_lib.topk_chunks(L_ref[:rows], max(1, C // 10)))
+
+
 # ------------------------------------------------------------------ top-k
 
 def _rows(synth_lib, kind, R, C, seed):
