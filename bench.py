@@ -179,6 +179,99 @@ def cpu_baseline(w, budget_s: float):
                        f"1/(attention s/step + re-selection s/{w.tau})")}
 
 
+def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_split: int = 0, delta=None):
+    """The host-tier workload: the whole K/V in pinned host memory, selected
+    chunks fetched into an HBM pool on a side stream every tau steps (lag 1,
+    two pool buffers), attention on the pool.  Eager launches.  The timed
+    steps continue after the warm-up intervals, so they show the steady state
+    where each interval's fetch overlaps the previous selection's attention.
+    Also reports each fetch method alone (HIP events on the side stream): the
+    host-to-HBM bandwidth, PCIe-inclusive."""
+    import torch
+
+    from lookahead_chunk_sparse_amd import lsa_fetch_chunks, lsa_fetch_chunks_pull
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    K = torch.from_numpy(W.indexer_keys(w)).to(dev)
+    ctx = torch.from_numpy(W.ctx_lens(w)).to(dev)
+    host_kv = W.pinned_kv_store(w)
+    dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, host_kv=host_kv, fetch=fetch,
+                     fetch_grid=fetch_grid, n_split=n_split, delta=delta, device=dev)
+    log(f"[bench] pinned host K/V {host_kv.numel() * 2 / 1e9:.2f} GB placed in {time.time() - t0:.1f}s")
+    n_warm_int = max(1, (warmup + w.tau - 1) // w.tau)
+    n_time_int = max(1, steps // w.tau)
+    q_all, qidx = make_queries(w, (n_warm_int + n_time_int) * w.tau)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+
+    # each fetch method alone
+    dec.reselect(qidx[0], 0)
+    ids_d = dec.sel_ids[0]
+    ids_h = ids_d.cpu()
+    if dec.delta:  # selection 0 needs its pool slots before attention reads through them
+        from lookahead_chunk_sparse_amd import lsa_pool_assign
+        lsa_pool_assign(None, None, ids_d, 2 * w.k, new_slots=dec.sel_slots[0], fetch_slots=dec.fetch_slots[0])
+    pool0 = dec.pool[0][:, :w.k]
+    fetch_bytes = w.B * w.k * w.chunk_bytes
+
+    def timed(fn, reps=3):
+        ms = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(dec.side)
+            fn()
+            b.record(dec.side)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return statistics.median(ms[1:])
+
+    pool0 = pool0.contiguous() if not pool0.is_contiguous() else pool0
+    alone = {"memcpy": timed(lambda: lsa_fetch_chunks(host_kv, ids_h, pool0, stream=dec.side))}
+    for g in (8, 16, 64):
+        alone[f"pull_grid{g}"] = timed(lambda: lsa_fetch_chunks_pull(host_kv, ids_d, pool0, grid=g,
+                                                                     stream=dec.side))
+    fetch_alone = {k: {"ms": round(v, 2), "GBs": round(fetch_bytes / (v * 1e-3) / 1e9, 1)} for k, v in alone.items()}
+    mean_att, _, _ = time_attention_launches(dec, w, q_all, 50)
+
+    def run(i0, n):
+        for i in range(i0, i0 + n):
+            ts = range(i * w.tau, (i + 1) * w.tau)
+            dec.run_interval(i, qidx[i], [q_all[t] for t in ts], [out] * len(ts))
+
+    run(0, n_warm_int)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    run(n_warm_int, n_time_int)
+    end.record()
+    dec.join()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    n_steps = n_time_int * w.tau
+    fetched = None
+    if dec.delta:
+        last = n_warm_int + n_time_int - 1
+        fetched = round(float((dec.fetch_slots[last % 2] >= 0).float().mean()), 4)
+    res = {
+        "metric": "LSA host-tier decode steps/s, 1M ctx batch 4 (selected chunks fetched from pinned host memory)",
+        "value": round(1000.0 * n_steps / ms_total, 2), "unit": "steps/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": n_warm_int * w.tau, "ms_per_step": round(ms_total / n_steps, 5), "higher_is_better": True,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {w.B}, {w.C} chunks of {w.T}, top-{w.k} fetched every {w.tau} "
+                               f"steps into a two-buffer HBM pool (lag 1), steady state after the warm-up",
+                   "fetch": fetch, "fetch_grid": fetch_grid or 16, "n_split": dec.n_split or "library default",
+                   "delta_fetch": dec.delta, "fetched_fraction_last_interval": fetched,
+                   "fetch_bytes_per_reselect": fetch_bytes,
+                   "fetch_alone": fetch_alone,
+                   "attention_us_per_step_alone": round(mean_att * 1e3, 2),
+                   "attention_GBs_alone": round(attend_bytes_per_launch(w) / (mean_att * 1e-3) / 1e9, 1),
+                   "interval_ms": round(ms_total / n_time_int, 2)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(n_bytes: int, reps: int):
     """A plain device-to-device copy of known size (for counter scaling)."""
     import torch
@@ -240,6 +333,10 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--fetch", default="pull", choices=("pull", "memcpy"), help="host-tier fetch method")
+    ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
+    ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
+    ap.add_argument("--drift", action="store_true", help="host tier: a fresh indexer query every interval")
     ap.add_argument("--score-sweep", action="store_true",
                     help="batched indexer scoring: MFMA vs GEMV kernel over nq (one key set)")
     ap.add_argument("--score-nq", default="1,2,4,8,16,32,64,128,256,512",
@@ -267,9 +364,12 @@ def main():
     from synth import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.drift:
+        w = w.replace(drift=True, n_golden=min(w.n_golden, w.C // max(1, (args.steps + args.warmup) // w.tau + 1)))
     if w.host_tier:
-        print("the headline bench runs HBM-resident workloads; see tests for the host tier", file=sys.stderr)
-        sys.exit(2)
+        host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
+                        False if args.no_delta else None)
+        return
     dec = setup(w, args.n_split)
     n_q = max(args.steps, args.warmup, w.tau)
     q_all, qidx = make_queries(w, n_q)

@@ -193,6 +193,70 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
                             const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
                             int32_t d, int32_t k, hipStream_t side_stream, hipEvent_t done);
 
+/*
+ * lsa_fetch_chunks_pull -- the same host-tier fetch as lsa_fetch_chunks, done
+ * by a kernel that reads the pinned host memory through the GPU's mapping of
+ * it (a gather over the host link) instead of one DMA copy per run.
+ *
+ * Defined by: the same passages as lsa_fetch_chunks.  For every request b
+ * and entry j:  pool_kv[b][slot] := host_kv[b][chunk_ids[b][j]]  with
+ * slot = slots[b][j] (NULL: slot j).  The ids and slots are read on the GPU,
+ * so the fetch can follow lsa_topk_chunks on the device with no host round
+ * trip, and can be captured in a HIP graph.  An entry whose id is outside
+ * [0, C) or whose slot is outside [0, P) is skipped (its slot is left as it
+ * was); the kernel never reads or writes outside the two buffers.
+ *
+ *  host_kv    pinned host bf16 [B][C][2][Hkv][64][d] (hipHostMalloc; its
+ *             device mapping is looked up with hipHostGetDevicePointer)
+ *  C          chunks per request in host_kv
+ *  chunk_ids  device int32 [B][k]
+ *  slots      device int32 [B][k] or NULL (k <= P then)
+ *  pool_kv    device bf16 [B][P][2][Hkv][64][d]
+ *  B, Hkv, k >= 1; d = 64 or 128
+ *  grid       workgroups of the gather (0 = 16).  The link is the bound:
+ *             8-16 workgroups already reach it (about 57 GB/s on MI355X),
+ *             and every workgroup parked on long host-link reads slows the
+ *             kernels that share its compute unit
+ *  stream     HIP stream (normally a side stream, so the copy overlaps
+ *             attention on the main stream)
+ * host_kv and pool_kv need 16-byte alignment.
+ */
+lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32_t* chunk_ids, const int32_t* slots,
+                                 uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv, int32_t d, int32_t k,
+                                 int32_t grid, hipStream_t stream);
+
+/*
+ * lsa_pool_assign -- HBM pool slots for a delta fetch.
+ *
+ * Defined by: LSA keeps in GPU memory only the recalled chunks and evicts the
+ * others to CPU memory (paperlayer.ai summary, 2.1 Architecture), fetching
+ * the critical chunks ahead of the next window (sergiiob.dev handbook, The
+ * Neural Memory Indexer, item 3).  Between two selections, the chunks kept
+ * by both need no copy.  For every request b, with S_prev = prev_ids[b]
+ * held at prev_slots[b] and S_new = new_ids[b]:
+ *   - a chunk of S_new that is also in S_prev keeps its slot
+ *     (new_slots = that slot, fetch_slots = -1: nothing to copy);
+ *   - the r-th chunk of S_new, in ascending id order, that is not in S_prev
+ *     gets the r-th lowest slot of [0, P) that no entry of S_prev holds
+ *     (new_slots = fetch_slots = that slot).
+ * Passing fetch_slots as the slots of lsa_fetch_chunks_pull then copies
+ * exactly the new chunks (entries with slot -1 are skipped), and new_slots
+ * are the slots lsa_gather_attend reads S_new from.  S_prev's slots stay
+ * untouched, so attention over S_prev may run while S_new is fetched.
+ *
+ *  prev_ids    device int32 [B][n_prev], ascending within each row (as
+ *              lsa_topk_chunks writes them); may be NULL when n_prev = 0
+ *  prev_slots  device int32 [B][n_prev], distinct within a row, in [0, P)
+ *  n_prev      0 for the first selection (every chunk is new)
+ *  new_ids     device int32 [B][k], ascending within each row
+ *  P           pool slots per request, >= n_prev + k;
+ *              (n_prev + P) * 4 + P <= 65536 (LSA_ERR_UNSUPPORTED otherwise)
+ *  new_slots, fetch_slots  device int32 [B][k] outputs
+ */
+lsa_status lsa_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int32_t n_prev, const int32_t* new_ids,
+                           int32_t B, int32_t k, int64_t P, int32_t* new_slots, int32_t* fetch_slots,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

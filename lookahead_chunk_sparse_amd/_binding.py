@@ -25,7 +25,7 @@ CHUNK_TOKENS = 64
 # Every symbol include/lsa.h declares.
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks",
            "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits", "lsa_gather_attend",
-           "lsa_fetch_chunks")
+           "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_pool_assign")
 
 
 class LsaError(RuntimeError):
@@ -60,6 +60,10 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend.restype = ctypes.c_int
     L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
     L.lsa_fetch_chunks.restype = ctypes.c_int
+    L.lsa_fetch_chunks_pull.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
+    L.lsa_fetch_chunks_pull.restype = ctypes.c_int
+    L.lsa_pool_assign.argtypes = [vp, vp, i32, vp, i32, i32, i64, vp, vp, vp]
+    L.lsa_pool_assign.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -191,3 +195,43 @@ def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_k
         ev = done.cuda_event if hasattr(done, "cuda_event") else int(done)
     _check(load_library().lsa_fetch_chunks(_ptr(host_kv), C, _ptr(host_chunk_ids), _ptr(host_slots),
                                            _ptr(pool_kv), P, B, Hkv, d, k, _stream(stream), ev))
+
+
+def lsa_fetch_chunks_pull(host_kv: torch.Tensor, chunk_ids: torch.Tensor, pool_kv: torch.Tensor,
+                          slots: torch.Tensor | None = None, grid: int = 0, stream=None):
+    """host_kv pinned bf16 [B][C][2][Hkv][64][d]; chunk_ids (and slots) device
+    int32 [B][k]; pool_kv device bf16 [B][P][2][Hkv][64][d]."""
+    _need(host_kv, torch.bfloat16, "host_kv", 6)
+    _need(pool_kv, torch.bfloat16, "pool_kv", 6)
+    _need(chunk_ids, torch.int32, "chunk_ids", 2)
+    if not chunk_ids.is_cuda or (slots is not None and not slots.is_cuda):
+        raise ValueError("chunk ids and slots for the pull fetch must be device tensors")
+    if slots is not None:
+        _need(slots, torch.int32, "slots", 2)
+    B, C, _, Hkv, T, d = host_kv.shape
+    P = pool_kv.shape[1]
+    k = chunk_ids.shape[1]
+    _check(load_library().lsa_fetch_chunks_pull(_ptr(host_kv), C, _ptr(chunk_ids), _ptr(slots), _ptr(pool_kv), P,
+                                                B, Hkv, d, k, grid, _stream(stream)))
+
+
+def lsa_pool_assign(prev_ids, prev_slots, new_ids: torch.Tensor, P: int, new_slots=None, fetch_slots=None,
+                    stream=None):
+    """Slots for S_new given S_prev (ids [B][n_prev] at slots [B][n_prev], or
+    None for the first selection).  Returns (new_slots, fetch_slots), int32 [B][k]."""
+    _need(new_ids, torch.int32, "new_ids", 2)
+    B, k = new_ids.shape
+    n_prev = 0
+    if prev_ids is not None:
+        _need(prev_ids, torch.int32, "prev_ids", 2)
+        _need(prev_slots, torch.int32, "prev_slots", 2)
+        n_prev = prev_ids.shape[1]
+        if prev_ids.shape[0] != B or tuple(prev_slots.shape) != tuple(prev_ids.shape):
+            raise ValueError("prev_ids / prev_slots shapes do not match")
+    if new_slots is None:
+        new_slots = torch.empty((B, k), dtype=torch.int32, device=new_ids.device)
+    if fetch_slots is None:
+        fetch_slots = torch.empty((B, k), dtype=torch.int32, device=new_ids.device)
+    _check(load_library().lsa_pool_assign(_ptr(prev_ids), _ptr(prev_slots), n_prev, _ptr(new_ids), B, k, P,
+                                          _ptr(new_slots), _ptr(fetch_slots), _stream(stream)))
+    return new_slots, fetch_slots

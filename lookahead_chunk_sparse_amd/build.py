@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblsa.so")
-SOURCES = ["lsa_abi.hip", "index_score.hip", "topk_chunks.hip", "gather_attend.hip"]
+SOURCES = ["lsa_abi.hip", "index_score.hip", "topk_chunks.hip", "gather_attend.hip", "fetch_pull.hip",
+           "pool_assign.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are kept out of the device code.

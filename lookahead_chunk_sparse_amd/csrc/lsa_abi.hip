@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdarg.h>
+#include <limits.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -201,6 +202,55 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
         hipError_t e = hipEventRecord(done, side_stream);
         if (e != hipSuccess) return hip_fail(e, "fetch event record");
     }
+    return ok();
+}
+
+lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32_t* chunk_ids, const int32_t* slots,
+                                 uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv, int32_t d, int32_t k,
+                                 int32_t grid, hipStream_t stream) {
+    if (!host_kv || !chunk_ids || !pool_kv)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv, chunk_ids and pool_kv are required");
+    if (C < 1 || P < 1 || B < 1 || Hkv < 1 || k < 1 || grid < 0)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, k must be >= 1 and grid >= 0");
+    if (d != 64 && d != 128) return fail(LSA_ERR_UNSUPPORTED, "d=%d: supported head dims are 64 and 128", d);
+    if (!slots && k > P) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d > P=%lld with default slots", k, (long long)P);
+    if ((int64_t)B * k >= ((int64_t)1 << 31)) return fail(LSA_ERR_INVALID_ARGUMENT, "B*k must be < 2^31");
+    if (!aligned(host_kv, 16) || !aligned(pool_kv, 16) || !aligned(chunk_ids, 4) || (slots && !aligned(slots, 4)))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv/pool_kv need 16-byte, ids/slots 4-byte alignment");
+    // The kernel reads host_kv through the GPU's mapping of pinned memory.
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof attr);
+    hipError_t pe = hipPointerGetAttributes(&attr, host_kv);
+    if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv is not pinned host memory (allocate it with hipHostMalloc)");
+    }
+    void* dev_view = nullptr;
+    pe = hipHostGetDevicePointer(&dev_view, const_cast<uint16_t*>(host_kv), 0);
+    if (pe != hipSuccess || !dev_view) {
+        (void)hipGetLastError();
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv is not mapped into the device address space");
+    }
+    hipError_t e = lsa::launch_fetch_pull(static_cast<const uint16_t*>(dev_view), C, chunk_ids, slots, pool_kv, P, B,
+                                          Hkv, d, k, grid ? grid : 16, stream);
+    if (e != hipSuccess) return hip_fail(e, "fetch-pull launch");
+    return ok();
+}
+
+lsa_status lsa_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int32_t n_prev, const int32_t* new_ids,
+                           int32_t B, int32_t k, int64_t P, int32_t* new_slots, int32_t* fetch_slots,
+                           hipStream_t stream) {
+    if (!new_ids || !new_slots || !fetch_slots || (n_prev > 0 && (!prev_ids || !prev_slots)))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "new_ids, new_slots, fetch_slots (and prev_* when n_prev > 0) are required");
+    if (B < 1 || k < 1 || n_prev < 0) return fail(LSA_ERR_INVALID_ARGUMENT, "B, k must be >= 1 and n_prev >= 0");
+    if (P < (int64_t)n_prev + k)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "P=%lld must be >= n_prev + k = %d", (long long)P, n_prev + k);
+    if (P > INT32_MAX || lsa::pool_assign_lds_bytes(n_prev, (int)P) > 65536)
+        return fail(LSA_ERR_UNSUPPORTED, "n_prev=%d, P=%lld: the assignment needs (n_prev + P) * 4 + P <= 65536 bytes",
+                    n_prev, (long long)P);
+    hipError_t e = lsa::launch_pool_assign(prev_ids, prev_slots, n_prev, new_ids, B, k, (int)P, new_slots, fetch_slots,
+                                           stream);
+    if (e != hipSuccess) return hip_fail(e, "pool-assign launch");
     return ok();
 }
 

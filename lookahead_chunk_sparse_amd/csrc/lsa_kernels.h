@@ -39,4 +39,13 @@ size_t attend_workspace_bytes(int B, int Hkv, int G, int d, int n_split);
 void attend_workspace_carve(AttendArgs& a, void* workspace);
 hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream);
 
+// ---- host-tier fetch as a device-side gather over the host link ----
+hipError_t launch_fetch_pull(const uint16_t* host_kv_dev, int64_t C, const int32_t* ids, const int32_t* slots,
+                             uint16_t* pool, int64_t P, int B, int Hkv, int d, int k, int grid, hipStream_t stream);
+
+// ---- pool-slot assignment for a delta fetch ----
+size_t pool_assign_lds_bytes(int n_prev, int P);
+hipError_t launch_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int n_prev, const int32_t* new_ids,
+                              int B, int k, int P, int32_t* new_slots, int32_t* fetch_slots, hipStream_t stream);
+
 }  // namespace lsa

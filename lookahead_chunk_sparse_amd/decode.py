@@ -15,7 +15,13 @@ Two placements of the K/V:
     i decodes with selection i-1 (the handbook page's asynchronous prefetch;
     the summary's eviction of non-recalled entries to CPU), so the copy
     overlaps attention.  Two pool buffers alternate; the first interval waits
-    for its own fetch.
+    for its own fetch.  The copy is either a device-side gather that reads
+    the selected ids on the GPU (fetch="pull", the default: no host round
+    trip, graph-capturable) or one DMA copy per run of chunks issued from the
+    host (fetch="memcpy": the ids are copied to the host first).
+    With delta=True (pull only, the default) one pool of 2k slots replaces the
+    two buffers: chunks selected again keep their slot and only new chunks
+    are copied, into slots the selection being attended over does not hold.
 
 This module only orders calls into liblsa.so on HIP streams and records
 events; it computes nothing itself.
@@ -26,7 +32,8 @@ import math
 
 import torch
 
-from ._binding import (alloc_workspace, lsa_fetch_chunks, lsa_gather_attend, lsa_index_score, lsa_topk_chunks)
+from ._binding import (alloc_workspace, lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend, lsa_index_score,
+                       lsa_pool_assign, lsa_topk_chunks)
 
 TAU = 64
 
@@ -47,7 +54,8 @@ class LsaDecoder:
 
     def __init__(self, *, k_idx: torch.Tensor, ctx_len: torch.Tensor, Hq: int, k: int, alpha: float,
                  kv: torch.Tensor | None = None, host_kv: torch.Tensor | None = None, tau: int = TAU,
-                 n_split: int = 0, sm_scale: float | None = None, device="cuda"):
+                 n_split: int = 0, sm_scale: float | None = None, fetch: str = "pull", fetch_grid: int = 0,
+                 delta: bool | None = None, device="cuda"):
         if (kv is None) == (host_kv is None):
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
@@ -59,7 +67,19 @@ class LsaDecoder:
         self.Hq, self.k, self.alpha, self.tau = Hq, k, alpha, tau
         self.d_idx = k_idx.shape[2]
         self.lag = 1 if host_kv is not None else 0
+        if host_kv is not None and n_split == 0:
+            # with the fetch gathering on a few compute units, more and smaller
+            # attention workgroups balance around them (measured on 1M: 4x the
+            # library's split count beats 1x by about 20%)
+            from ._binding import lsa_gather_attend_default_splits
+            n_split = min(k, 4 * lsa_gather_attend_default_splits(self.B, self.Hkv, k))
         self.n_split = n_split
+        if fetch not in ("pull", "memcpy"):
+            raise ValueError("fetch must be 'pull' or 'memcpy'")
+        self.fetch, self.fetch_grid = fetch, fetch_grid
+        self.delta = (fetch == "pull") if delta is None else bool(delta)
+        if self.delta and fetch != "pull":
+            raise ValueError("the delta fetch needs fetch='pull' (slots are assigned on the device)")
         self.sm_scale = 1.0 / math.sqrt(self.d) if sm_scale is None else sm_scale
         dev = torch.device(device)
         B = self.B
@@ -70,12 +90,19 @@ class LsaDecoder:
         self.sel_ids = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
         self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
         if self.lag:
-            self.pool = [torch.empty((B, k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
-                         for _ in range(2)]
+            if self.delta:
+                one = torch.empty((B, 2 * k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
+                self.pool = [one, one]  # one pool, indexed through per-selection slots
+                self.sel_slots = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
+                self.fetch_slots = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
+            else:
+                self.pool = [torch.empty((B, k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
+                             for _ in range(2)]
             self.slots = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
             self.host_ids = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)]
             self.side = torch.cuda.Stream(device=dev)
             self.ev_ids = torch.cuda.Event()
+            self.ev_sel = torch.cuda.Event()
             self.fetch_done = [torch.cuda.Event() for _ in range(2)]
             self.attn_done = torch.cuda.Event()
             self._attn_done_valid = False
@@ -90,10 +117,13 @@ class LsaDecoder:
         return ids
 
     def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None) -> torch.Tensor:
-        """One decode step's attention with selection `sel`."""
+        """One decode step's attention with selection `sel` (on the host tier
+        with the delta fetch, the selection's pool slots must have been
+        assigned, as run_interval does)."""
         ids = self.sel_ids[sel % 2]
         if self.lag:
-            return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=self.slots,
+            slots = self.sel_slots[sel % 2] if self.delta else self.slots
+            return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
                                      workspace=self.workspace, n_split=self.n_split, out=out, stream=stream)
         return lsa_gather_attend(q, self.kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
                                  n_split=self.n_split, out=out, stream=stream)
@@ -110,8 +140,15 @@ class LsaDecoder:
             return
         main = torch.cuda.current_stream()
         self.reselect(q_idx, i)
-        self.host_ids[i % 2].copy_(self.sel_ids[i % 2], non_blocking=True)
-        self.ev_ids.record(main)
+        if self.delta:
+            prev = (self.sel_ids[(i - 1) % 2], self.sel_slots[(i - 1) % 2]) if i >= 1 else (None, None)
+            lsa_pool_assign(prev[0], prev[1], self.sel_ids[i % 2], 2 * self.k, new_slots=self.sel_slots[i % 2],
+                            fetch_slots=self.fetch_slots[i % 2])
+        if self.fetch == "memcpy":
+            self.host_ids[i % 2].copy_(self.sel_ids[i % 2], non_blocking=True)
+            self.ev_ids.record(main)
+        else:
+            self.ev_sel.record(main)
         if i == 0:
             self._fetch(0)
         src = max(i - 1, 0)
@@ -125,10 +162,23 @@ class LsaDecoder:
 
     def _fetch(self, i: int) -> None:
         """Copy selection i's chunks from host into pool buffer i % 2 on the side stream."""
-        self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
         if self._attn_done_valid:
             # pool buffer i % 2 was last read by the previous interval
             self.side.wait_event(self.attn_done)
-        lsa_fetch_chunks(self.host_kv, self.host_ids[i % 2], self.pool[i % 2], host_slots=None,
-                         stream=self.side, done=None)
+        if self.fetch == "memcpy":
+            self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
+            lsa_fetch_chunks(self.host_kv, self.host_ids[i % 2], self.pool[i % 2], host_slots=None,
+                             stream=self.side, done=None)
+        else:
+            self.side.wait_event(self.ev_sel)  # selection i (and its slots) are on the device
+            lsa_fetch_chunks_pull(self.host_kv, self.sel_ids[i % 2], self.pool[i % 2],
+                                  slots=self.fetch_slots[i % 2] if self.delta else None, grid=self.fetch_grid,
+                                  stream=self.side)
         self.fetch_done[i % 2].record(self.side)
+
+    def join(self) -> None:
+        """Make the current stream wait for every copy issued so far (needed
+        before the end of a graph capture, and before reading the pool)."""
+        if self.lag:
+            for ev in self.fetch_done:
+                torch.cuda.current_stream().wait_event(ev)

@@ -57,6 +57,8 @@ def lib():
         L.oracle_gather_attend.restype = ctypes.c_int
         L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
         L.oracle_fetch_chunks.restype = ctypes.c_int
+        L.oracle_pool_assign.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, vp]
+        L.oracle_pool_assign.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -129,7 +131,7 @@ def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len:
 
 
 def fetch_chunks(host_kv: np.ndarray, chunk_ids: np.ndarray, P: int, slots: np.ndarray | None = None,
-                 pool: np.ndarray | None = None) -> np.ndarray:
+                 pool: np.ndarray | None = None, skip_negative_slots: bool = False) -> np.ndarray:
     """host_kv uint16 [B][C][2][Hkv][T][d] -> pool uint16 [B][P][2][Hkv][T][d]."""
     host_kv = _c(host_kv, np.uint16)
     B, C, _, Hkv, T, d = host_kv.shape
@@ -140,12 +142,38 @@ def fetch_chunks(host_kv: np.ndarray, chunk_ids: np.ndarray, P: int, slots: np.n
     sl = 0
     if slots is not None:
         slots = _c(slots, np.int32)
+        if skip_negative_slots:  # a delta fetch: entries with slot -1 copy nothing
+            for b in range(B):
+                keep = slots[b] >= 0
+                if keep.any():
+                    fetch_chunks(host_kv[b:b + 1], chunk_ids[b:b + 1, keep], P, slots[b:b + 1, keep],
+                                 pool=pool[b:b + 1] if pool is not None else None)
+            return pool
         sl = slots.ctypes.data
     rc = lib().oracle_fetch_chunks(host_kv.ctypes.data, C, chunk_ids.ctypes.data, sl, pool.ctypes.data, P, B,
                                    Hkv, d, k, T)
     if rc != 0:
         raise ValueError("oracle fetch: chunk id or slot out of range")
     return pool
+
+
+def pool_assign(prev_ids, prev_slots, new_ids: np.ndarray, P: int):
+    """Delta-fetch slots: (new_slots, fetch_slots) int32 [B][k]; prev_* may be
+    None for the first selection."""
+    new_ids = _c(new_ids, np.int32)
+    B, k = new_ids.shape
+    if prev_ids is None:
+        n_prev, pi, ps = 0, 0, 0
+    else:
+        prev_ids, prev_slots = _c(prev_ids, np.int32), _c(prev_slots, np.int32)
+        n_prev, pi, ps = prev_ids.shape[1], prev_ids.ctypes.data, prev_slots.ctypes.data
+    new_slots = np.empty((B, k), dtype=np.int32)
+    fetch_slots = np.empty((B, k), dtype=np.int32)
+    rc = lib().oracle_pool_assign(pi, ps, n_prev, new_ids.ctypes.data, B, k, P, new_slots.ctypes.data,
+                                  fetch_slots.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle pool assignment failed (rc={rc})")
+    return new_slots, fetch_slots
 
 
 # ---- decode schedule ----------------------------------------------------

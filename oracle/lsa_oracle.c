@@ -32,6 +32,10 @@
  *     (paperlayer.ai summary, 2.1 Architecture: non-recalled entries are
  *     evicted to CPU; 3 Experiments / Experimental Setup: recalled chunks are
  *     retrieved from CPU cold storage every tau = 64 steps).
+ *  6. Pool slots of a delta fetch (the same passages: only the chunks not
+ *     already recalled need fetching): a chunk kept from the previous
+ *     selection keeps its slot; the r-th new chunk in ascending id order takes
+ *     the r-th lowest slot the previous selection does not hold.
  *
  * Layouts (row-major):
  *   q_idx  int8   [B][nq][d_idx]        K_idx int8 [B][C][d_idx]
@@ -205,4 +209,44 @@ int oracle_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* chunk
             memcpy(pool_kv + (b * P + p) * chunk, host_kv + (b * C + c) * chunk, sizeof(uint16_t) * (size_t)chunk);
         }
     return 0;
+}
+
+/* 6. Delta-fetch slots.  For each request: chunk new_ids[j] found among
+ *    prev_ids keeps that entry's slot (fetch_slots[j] = -1); otherwise it
+ *    takes the next slot, in ascending order, held by no entry of the
+ *    previous selection (fetch_slots[j] = that slot).  new_ids is walked in
+ *    the order given (ascending for selections).
+ *    Returns 0; -1 for a previous slot outside [0, P); -2 if the free slots
+ *    run out. */
+int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64_t n_prev, const int32_t* new_ids,
+                       int64_t B, int64_t k, int64_t P, int32_t* new_slots, int32_t* fetch_slots) {
+    unsigned char* held = (unsigned char*)malloc((size_t)P);
+    int rc = 0;
+    for (int64_t b = 0; b < B && rc == 0; ++b) {
+        memset(held, 0, (size_t)P);
+        for (int64_t j = 0; j < n_prev; ++j) {
+            const int64_t sl = prev_slots[b * n_prev + j];
+            if (sl < 0 || sl >= P) { rc = -1; break; }
+            held[sl] = 1;
+        }
+        int64_t next = 0;
+        for (int64_t j = 0; j < k && rc == 0; ++j) {
+            const int32_t c = new_ids[b * k + j];
+            int64_t found = -1;
+            for (int64_t q = 0; q < n_prev; ++q)
+                if (prev_ids[b * n_prev + q] == c) { found = q; break; }
+            if (found >= 0) {
+                new_slots[b * k + j] = prev_slots[b * n_prev + found];
+                fetch_slots[b * k + j] = -1;
+            } else {
+                while (next < P && held[next]) ++next;
+                if (next >= P) { rc = -2; break; }
+                new_slots[b * k + j] = (int32_t)next;
+                fetch_slots[b * k + j] = (int32_t)next;
+                ++next;
+            }
+        }
+    }
+    free(held);
+    return rc;
 }

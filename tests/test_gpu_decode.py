@@ -44,21 +44,29 @@ def oracle_output(oracle, W, w, t, b, ids_b):
     return oracle.gather_attend(q, chunks, ids_b[None].astype(np.int32), ctx, w.Hkv, w.sm_scale, slots=slots)[0]
 
 
-@pytest.mark.parametrize("name", ["tiny", "32k", "128k", "500k", "1m_host"])
-def test_decode_workload(oracle_lib, name):
+@pytest.mark.parametrize("name,fetch,delta", [("tiny", None, None), ("32k", None, None), ("128k", None, None),
+                                              ("500k", None, None), ("1m_host", "pull", True),
+                                              ("1m_host", "pull", False), ("1m_host", "memcpy", False),
+                                              ("128k_host", "pull", True)])
+def test_decode_workload(oracle_lib, name, fetch, delta):
     import torch
 
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
     from synth import workloads as W
 
-    w = W.WORKLOADS[name]
-    steps, reqs = SAMPLED[name]
+    if name == "128k_host":  # the drifting 128K workload on the host tier: selections change every interval
+        w = W.WORKLOADS["128k"].replace(host_tier=True)
+        steps, reqs = [0, 63, 64, 128, 191, 192, 255], [0, 9]
+    else:
+        w = W.WORKLOADS[name]
+        steps, reqs = SAMPLED[name]
     say(f"decode {name}: B={w.B} C={w.C} k={w.k} steps={w.steps} host_tier={w.host_tier}")
     dev = torch.device("cuda")
     K = to_dev(W.indexer_keys(w))
     ctx = to_dev(W.ctx_lens(w))
     if w.host_tier:
-        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, host_kv=W.pinned_kv_store(w))
+        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, host_kv=W.pinned_kv_store(w),
+                         fetch=fetch, delta=delta)
     else:
         dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=W.device_kv_store(w, dev))
     say("  inputs placed")
@@ -70,6 +78,7 @@ def test_decode_workload(oracle_lib, name):
         qs = [to_dev_bf16(W.attn_query(w, t)) for t in ts]
         dec.run_interval(i, to_dev(W.indexer_query(w, i)), qs, [keep.get(t, scratch) for t in ts])
         gpu_sel[i] = dec.sel_ids[i % 2].clone()
+    dec.join()
     torch.cuda.synchronize()
     say("  GPU run done")
 
@@ -87,8 +96,9 @@ def test_decode_workload(oracle_lib, name):
     say(f"  parity ok; worst max-abs error / output RMS = {worst:.3e}")
 
     if w.host_tier:
-        # the pool holds, byte for byte, the chunks of the last fetched selection
+        # the pool holds, byte for byte, the chunks of the last fetched selection at their slots
         last = w.intervals - 1
         pool = dec.pool[last % 2].cpu().view(torch.int16).numpy().view(np.uint16)
+        slots = dec.sel_slots[last % 2].cpu().numpy() if dec.delta else np.tile(np.arange(w.k), (w.B, 1))
         for b in reqs:
-            assert np.array_equal(pool[b], W.kv_chunks(w, b, sels[last][b])), f"pool of request {b}"
+            assert np.array_equal(pool[b][slots[b]], W.kv_chunks(w, b, sels[last][b])), f"pool of request {b}"

@@ -57,3 +57,51 @@ def test_graph_replays_match_eager(n_split):
     torch.cuda.synchronize()
     for t in range(steps):
         assert np.array_equal(outs[t].cpu().numpy(), eager[t])
+
+
+def test_host_tier_graph_replays_match_eager():
+    """Host tier with the device-side fetch: two intervals (fetch, lag 1,
+    both pool buffers) captured in one graph replay to the eager bits."""
+    import torch
+
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"].replace(host_tier=True)
+    dev = torch.device("cuda")
+    K = to_dev(W.indexer_keys(w))
+    ctx = to_dev(W.ctx_lens(w))
+    dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, host_kv=W.pinned_kv_store(w))
+    per = 4
+    qs = [[to_dev_bf16(W.attn_query(w, 64 * i + t)) for t in range(per)] for i in range(3)]
+    qidx = [to_dev(W.indexer_query(w, i)) for i in range(3)]
+    outs = [[torch.zeros((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for _ in range(per)] for _ in range(3)]
+
+    def run():
+        for i in range(3):
+            dec.run_interval(i, qidx[i], qs[i], outs[i])
+        dec.join()
+
+    run()
+    torch.cuda.synchronize()
+    eager = [[o.cpu().numpy().copy() for o in row] for row in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    dec._attn_done_valid = False
+    with torch.cuda.graph(g, stream=s):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for row in outs:
+            for o in row:
+                o.fill_(float("nan"))
+        for p in dec.pool:
+            p.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            for t in range(per):
+                assert np.array_equal(outs[i][t].cpu().numpy(), eager[i][t]), f"replay {rep}, interval {i}, step {t}"

@@ -256,6 +256,78 @@ def test_fetch_byte_exact(lsa, oracle_lib, synth_lib):
     assert np.array_equal(pool2.cpu().view(torch.int16).numpy().view(np.uint16), oracle_lib.fetch_chunks(host, ids, k))
 
 
+def test_fetch_pull_byte_exact(lsa, oracle_lib, synth_lib):
+    """The device-side gather: same pool bytes as the oracle's copy; entries
+    with an id or slot out of range are skipped and leave their slot as it was."""
+    import torch
+    B, C, Hkv, d, k, P = 3, 40, 2, 128, 7, 9
+    host = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), 19, synth_lib.stream(synth_lib.TAG_MISC, 960))
+    host_t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).pin_memory()
+    ids = np.array([[0, 1, 2, 5, 17, 38, 39], [3, 4, 6, 8, 9, 10, 11], [1, 9, 12, 20, 25, 30, 33]], dtype=np.int32)
+    slots = np.array([[8, 7, 6, 5, 4, 3, 2], [0, 1, 2, 3, 4, 5, 6], [2, 4, 6, 8, 1, 3, 5]], dtype=np.int32)
+    pool = torch.zeros((B, P, 2, Hkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    for grid in (1, 5, 0):
+        pool.zero_()
+        lsa.lsa_fetch_chunks_pull(host_t, to_dev(ids), pool, slots=to_dev(slots), grid=grid)
+        torch.cuda.synchronize()
+        ref = oracle_lib.fetch_chunks(host, ids, P, slots=slots)
+        assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), ref), grid
+    pool2 = torch.zeros((B, k, 2, Hkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_fetch_chunks_pull(host_t, to_dev(ids), pool2)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool2.cpu().view(torch.int16).numpy().view(np.uint16), oracle_lib.fetch_chunks(host, ids, k))
+    # out-of-range entries: skipped by the kernel's own bounds check
+    bad_ids = ids.copy()
+    bad_ids[0, 1] = C          # id past the store
+    bad_ids[1, 2] = -1         # negative id
+    bad_slots = slots.copy()
+    bad_slots[2, 3] = P        # slot past the pool
+    pool.fill_(1.0)
+    lsa.lsa_fetch_chunks_pull(host_t, to_dev(bad_ids), pool, slots=to_dev(bad_slots))
+    torch.cuda.synchronize()
+    got = pool.cpu().view(torch.int16).numpy().view(np.uint16)
+    one = np.uint16(0x3F80)  # bf16 1.0
+    for b in range(B):
+        for j in range(k):
+            c, p = bad_ids[b, j], bad_slots[b, j]
+            if 0 <= c < C and 0 <= p < P:
+                assert np.array_equal(got[b, p], host[b, c])
+            elif 0 <= p < P:
+                assert (got[b, p] == one).all()
+
+
+def test_fetch_pull_rejects_pageable(lsa):
+    import torch
+    host = torch.zeros((1, 4, 2, 1, 64, 64), dtype=torch.bfloat16)
+    pool = torch.zeros((1, 2, 2, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lsa.LsaError, match="pinned"):
+        lsa.lsa_fetch_chunks_pull(host, torch.tensor([[0, 1]], dtype=torch.int32, device="cuda"), pool)
+
+
+@pytest.mark.parametrize("B,C,k", [(1, 30, 5), (3, 2048, 276), (4, 16384, 1638), (2, 100, 1)])
+def test_pool_assign_parity(lsa, oracle_lib, synth_lib, B, C, k):
+    """Delta-fetch slots: bit-exact with the oracle over a chain of selections
+    (overlapping ones, disjoint ones, identical ones)."""
+    P = 2 * k
+    prev_ids = prev_slots = None
+    prev_d = (None, None)
+    for step in range(6):
+        span = C if step % 2 else max(k, C // 3)  # alternate wide and narrow draws: overlaps vary
+        ids = np.stack([np.sort(synth_lib.choose(k, span, 8, synth_lib.stream(synth_lib.TAG_MISC, 2000 + 16 * step + b)))
+                        for b in range(B)]).astype(np.int32)
+        if step == 3:
+            ids = prev_ids.copy()  # the same selection again: nothing to fetch
+        ns_ref, fs_ref = oracle_lib.pool_assign(prev_ids, prev_slots, ids, P)
+        ids_d = to_dev(ids)
+        ns, fs = lsa.lsa_pool_assign(prev_d[0], prev_d[1], ids_d, P)
+        assert np.array_equal(ns.cpu().numpy(), ns_ref), step
+        assert np.array_equal(fs.cpu().numpy(), fs_ref), step
+        if step == 3:
+            assert (fs_ref == -1).all()
+        prev_ids, prev_slots = ids, ns_ref
+        prev_d = (ids_d, ns)
+
+
 def test_fetch_rejects_pageable(lsa):
     import torch
     host = torch.zeros((1, 4, 2, 1, 64, 64), dtype=torch.bfloat16)  # not pinned

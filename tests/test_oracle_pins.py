@@ -358,3 +358,49 @@ def test_schedule(oracle_lib):
     assert [t for t in range(256) if oracle_lib.is_reselect_step(t, tau)] == [0, 64, 128, 192]
     assert [oracle_lib.selection_for_step(t, tau, 0) for t in (0, 63, 64, 255)] == [0, 0, 1, 3]
     assert [oracle_lib.selection_for_step(t, tau, 1) for t in (0, 63, 64, 127, 128, 255)] == [0, 0, 0, 0, 1, 2]
+
+
+# ---------------------------------------------------------------- delta-fetch slots
+
+def test_pool_assign_closed_form(oracle_lib):
+    g = _golden("closed_forms.json")["pool_assign"]
+    ns, fs = oracle_lib.pool_assign(np.array([g["prev_ids"]]), np.array([g["prev_slots"]]),
+                                    np.array([g["new_ids"]]), g["P"])
+    assert ns[0].tolist() == g["expected_new_slots"]
+    assert fs[0].tolist() == g["expected_fetch_slots"]
+
+
+def test_pool_assign_chain_keeps_pool_consistent(oracle_lib, synth_lib):
+    """Over a chain of random selections, with only the new chunks fetched:
+    kept chunks keep their slots, new chunks land in slots the previous
+    selection does not hold (distinct, lowest first), and the pool always
+    holds every selected chunk at its slot (checked against a full copy)."""
+    B, C, k = 3, 40, 9
+    P = 2 * k
+    host = synth_lib.normal_bf16((B, C, 2, 1, 64, 8), 4, synth_lib.stream(synth_lib.TAG_MISC, 1700))
+    pool = np.zeros((B, P, 2, 1, 64, 8), dtype=np.uint16)
+    prev_ids = prev_slots = None
+    for step in range(12):
+        ids = np.stack([np.sort(synth_lib.choose(k, C if step % 3 else 12, 4,
+                                                 synth_lib.stream(synth_lib.TAG_MISC, 1800 + 10 * step + b)))
+                        for b in range(B)]).astype(np.int32)
+        ns, fs = oracle_lib.pool_assign(prev_ids, prev_slots, ids, P)
+        for b in range(B):
+            assert len(set(ns[b].tolist())) == k and (ns[b] >= 0).all() and (ns[b] < P).all()
+            prev_map = {} if prev_ids is None else dict(zip(prev_ids[b].tolist(), prev_slots[b].tolist()))
+            held = set(prev_map.values())
+            new_slots = []
+            for j in range(k):
+                c = int(ids[b, j])
+                if c in prev_map:
+                    assert ns[b, j] == prev_map[c] and fs[b, j] == -1
+                else:
+                    assert fs[b, j] == ns[b, j] and ns[b, j] not in held
+                    new_slots.append(int(ns[b, j]))
+            free = [s for s in range(P) if s not in held]
+            assert new_slots == free[:len(new_slots)]  # lowest free slots, in id order
+        oracle_lib.fetch_chunks(host, ids, P, slots=fs, pool=pool, skip_negative_slots=True)
+        for b in range(B):
+            for j in range(k):
+                assert np.array_equal(pool[b, ns[b, j]], host[b, ids[b, j]]), (step, b, j)
+        prev_ids, prev_slots = ids, ns
