@@ -106,6 +106,31 @@ lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t 
                            hipStream_t stream);
 
 /*
+ * lsa_threshold_chunks -- the pages' own selection rule: sigmoid gating with
+ * a variable budget.
+ *
+ * Defined by: the memory indexer keeps every chunk whose sigmoid score
+ * passes a threshold (0.5 in the reported configuration) instead of a fixed
+ * top-k (paperlayer.ai summary, 2.1 Architecture and 2.4 Configuration).  The
+ * budget per request is then variable, here capped at k_max (the HBM pool
+ * size).  For each row r: the chunks with logit > logit_threshold; if more
+ * than k_max pass, the first k_max of the order (logit descending, chunk
+ * index ascending).  Written in ascending chunk order into
+ * chunk_ids[r][0..counts[r]), the rest of the row set to -1.
+ * With scores sigma(alpha * logit), alpha > 0: sigma > 0.5 exactly when
+ * alpha * logit > 0, i.e. logit > 0, so the 0.5 threshold is
+ * logit_threshold = 0.  Another score threshold s maps to the largest
+ * integer logit whose score does not exceed s.
+ *
+ *  logits      device int32 [R][C]
+ *  R >= 1, 1 <= C <= 65536, 1 <= k_max <= C
+ *  chunk_ids   device int32 [R][k_max] output
+ *  counts      device int32 [R] output, chunks kept per row (0..k_max)
+ */
+lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t logit_threshold, int32_t k_max,
+                                int32_t* chunk_ids, int32_t* counts, hipStream_t stream);
+
+/*
  * Number of bytes of workspace lsa_gather_attend needs for these sizes and
  * this split count (n_split = 0: the library's own choice).  Returns 0 when
  * no workspace is needed, (size_t)-1 when the arguments are invalid.
@@ -142,6 +167,9 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *  chunk_ids  device int32 [B][k]: context chunk index of each list entry
  *             (decides which tokens are < ctx_len)
  *  slots      device int32 [B][k] store position of each entry, or NULL
+ *  counts     device int32 [B]: entries in use per request (the first
+ *             counts[b] of the row; as lsa_threshold_chunks writes them), or
+ *             NULL: all k
  *  ctx_len    device int32 [B]: valid tokens per request; a request whose
  *             listed chunks hold no valid token gets out = 0
  *  B >= 1; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16; d = 64 or 128; 1 <= k
@@ -158,7 +186,8 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  * q, kv and out need 16-byte alignment.
  */
 lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                             const int32_t* slots, const int32_t* ctx_len, int32_t B, int32_t Hq, int32_t Hkv,
+                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int32_t B,
+                             int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
                              int32_t n_split, float* out, hipStream_t stream);
 

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "LSA_OK", 1: "LSA_ERR_INVALID_ARGUMENT", 2: "LSA_ERR_UNSUPPOR
 CHUNK_TOKENS = 64
 
 # Every symbol include/lsa.h declares.
-EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks",
+EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
            "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits", "lsa_gather_attend",
            "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_pool_assign")
 
@@ -56,7 +56,9 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend_workspace_size.restype = sz
     L.lsa_gather_attend_default_splits.argtypes = [i32, i32, i32]
     L.lsa_gather_attend_default_splits.restype = i32
-    L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, sz, i32, vp, vp]
+    L.lsa_threshold_chunks.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    L.lsa_threshold_chunks.restype = ctypes.c_int
+    L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, sz, i32, vp, vp]
     L.lsa_gather_attend.restype = ctypes.c_int
     L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
     L.lsa_fetch_chunks.restype = ctypes.c_int
@@ -124,6 +126,22 @@ def lsa_topk_chunks(logits: torch.Tensor, k: int, chunk_ids=None, stream=None) -
     return chunk_ids
 
 
+def lsa_threshold_chunks(logits: torch.Tensor, k_max: int, logit_threshold: int = 0, chunk_ids=None, counts=None,
+                         stream=None):
+    """logits int32 [..., C] -> (chunk_ids int32 [..., k_max] padded with -1,
+    counts int32 [...]): chunks with logit > logit_threshold, at most k_max."""
+    _need(logits, torch.int32, "logits")
+    C = logits.shape[-1]
+    R = logits.numel() // C
+    if chunk_ids is None:
+        chunk_ids = torch.empty((*logits.shape[:-1], k_max), dtype=torch.int32, device=logits.device)
+    if counts is None:
+        counts = torch.empty(logits.shape[:-1], dtype=torch.int32, device=logits.device)
+    _check(load_library().lsa_threshold_chunks(_ptr(logits), R, C, int(logit_threshold), k_max, _ptr(chunk_ids),
+                                               _ptr(counts), _stream(stream)))
+    return chunk_ids, counts
+
+
 def lsa_gather_attend_workspace_size(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0) -> int:
     n = load_library().lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
     if n == ctypes.c_size_t(-1).value:
@@ -145,9 +163,10 @@ def alloc_workspace(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0,
 
 def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor,
                       sm_scale: float | None = None, slots: torch.Tensor | None = None, workspace=None,
-                      n_split: int = 0, out=None, stream=None) -> torch.Tensor:
+                      n_split: int = 0, out=None, counts: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """q bf16 [B][Hq][d]; kv bf16 [B][C_store][2][Hkv][64][d]; chunk_ids int32 [B][k];
-    ctx_len int32 [B]; slots int32 [B][k] or None.  Returns fp32 [B][Hq][d]."""
+    ctx_len int32 [B]; slots int32 [B][k] or None; counts int32 [B] or None.
+    Returns fp32 [B][Hq][d]."""
     _need(q, torch.bfloat16, "q", 3)
     _need(kv, torch.bfloat16, "kv", 6)
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
@@ -163,6 +182,10 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
         _need(slots, torch.int32, "slots", 2)
         if tuple(slots.shape) != tuple(chunk_ids.shape):
             raise ValueError("slots must have the shape of chunk_ids")
+    if counts is not None:
+        _need(counts, torch.int32, "counts", 1)
+        if counts.shape[0] != B:
+            raise ValueError("counts must have one entry per request")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if workspace is None:
@@ -171,7 +194,8 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().lsa_gather_attend(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
-                                            _ptr(ctx_len), B, Hq, Hkv, d, k, sm_scale, _ptr(workspace), ws_bytes,
+                                            _ptr(counts), _ptr(ctx_len), B, Hq, Hkv, d, k, sm_scale,
+                                            _ptr(workspace), ws_bytes,
                                             n_split, _ptr(out), _stream(stream)))
     return out
 

@@ -200,8 +200,14 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     const int b = blk / a.Hkv;
     const int G = a.G;
 
-    const int64_t j0 = ((int64_t)s * a.k) / a.n_split;
-    const int64_t j1 = ((int64_t)(s + 1) * a.k) / a.n_split;
+    // entries of this request's list in use (variable with threshold selection)
+    int64_t kb = a.k;
+    if (a.counts) {
+        const int64_t cnt = a.counts[b];
+        kb = cnt < 0 ? 0 : cnt > a.k ? a.k : cnt;
+    }
+    const int64_t j0 = ((int64_t)s * kb) / a.n_split;
+    const int64_t j1 = ((int64_t)(s + 1) * kb) / a.n_split;
     const int ctx = a.ctx[b];
     const int32_t* ids = a.ids + (int64_t)b * a.k;
 

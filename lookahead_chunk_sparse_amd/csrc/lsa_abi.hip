@@ -82,8 +82,22 @@ lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t 
     if (C > lsa::kTopkMaxC) return fail(LSA_ERR_UNSUPPORTED, "C=%d exceeds %d", C, lsa::kTopkMaxC);
     if (!aligned(logits, 4) || !aligned(chunk_ids, 4))
         return fail(LSA_ERR_INVALID_ARGUMENT, "logits and chunk_ids need 4-byte alignment");
-    hipError_t e = lsa::launch_topk(logits, R, C, k, chunk_ids, stream);
+    hipError_t e = lsa::launch_topk(logits, R, C, k, chunk_ids, 0, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return ok();
+}
+
+lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t logit_threshold, int32_t k_max,
+                                int32_t* chunk_ids, int32_t* counts, hipStream_t stream) {
+    if (!logits || !chunk_ids || !counts)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "logits, chunk_ids and counts are required");
+    if (R < 1 || C < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "R=%d C=%d must be >= 1", R, C);
+    if (k_max < 1 || k_max > C) return fail(LSA_ERR_INVALID_ARGUMENT, "k_max=%d must be in [1, C=%d]", k_max, C);
+    if (C > lsa::kTopkMaxC) return fail(LSA_ERR_UNSUPPORTED, "C=%d exceeds %d", C, lsa::kTopkMaxC);
+    if (!aligned(logits, 4) || !aligned(chunk_ids, 4) || !aligned(counts, 4))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "logits, chunk_ids and counts need 4-byte alignment");
+    hipError_t e = lsa::launch_topk(logits, R, C, k_max, chunk_ids, logit_threshold, counts, stream);
+    if (e != hipSuccess) return hip_fail(e, "threshold-select launch");
     return ok();
 }
 
@@ -111,7 +125,8 @@ size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
 }
 
 lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                             const int32_t* slots, const int32_t* ctx_len, int32_t B, int32_t Hq, int32_t Hkv,
+                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int32_t B,
+                             int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
                              int32_t n_split, float* out, hipStream_t stream) {
     if (!q || !kv || !chunk_ids || !ctx_len || !out)
@@ -138,6 +153,7 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     a.C_store = C_store;
     a.ids = chunk_ids;
     a.slots = slots;
+    a.counts = counts;
     a.ctx = ctx_len;
     a.B = B;
     a.Hq = Hq;

@@ -15,7 +15,9 @@ hipError_t launch_index_score(const int8_t* q_idx, const int8_t* k_idx, int B, i
 // ---- top-k chunk selection ----
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkMaxC = 65536;
-hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, hipStream_t stream);
+// counts == nullptr: top-k; else keep logits > thr, at most k, counts[r] = kept
+hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
+                       hipStream_t stream);
 
 // ---- gathered GQA decode attention ----
 struct AttendArgs {
@@ -24,6 +26,7 @@ struct AttendArgs {
     int64_t C_store;
     const int32_t* ids;     // [B][k]
     const int32_t* slots;   // [B][k] or nullptr
+    const int32_t* counts;  // [B] entries used per request, or nullptr (all k)
     const int32_t* ctx;     // [B]
     int B, Hq, Hkv, G, d, k, n_split;
     int depth;              // chunks in flight per wave + 1 (register ring size)

@@ -76,9 +76,13 @@ __device__ inline uint32_t wave_and(uint32_t v) {
     return v;
 }
 
+// Threshold mode (counts != nullptr): the row keeps the chunks whose logit
+// exceeds `thr`, at most k of them (the first k in the same order when more
+// pass); the output row is padded with -1 and counts[row] = chunks kept.
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restrict__ logits, int C, int k,
-                                                        int32_t* __restrict__ out) {
+                                                        int32_t* __restrict__ out, int32_t thr,
+                                                        int32_t* __restrict__ counts) {
     __shared__ int sm_i[kWaves];
     __shared__ uint32_t sm_or[kWaves], sm_and[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -112,9 +116,23 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
         land &= sm_and[w];
     }
 
+    // --- how many to keep ---
+    int kk = k;
+    if (counts) {
+        const uint32_t tkey = (uint32_t)thr ^ 0x80000000u;
+        int above = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) above += (base + e < C) && (key[e] > tkey);
+        above = block_sum(above, sm_i, lane, wave);
+        kk = above < k ? above : k;
+        if (tid == 0) counts[blockIdx.x] = kk;
+        for (int j = kk + tid; j < k; j += kThreads) dst[j] = -1;
+        if (kk == 0) return;  // uniform: every thread saw the same sum
+    }
+
     // --- radix select over the bits where keys differ ---
     uint32_t prefix = land;  // correct on every common bit
-    int need = k;
+    int need = kk;
     const uint32_t diff = lor ^ land;
     if (diff != 0u) {
         const int top = 31 - __builtin_clz(diff);
@@ -154,14 +172,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
     for (int e = 0; e < KPT; ++e) {
         const int idx = base + e;
         if (idx >= C) continue;
-        // pos < k holds by construction (|{> v*}| + need == k); the test keeps
-        // every store inside the row even so.
+        // pos < kk holds by construction (|{> v*}| + need == kk); the test
+        // keeps every store inside the row even so.
         if (key[e] > vstar) {
-            if (pos < k) dst[pos] = idx;
+            if (pos < kk) dst[pos] = idx;
             ++pos;
         } else if (key[e] == vstar) {
             if (eq_seen < need) {
-                if (pos < k) dst[pos] = idx;
+                if (pos < kk) dst[pos] = idx;
                 ++pos;
             }
             ++eq_seen;
@@ -170,22 +188,24 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
 }
 
 template <int KPT>
-hipError_t launch(const int32_t* logits, int R, int C, int k, int32_t* ids, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_kernel<KPT>, dim3((unsigned)R), dim3(kThreads), 0, stream, logits, C, k, ids);
+hipError_t launch(const int32_t* logits, int R, int C, int k, int32_t* ids, int32_t thr, int32_t* counts,
+                  hipStream_t stream) {
+    hipLaunchKernelGGL(topk_kernel<KPT>, dim3((unsigned)R), dim3(kThreads), 0, stream, logits, C, k, ids, thr, counts);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, hipStream_t stream) {
+hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
+                       hipStream_t stream) {
     const int kpt = (C + kThreads - 1) / kThreads;
-    if (kpt <= 1) return launch<1>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 2) return launch<2>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 4) return launch<4>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 8) return launch<8>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 16) return launch<16>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 32) return launch<32>(logits, R, C, k, chunk_ids, stream);
-    if (kpt <= 64) return launch<64>(logits, R, C, k, chunk_ids, stream);
+    if (kpt <= 1) return launch<1>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 2) return launch<2>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 4) return launch<4>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 8) return launch<8>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 16) return launch<16>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 32) return launch<32>(logits, R, C, k, chunk_ids, thr, counts, stream);
+    if (kpt <= 64) return launch<64>(logits, R, C, k, chunk_ids, thr, counts, stream);
     return hipErrorInvalidValue;
 }
 

@@ -23,6 +23,11 @@ Two placements of the K/V:
     two buffers: chunks selected again keep their slot and only new chunks
     are copied, into slots the selection being attended over does not hold.
 
+Two selection rules: a fixed budget of k chunks (selection="topk"), or the
+pages' sigmoid gating (selection="threshold": chunks whose score passes 0.5,
+i.e. logit > 0, at most k of them; 2.1 Architecture and 2.4 Configuration of
+the summary), whose budget varies per request.
+
 This module only orders calls into liblsa.so on HIP streams and records
 events; it computes nothing itself.
 """
@@ -33,7 +38,7 @@ import math
 import torch
 
 from ._binding import (alloc_workspace, lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend, lsa_index_score,
-                       lsa_pool_assign, lsa_topk_chunks)
+                       lsa_pool_assign, lsa_threshold_chunks, lsa_topk_chunks)
 
 TAU = 64
 
@@ -55,7 +60,8 @@ class LsaDecoder:
     def __init__(self, *, k_idx: torch.Tensor, ctx_len: torch.Tensor, Hq: int, k: int, alpha: float,
                  kv: torch.Tensor | None = None, host_kv: torch.Tensor | None = None, tau: int = TAU,
                  n_split: int = 0, sm_scale: float | None = None, fetch: str = "pull", fetch_grid: int = 0,
-                 delta: bool | None = None, device="cuda"):
+                 delta: bool | None = None, selection: str = "topk", logit_threshold: int = 0,
+                 device="cuda"):
         if (kv is None) == (host_kv is None):
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
@@ -77,6 +83,11 @@ class LsaDecoder:
         if fetch not in ("pull", "memcpy"):
             raise ValueError("fetch must be 'pull' or 'memcpy'")
         self.fetch, self.fetch_grid = fetch, fetch_grid
+        if selection not in ("topk", "threshold"):
+            raise ValueError("selection must be 'topk' or 'threshold'")
+        if selection == "threshold" and host_kv is not None:
+            raise NotImplementedError("threshold selection is implemented for the HBM-resident store")
+        self.selection, self.logit_threshold = selection, int(logit_threshold)
         self.delta = (fetch == "pull") if delta is None else bool(delta)
         if self.delta and fetch != "pull":
             raise ValueError("the delta fetch needs fetch='pull' (slots are assigned on the device)")
@@ -88,6 +99,8 @@ class LsaDecoder:
         # selection buffers alternate by selection parity so a new selection
         # never overwrites the one the current interval attends with
         self.sel_ids = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
+        self.sel_counts = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)] \
+            if selection == "threshold" else [None, None]
         self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
         if self.lag:
             if self.delta:
@@ -113,7 +126,11 @@ class LsaDecoder:
         into selection buffer sel % 2."""
         lsa_index_score(q_idx, self.k_idx, self.alpha, logits=self.logits, scores=self.scores, stream=stream)
         ids = self.sel_ids[sel % 2]
-        lsa_topk_chunks(self.logits.view(self.B, self.C), self.k, chunk_ids=ids, stream=stream)
+        if self.selection == "threshold":
+            lsa_threshold_chunks(self.logits.view(self.B, self.C), self.k, self.logit_threshold, chunk_ids=ids,
+                                 counts=self.sel_counts[sel % 2], stream=stream)
+        else:
+            lsa_topk_chunks(self.logits.view(self.B, self.C), self.k, chunk_ids=ids, stream=stream)
         return ids
 
     def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None) -> torch.Tensor:
@@ -126,7 +143,7 @@ class LsaDecoder:
             return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
                                      workspace=self.workspace, n_split=self.n_split, out=out, stream=stream)
         return lsa_gather_attend(q, self.kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
-                                 n_split=self.n_split, out=out, stream=stream)
+                                 n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2], stream=stream)
 
     # ---- one interval ------------------------------------------------------
     def run_interval(self, i: int, q_idx: torch.Tensor, qs, outs) -> None:

@@ -53,12 +53,14 @@ def lib():
         L.oracle_topk_i64.restype = ctypes.c_int
         L.oracle_topk_f64.argtypes = [vp, i64, i64, i64, vp]
         L.oracle_topk_f64.restype = ctypes.c_int
-        L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, vp, vp]
+        L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, vp, vp]
         L.oracle_gather_attend.restype = ctypes.c_int
         L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
         L.oracle_fetch_chunks.restype = ctypes.c_int
         L.oracle_pool_assign.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, vp]
         L.oracle_pool_assign.restype = ctypes.c_int
+        L.oracle_threshold_i64.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+        L.oracle_threshold_i64.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -104,9 +106,10 @@ def topk_chunks(keys: np.ndarray, k: int) -> np.ndarray:
 
 def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len: np.ndarray, Hkv: int,
                   sm_scale: float, slots: np.ndarray | None = None, T: int = 64,
-                  want_weights: bool = False):
+                  want_weights: bool = False, counts: np.ndarray | None = None):
     """q uint16 (bf16 bits) [B][Hq][d]; kv uint16 [B][C_store][2][Hkv][T][d];
-    chunk_ids int32 [B][k]; ctx_len int [B]; slots int32 [B][k] or None.
+    chunk_ids int32 [B][k]; ctx_len int [B]; slots int32 [B][k] or None;
+    counts int32 [B] (entries used per request) or None.
     Returns out float64 [B][Hq][d] (and weights [B][Hq][k*T] if asked)."""
     q, kv = _c(q, np.uint16), _c(kv, np.uint16)
     chunk_ids = _c(chunk_ids, np.int32)
@@ -120,14 +123,33 @@ def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len:
         slots = _c(slots, np.int32)
         assert slots.shape == chunk_ids.shape
         sl = slots.ctypes.data
+    cn = 0
+    if counts is not None:
+        counts = _c(counts, np.int32)
+        cn = counts.ctypes.data
     out = np.empty((B, Hq, d), dtype=np.float64)
     wts = np.empty((B, Hq, k * T), dtype=np.float64) if want_weights else None
-    rc = lib().oracle_gather_attend(q.ctypes.data, kv.ctypes.data, C_store, chunk_ids.ctypes.data, sl,
+    rc = lib().oracle_gather_attend(q.ctypes.data, kv.ctypes.data, C_store, chunk_ids.ctypes.data, sl, cn,
                                     ctx.ctypes.data, B, Hq, Hkv, d, k, T, float(sm_scale), out.ctypes.data,
                                     wts.ctypes.data if wts is not None else 0)
     if rc != 0:
         raise ValueError(f"oracle attention rejected its arguments (rc={rc})")
     return (out, wts) if want_weights else out
+
+
+def threshold_chunks(logits: np.ndarray, k_max: int, logit_threshold: int = 0):
+    """Chunks with logit > logit_threshold, at most k_max (the first k_max of
+    the order (logit descending, index ascending)): (ids int32 [R][k_max]
+    padded with -1, counts int32 [R])."""
+    logits = _c(logits, np.int64)
+    R, C = logits.shape
+    ids = np.empty((R, k_max), dtype=np.int32)
+    counts = np.empty(R, dtype=np.int32)
+    rc = lib().oracle_threshold_i64(logits.ctypes.data, R, C, int(logit_threshold), k_max, ids.ctypes.data,
+                                    counts.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle threshold selection rejected its arguments (rc={rc})")
+    return ids, counts
 
 
 def fetch_chunks(host_kv: np.ndarray, chunk_ids: np.ndarray, P: int, slots: np.ndarray | None = None,

@@ -32,6 +32,9 @@
  *     (paperlayer.ai summary, 2.1 Architecture: non-recalled entries are
  *     evicted to CPU; 3 Experiments / Experimental Setup: recalled chunks are
  *     retrieved from CPU cold storage every tau = 64 steps).
+ *  7. Threshold selection (summary 2.1 Architecture, 2.4 Configuration:
+ *     sigmoid gating at 0.5 instead of a fixed top-k): the chunks whose logit
+ *     exceeds a threshold, capped at k_max by the same order as item 3.
  *  6. Pool slots of a delta fetch (the same passages: only the chunks not
  *     already recalled need fetching): a chunk kept from the previous
  *     selection keeps its slot; the r-th new chunk in ascending id order takes
@@ -126,12 +129,13 @@ int oracle_topk_f64(const double* keys, int64_t R, int64_t C, int64_t k, int32_t
  *      z  = (q[b][h] . K[token]) * sm_scale
  *      w  = exp(z - max z)
  *      out[b][h] = sum_token w * V[token] / sum_token w
+ *    counts (may be NULL) limits request b to its first counts[b] entries.
  *    If `weights` is not NULL it receives the normalised softmax weight of
  *    every (list entry, token) pair, [B][Hq][k*T], 0 for unused tokens.
  *    Returns 0, -1 on bad arguments, -3 if a request has no usable token. */
 int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                         const int32_t* slots, const int32_t* ctx_len, int64_t B, int64_t Hq, int64_t Hkv,
-                         int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights) {
+                         const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || k < 1 || T < 1) return -1;
     const int64_t group = Hq / Hkv;
     const int64_t tile = T * d;              /* one (K|V, head) tile        */
@@ -146,13 +150,14 @@ int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store,
             unsigned char* use = (unsigned char*)malloc((size_t)(k * T));
             double m = -INFINITY;
             int64_t n_used = 0;
+            const int64_t kb = counts ? counts[b] : k;
             for (int64_t j = 0; j < k; ++j) {
                 const int64_t c = chunk_ids[b * k + j];
                 const int64_t p = slots ? slots[b * k + j] : c;
                 const uint16_t* K = kv + (b * C_store + p) * chunk + (0 * Hkv + g) * tile;
                 for (int64_t t = 0; t < T; ++t) {
                     const int64_t e = j * T + t;
-                    use[e] = (c * T + t) < (int64_t)ctx_len[b];
+                    use[e] = j < kb && (c * T + t) < (int64_t)ctx_len[b];
                     z[e] = 0.0;
                     if (!use[e]) continue;
                     double dot = 0.0;
@@ -249,4 +254,30 @@ int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64
     }
     free(held);
     return rc;
+}
+
+/* 7. Threshold selection: in row r, count the keys above thr; keep
+ *    kk = min(count, k_max) chunks, those that fewer than kk chunks precede
+ *    in the order of item 3 (they are exactly the keys above thr when
+ *    count <= k_max).  Ascending ids, then -1 up to k_max; counts[r] = kk. */
+int oracle_threshold_i64(const int64_t* keys, int64_t R, int64_t C, int64_t thr, int64_t k_max, int32_t* ids,
+                         int32_t* counts) {
+    if (k_max < 1 || k_max > C) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t* row = keys + r * C;
+        int64_t above = 0;
+        for (int64_t c = 0; c < C; ++c) above += row[c] > thr;
+        const int64_t kk = above < k_max ? above : k_max;
+        int64_t n_out = 0;
+        for (int64_t c = 0; c < C; ++c) {
+            int64_t before = 0;
+            for (int64_t c2 = 0; c2 < C; ++c2)
+                if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;
+            if (before < kk) ids[r * k_max + n_out++] = (int32_t)c;
+        }
+        if (n_out != kk) return -2;
+        for (int64_t j = n_out; j < k_max; ++j) ids[r * k_max + j] = -1;
+        counts[r] = (int32_t)kk;
+    }
+    return 0;
 }

@@ -77,15 +77,24 @@ def test_topk_validation(lib):
     assert f(BOGUS, 1, 65537, 1, BOGUS, 0) == 2
 
 
+def test_threshold_validation(lib):
+    f = lib.lsa_threshold_chunks
+    assert f(0, 1, 8, 0, 2, BOGUS, BOGUS, 0) == 1
+    assert f(BOGUS, 1, 8, 0, 2, BOGUS, 0, 0) == 1 and "counts" in _err(lib)
+    assert f(BOGUS, 1, 8, 0, 0, BOGUS, BOGUS, 0) == 1 and "k_max=0" in _err(lib)
+    assert f(BOGUS, 1, 8, 0, 9, BOGUS, BOGUS, 0) == 1
+    assert f(BOGUS, 1, 65537, 0, 1, BOGUS, BOGUS, 0) == 2
+
+
 def test_attend_validation(lsa, lib):
     f = lib.lsa_gather_attend
-    # q, kv, C_store, ids, slots, ctx, B, Hq, Hkv, d, k, scale, ws, ws_bytes, n_split, out, stream
+    # q, kv, C_store, ids, slots, counts, ctx, B, Hq, Hkv, d, k, scale, ws, ws_bytes, n_split, out, stream
     ok = dict(q=BOGUS, kv=BOGUS, C=16, ids=BOGUS, slots=0, ctx=BOGUS, B=2, Hq=64, Hkv=8, d=128, k=4,
               scale=0.088, ws=0, wsb=0, ns=1, out=BOGUS)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["q"], a["kv"], a["C"], a["ids"], a["slots"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["d"],
+        return f(a["q"], a["kv"], a["C"], a["ids"], a["slots"], 0, a["ctx"], a["B"], a["Hq"], a["Hkv"], a["d"],
                  a["k"], a["scale"], a["ws"], a["wsb"], a["ns"], a["out"], 0)
 
     assert call(q=0) == 1

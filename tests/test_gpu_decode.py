@@ -102,3 +102,56 @@ def test_decode_workload(oracle_lib, name, fetch, delta):
         slots = dec.sel_slots[last % 2].cpu().numpy() if dec.delta else np.tile(np.arange(w.k), (w.B, 1))
         for b in reqs:
             assert np.array_equal(pool[b][slots[b]], W.kv_chunks(w, b, sels[last][b])), f"pool of request {b}"
+
+
+def test_decode_threshold_selection(oracle_lib):
+    """The pages' gating rule end to end: sigma > 0.5 (logit > 0) with the pool
+    size as cap.  A calibrated indexer is synthesised: background keys lean
+    against the query (negative logits), each request plants its own number
+    of relevant chunks, so the budget differs per request and per interval."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"].replace(B=4, k=64)
+    dev = torch.device("cuda")
+    s = synth.stream
+    sets = {}
+    q0 = W.indexer_query(w, 0)
+    q_idx = [q0, q0]  # same query; the second interval adds a second relevant set
+    noise = synth.uniform_i8((w.B, w.C, w.d_idx), 3, s(synth.TAG_MISC, 3001), -4, 4).astype(np.int32)
+    K = (-np.sign(q_idx[0].astype(np.int32)) + noise).astype(np.int8)  # background: logit about -sum|q|
+    for it, q in enumerate(q_idx):
+        for b in range(w.B):
+            n_rel = [5, 20, 90, 0][(b + it) % 4]  # 90 > k: the cap applies (sets may overlap)
+            pos = synth.choose(n_rel, w.C, 3, s(synth.TAG_MISC, 3100 + 10 * it + b))
+            sets[(it, b)] = pos
+            K[b, pos] = (8 * np.sign(q[b, 0].astype(np.int32)) + noise[b, pos]).astype(np.int8)
+    kv = W.device_kv_store(w, dev)
+    ctx = to_dev(W.ctx_lens(w))
+    dec = LsaDecoder(k_idx=to_dev(K), ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, selection="threshold")
+    outs = {}
+    for it in range(2):
+        qs = [to_dev_bf16(W.attn_query(w, 64 * it + t)) for t in range(3)]
+        o = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for _ in range(3)]
+        dec.run_interval(it, to_dev(q_idx[it]), qs, o)
+        torch.cuda.synchronize()
+        L = oracle_lib.index_logits(q_idx[it], K)
+        ref_ids, ref_counts = oracle_lib.threshold_chunks(L, w.k, 0)
+        got_counts = dec.sel_counts[it % 2].cpu().numpy()
+        assert np.array_equal(got_counts, ref_counts), (it, got_counts, ref_counts)
+        assert np.array_equal(dec.sel_ids[it % 2].cpu().numpy(), ref_ids)
+        assert len(set(ref_counts.tolist())) >= 3  # the budget really varies
+        for b in range(w.B):
+            if ref_counts[b] == 0:
+                assert (o[0][b].cpu().numpy() == 0).all()
+                continue
+            idsb = ref_ids[b, :ref_counts[b]]
+            for t in range(3):
+                chunks = W.kv_chunks(w, b, idsb)[None]
+                ref = oracle_lib.gather_attend(W.attn_query(w, 64 * it + t)[b:b + 1], chunks, idsb[None],
+                                               W.ctx_lens(w)[b:b + 1], w.Hkv, w.sm_scale,
+                                               slots=np.arange(len(idsb), dtype=np.int32)[None])
+                check_attention(o[t][b].cpu().numpy(), ref[0], f"threshold interval {it} request {b} step {t}")

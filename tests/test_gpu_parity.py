@@ -144,6 +144,26 @@ def test_topk_large_rows(lsa, oracle_lib, synth_lib, C):
         assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (C, k)
 
 
+@pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes", "none", "all"])
+@pytest.mark.parametrize("C", [1, 64, 1000, 2048, 16384])
+def test_threshold_parity(lsa, oracle_lib, synth_lib, kind, C):
+    """Sigmoid gating with a cap: ids, padding and counts bit-exact."""
+    R = 3 if C <= 2048 else 1
+    if kind == "none":
+        rows = -np.abs(_rows(synth_lib, "narrow", R, C, seed=C + 1)) - 1
+    elif kind == "all":
+        rows = np.abs(_rows(synth_lib, "narrow", R, C, seed=C + 2)) + 1
+    else:
+        rows = _rows(synth_lib, kind if kind != "random" else "narrow", R, C, seed=C + 3)
+    dl = to_dev(rows.astype(np.int32))
+    for k_max in sorted({1, C, max(1, C // 7)}):
+        for thr in (0, 5, -(2 ** 31)):
+            ids, counts = lsa.lsa_threshold_chunks(dl, k_max, thr)
+            ref_ids, ref_counts = oracle_lib.threshold_chunks(rows.astype(np.int64), k_max, thr)
+            assert np.array_equal(counts.cpu().numpy(), ref_counts), (kind, C, k_max, thr)
+            assert np.array_equal(ids.cpu().numpy(), ref_ids), (kind, C, k_max, thr)
+
+
 # ------------------------------------------------------------------ attention
 
 def _problem(synth_lib, B, Hq, Hkv, d, C, seed, qscale=1.0):
@@ -192,6 +212,26 @@ def test_attend_parity(lsa, oracle_lib, synth_lib, B, Hq, Hkv, d, C, k, ctx, n_s
     # requests without any valid token give 0 on the GPU; the oracle rejects them
     stats = check_attention(out.cpu().numpy(), ref, "attend")
     say("  ", stats)
+
+
+@pytest.mark.parametrize("n_split", [0, 1, 3])
+def test_attend_counts_parity(lsa, oracle_lib, synth_lib, n_split):
+    """Variable list lengths per request (threshold selection), including an
+    empty list (output 0)."""
+    B, Hq, Hkv, d, C, k = 4, 64, 8, 128, 30, 12
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=55, qscale=2.0)
+    ids = _ids(synth_lib, B, C, k, seed=56)
+    counts = np.array([12, 5, 0, 1], dtype=np.int32)
+    for b in range(B):
+        ids[b, counts[b]:] = -1  # unused entries, as the threshold selection writes them
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    out = lsa.lsa_gather_attend(to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx), 1 / math.sqrt(d),
+                                n_split=n_split, counts=to_dev(counts)).cpu().numpy()
+    assert (out[2] == 0).all()
+    live = [0, 1, 3]
+    ref = oracle_lib.gather_attend(q[live], kv[live], np.where(ids[live] < 0, 0, ids[live]), ctx[live], Hkv,
+                                   1 / math.sqrt(d), counts=counts[live])
+    check_attention(out[live], ref, "counts")
 
 
 def test_attend_no_valid_token_gives_zero(lsa, synth_lib):

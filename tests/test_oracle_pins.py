@@ -404,3 +404,56 @@ def test_pool_assign_chain_keeps_pool_consistent(oracle_lib, synth_lib):
             for j in range(k):
                 assert np.array_equal(pool[b, ns[b, j]], host[b, ids[b, j]]), (step, b, j)
         prev_ids, prev_slots = ids, ns
+
+
+# ---------------------------------------------------------------- threshold selection
+
+def brute_threshold(row, thr, k_max):
+    passing = [c for c in range(len(row)) if row[c] > thr]
+    order = sorted(passing, key=lambda c: (-row[c], c))[:k_max]
+    return sorted(order)
+
+
+@pytest.mark.parametrize("kind", ["random", "few_values", "none_pass", "all_pass"])
+def test_threshold_vs_brute_force(oracle_lib, synth_lib, kind):
+    for C in (1, 5, 33, 64, 200):
+        if kind == "random":
+            row = synth_lib.uniform_i32((C,), 6, synth_lib.stream(synth_lib.TAG_MISC, 2100 + C), -50, 50)
+        elif kind == "few_values":
+            row = synth_lib.uniform_i32((C,), 7, synth_lib.stream(synth_lib.TAG_MISC, 2200 + C), -1, 1)
+        elif kind == "none_pass":
+            row = -np.abs(synth_lib.uniform_i32((C,), 8, synth_lib.stream(synth_lib.TAG_MISC, 2300 + C), 0, 9))
+        else:
+            row = 1 + np.abs(synth_lib.uniform_i32((C,), 9, synth_lib.stream(synth_lib.TAG_MISC, 2400 + C), 0, 9))
+        for k_max in sorted({1, C, max(1, C // 3)}):
+            for thr in (-1, 0, 3):
+                ids, counts = oracle_lib.threshold_chunks(row.reshape(1, -1).astype(np.int64), k_max, thr)
+                want = brute_threshold(row.tolist(), thr, k_max)
+                assert counts[0] == len(want)
+                assert ids[0, :len(want)].tolist() == want and (ids[0, len(want):] == -1).all()
+
+
+def test_threshold_zero_is_sigmoid_half(oracle_lib, synth_lib):
+    """sigma(alpha * logit) > 0.5 keeps the same chunks as logit > 0 (scipy's
+    logistic on the fp32 argument decides the first)."""
+    from scipy.special import expit
+    row = synth_lib.uniform_i32((300,), 10, synth_lib.stream(synth_lib.TAG_MISC, 2500), -3000, 3000)
+    row[:5] = [0, 1, -1, 2, -2]
+    alpha = 2.0 ** -11
+    x = (np.float32(alpha) * row.astype(np.float32)).astype(np.float64)
+    passing = np.nonzero(expit(x) > 0.5)[0]
+    ids, counts = oracle_lib.threshold_chunks(row.reshape(1, -1).astype(np.int64), 300, 0)
+    assert np.array_equal(ids[0, :counts[0]], passing)
+
+
+def test_attention_counts_truncate_lists(oracle_lib, synth_lib):
+    """counts[b] limits request b to its first counts[b] entries."""
+    B, Hq, Hkv, d, C = 3, 8, 2, 64, 6
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=15, qscale=2.0)
+    ids = np.array([[0, 2, 4, 5], [1, 3, 5, -1], [4, -1, -1, -1]], dtype=np.int32)
+    counts = np.array([4, 3, 1], dtype=np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, np.where(ids < 0, 0, ids), ctx, Hkv, 0.125, counts=counts)
+    for b in range(B):
+        ref = oracle_lib.gather_attend(q[b:b + 1], kv[b:b + 1], ids[b:b + 1, :counts[b]], ctx[b:b + 1], Hkv, 0.125)
+        np.testing.assert_allclose(out[b], ref[0], rtol=0, atol=0)
