@@ -171,7 +171,18 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *             counts[b] of the row; as lsa_threshold_chunks writes them), or
  *             NULL: all k
  *  ctx_len    device int32 [B]: valid tokens per request; a request whose
- *             listed chunks hold no valid token gets out = 0
+ *             listed chunks (and segment) hold no valid token gets out = 0
+ *  seg_kv     device bf16 [B][2][Hkv][S_max][d], or NULL: a resident segment
+ *             attended in the same softmax as the chunks -- the local
+ *             sliding window and the freshly decoded tokens the pages always
+ *             keep in GPU memory (paperlayer.ai summary, 2.1 Architecture:
+ *             recalled entries are combined with the non-offloadable
+ *             sliding-window KV; 3 Experiments / Experimental Setup: the
+ *             local 8K / decoded window is retained).  Its tokens are not
+ *             chunk tokens: ctx_len bounds only the chunks, so a caller
+ *             passes the length of the offloadable history there.
+ *  seg_len    device int32 [B]: tokens of the segment in use (<= S_max)
+ *  S_max      segment capacity, a multiple of 64 (ignored without seg_kv)
  *  B >= 1; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16; d = 64 or 128; 1 <= k
  *  sm_scale   softmax scale, normally 1/sqrt(d)
  *  workspace  device buffer of at least
@@ -186,7 +197,8 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  * q, kv and out need 16-byte alignment.
  */
 lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int32_t B,
+                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                             const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
                              int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
                              int32_t n_split, float* out, hipStream_t stream);

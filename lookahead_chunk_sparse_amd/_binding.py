@@ -58,7 +58,8 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend_default_splits.restype = i32
     L.lsa_threshold_chunks.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     L.lsa_threshold_chunks.restype = ctypes.c_int
-    L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, sz, i32, vp, vp]
+    L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz,
+                                    i32, vp, vp]
     L.lsa_gather_attend.restype = ctypes.c_int
     L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
     L.lsa_fetch_chunks.restype = ctypes.c_int
@@ -163,10 +164,13 @@ def alloc_workspace(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0,
 
 def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor,
                       sm_scale: float | None = None, slots: torch.Tensor | None = None, workspace=None,
-                      n_split: int = 0, out=None, counts: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                      n_split: int = 0, out=None, counts: torch.Tensor | None = None,
+                      seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
     """q bf16 [B][Hq][d]; kv bf16 [B][C_store][2][Hkv][64][d]; chunk_ids int32 [B][k];
-    ctx_len int32 [B]; slots int32 [B][k] or None; counts int32 [B] or None.
-    Returns fp32 [B][Hq][d]."""
+    ctx_len int32 [B]; slots int32 [B][k] or None; counts int32 [B] or None;
+    seg_kv bf16 [B][2][Hkv][S_max][d] (resident window) with seg_len int32 [B],
+    or None.  Returns fp32 [B][Hq][d]."""
     _need(q, torch.bfloat16, "q", 3)
     _need(kv, torch.bfloat16, "kv", 6)
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
@@ -186,6 +190,13 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
         _need(counts, torch.int32, "counts", 1)
         if counts.shape[0] != B:
             raise ValueError("counts must have one entry per request")
+    S_max = 0
+    if seg_kv is not None:
+        _need(seg_kv, torch.bfloat16, "seg_kv", 5)
+        _need(seg_len, torch.int32, "seg_len", 1)
+        if seg_kv.shape[0] != B or seg_kv.shape[1] != 2 or seg_kv.shape[2] != Hkv or seg_kv.shape[4] != d:
+            raise ValueError(f"seg_kv shape {tuple(seg_kv.shape)} does not match [B][2][Hkv][S_max][d]")
+        S_max = seg_kv.shape[3]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if workspace is None:
@@ -194,7 +205,8 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().lsa_gather_attend(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
-                                            _ptr(counts), _ptr(ctx_len), B, Hq, Hkv, d, k, sm_scale,
+                                            _ptr(counts), _ptr(ctx_len), _ptr(seg_kv), _ptr(seg_len), S_max, B, Hq,
+                                            Hkv, d, k, sm_scale,
                                             _ptr(workspace), ws_bytes,
                                             n_split, _ptr(out), _stream(stream)))
     return out

@@ -46,7 +46,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSliceTokens = 16;
-constexpr int kListCache = 1024;  // list entries staged in LDS per segment
+constexpr int kListCache = 512;  // list entries staged in LDS at a time
 
 template <int D>
 struct VRow;  // one lane's share of one V row: D/16 bf16 values
@@ -206,8 +206,15 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
         const int64_t cnt = a.counts[b];
         kb = cnt < 0 ? 0 : cnt > a.k ? a.k : cnt;
     }
-    const int64_t j0 = ((int64_t)s * kb) / a.n_split;
-    const int64_t j1 = ((int64_t)(s + 1) * kb) / a.n_split;
+    // then the resident segment (local window + decoded tokens) as 64-token blocks
+    int seg_len = 0;
+    if (a.seg_kv) {
+        const int sl = a.seg_len[b];
+        seg_len = sl < 0 ? 0 : sl > a.S_max ? a.S_max : sl;
+    }
+    const int64_t total = kb + (seg_len + kChunkTokens - 1) / kChunkTokens;
+    const int64_t j0 = ((int64_t)s * total) / a.n_split;
+    const int64_t j1 = ((int64_t)(s + 1) * total) / a.n_split;
     const int ctx = a.ctx[b];
     const int32_t* ids = a.ids + (int64_t)b * a.k;
 
@@ -233,12 +240,20 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     float m_run = -INFINITY;  // running max (log2 domain) of head n
     float l_run = 0.f;        // this lane's share of the running sum of head n
 
-    // The workgroup's list entries (store position, valid tokens) are staged
-    // in LDS, a segment of up to kListCache entries at a time, so computing a
-    // prefetch address never waits behind the K/V loads in flight.
-    __shared__ int sm_pos[kListCache];
+    // The workgroup's list entries (K tile offset, valid tokens, source) are
+    // staged in LDS, up to kListCache entries at a time, so computing a
+    // prefetch address never waits behind the K/V loads in flight.  Entry j
+    // < kb is gathered chunk j; entry kb + m is block m of the segment
+    // (flag kSegBit in sm_nv).  Offsets, not pointers, are staged: addresses
+    // formed from the kernel's own buffer arguments stay in the global
+    // address space, whose loads only count against vmcnt.
+    constexpr int kSegBit = 1 << 16;
+    __shared__ int64_t sm_off[kListCache];
     __shared__ int sm_nv[kListCache];
     const int32_t* pos_src = a.slots ? a.slots + (int64_t)b * a.k : ids;
+    const uint16_t* seg_b =
+        a.seg_kv ? a.seg_kv + ((int64_t)b * 2 * a.Hkv + g) * (int64_t)a.S_max * D : kv_b;  // kv_b: never used
+    const int64_t seg_v_off = (int64_t)a.Hkv * a.S_max * D;
 
     // Ring of NBUF register buffers: entry e of a segment lives in
     // buf[e % NBUF]; NBUF - 1 entries are in flight while one is processed.
@@ -248,20 +263,33 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     // kept in program order: a buffer's loads must be older than those of
     // every buffer issued after it for the waits to stay partial.
     auto issue = [&](int e, int bi) {
-        nv[bi] = sm_nv[e];
-        const uint16_t* kt = kv_b + (int64_t)sm_pos[e] * chunk_elems;
+        const int f = sm_nv[e];
+        const bool in_seg = (f & kSegBit) != 0;
+        nv[bi] = f & (kSegBit - 1);
+        const uint16_t* kt = (in_seg ? seg_b : kv_b) + sm_off[e];
+        const uint16_t* vt = kt + (in_seg ? seg_v_off : v_off);
         __builtin_amdgcn_sched_barrier(0);
-        load_slice<D>(buf[bi], kt, kt + v_off, wave, lane);
+        load_slice<D>(buf[bi], kt, vt, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
     };
     for (int64_t seg = j0; seg < j1; seg += kListCache) {
         const int segn = (int)(j1 - seg < kListCache ? j1 - seg : kListCache);
         __syncthreads();  // the previous segment's entries are no longer read
         for (int e = threadIdx.x; e < segn; e += kThreads) {
-            const int64_t c = ids[seg + e];
-            const int64_t v = (int64_t)ctx - c * kChunkTokens;
-            sm_pos[e] = pos_src[seg + e];
-            sm_nv[e] = v < 0 ? 0 : v > kChunkTokens ? kChunkTokens : (int)v;
+            const int64_t j = seg + e;
+            int64_t v;
+            int flag = 0;
+            if (j < kb) {
+                const int64_t c = ids[j];
+                v = (int64_t)ctx - c * kChunkTokens;
+                sm_off[e] = (int64_t)pos_src[j] * chunk_elems;
+            } else {
+                const int64_t m = j - kb;
+                v = (int64_t)seg_len - m * kChunkTokens;
+                sm_off[e] = m * kChunkTokens * D;
+                flag = kSegBit;
+            }
+            sm_nv[e] = (v < 0 ? 0 : v > kChunkTokens ? kChunkTokens : (int)v) | flag;
         }
         __syncthreads();
         // Every step issues one prefetch (past the segment's end it re-reads

@@ -125,7 +125,8 @@ size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
 }
 
 lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int32_t B,
+                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                             const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
                              int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
                              int32_t n_split, float* out, hipStream_t stream) {
@@ -136,6 +137,9 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     if (C_store < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "C_store=%lld must be >= 1", (long long)C_store);
     if (!std::isfinite(sm_scale)) return fail(LSA_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
     if (n_split < 0) return fail(LSA_ERR_INVALID_ARGUMENT, "n_split=%d must be >= 0", n_split);
+    if (seg_kv && (!seg_len || S_max < lsa::kChunkTokens || S_max % lsa::kChunkTokens != 0 || !aligned(seg_kv, 16)))
+        return fail(LSA_ERR_INVALID_ARGUMENT,
+                    "a segment needs seg_len, S_max a positive multiple of 64 (S_max=%d) and 16-byte alignment", S_max);
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
         return fail(LSA_ERR_INVALID_ARGUMENT, "q, kv and out need 16-byte alignment");
     if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
@@ -155,6 +159,9 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     a.slots = slots;
     a.counts = counts;
     a.ctx = ctx_len;
+    a.seg_kv = seg_kv;
+    a.seg_len = seg_kv ? seg_len : nullptr;
+    a.S_max = seg_kv ? S_max : 0;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;

@@ -28,6 +28,9 @@ struct AttendArgs {
     const int32_t* slots;   // [B][k] or nullptr
     const int32_t* counts;  // [B] entries used per request, or nullptr (all k)
     const int32_t* ctx;     // [B]
+    const uint16_t* seg_kv; // [B][2][Hkv][S_max][d] resident segment, or nullptr
+    const int32_t* seg_len; // [B] tokens in the segment
+    int S_max;
     int B, Hq, Hkv, G, d, k, n_split;
     int depth;              // chunks in flight per wave + 1 (register ring size)
     float scale_log2;       // sm_scale * log2(e)

@@ -61,11 +61,15 @@ class LsaDecoder:
                  kv: torch.Tensor | None = None, host_kv: torch.Tensor | None = None, tau: int = TAU,
                  n_split: int = 0, sm_scale: float | None = None, fetch: str = "pull", fetch_grid: int = 0,
                  delta: bool | None = None, selection: str = "topk", logit_threshold: int = 0,
-                 device="cuda"):
+                 seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None, device="cuda"):
         if (kv is None) == (host_kv is None):
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
         self.ctx_len = ctx_len
+        # resident segment: the local window and the decoded tokens, always in
+        # HBM and attended with the recalled chunks (ctx_len then bounds only
+        # the offloadable history); the caller appends to it and bumps seg_len
+        self.seg_kv, self.seg_len = seg_kv, seg_len
         self.kv = kv
         self.host_kv = host_kv
         store = kv if kv is not None else host_kv
@@ -141,9 +145,11 @@ class LsaDecoder:
         if self.lag:
             slots = self.sel_slots[sel % 2] if self.delta else self.slots
             return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
-                                     workspace=self.workspace, n_split=self.n_split, out=out, stream=stream)
+                                     workspace=self.workspace, n_split=self.n_split, out=out,
+                                     seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
         return lsa_gather_attend(q, self.kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
-                                 n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2], stream=stream)
+                                 n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2],
+                                 seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
 
     # ---- one interval ------------------------------------------------------
     def run_interval(self, i: int, q_idx: torch.Tensor, qs, outs) -> None:

@@ -53,7 +53,8 @@ def lib():
         L.oracle_topk_i64.restype = ctypes.c_int
         L.oracle_topk_f64.argtypes = [vp, i64, i64, i64, vp]
         L.oracle_topk_f64.restype = ctypes.c_int
-        L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, vp, vp]
+        L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl,
+                                           vp, vp]
         L.oracle_gather_attend.restype = ctypes.c_int
         L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
         L.oracle_fetch_chunks.restype = ctypes.c_int
@@ -106,11 +107,13 @@ def topk_chunks(keys: np.ndarray, k: int) -> np.ndarray:
 
 def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len: np.ndarray, Hkv: int,
                   sm_scale: float, slots: np.ndarray | None = None, T: int = 64,
-                  want_weights: bool = False, counts: np.ndarray | None = None):
+                  want_weights: bool = False, counts: np.ndarray | None = None,
+                  seg_kv: np.ndarray | None = None, seg_len: np.ndarray | None = None):
     """q uint16 (bf16 bits) [B][Hq][d]; kv uint16 [B][C_store][2][Hkv][T][d];
     chunk_ids int32 [B][k]; ctx_len int [B]; slots int32 [B][k] or None;
-    counts int32 [B] (entries used per request) or None.
-    Returns out float64 [B][Hq][d] (and weights [B][Hq][k*T] if asked)."""
+    counts int32 [B] (entries used per request) or None; seg_kv uint16
+    [B][2][Hkv][S_max][d] with seg_len int [B] (resident tokens) or None.
+    Returns out float64 [B][Hq][d] (and weights [B][Hq][k*T + S_max] if asked)."""
     q, kv = _c(q, np.uint16), _c(kv, np.uint16)
     chunk_ids = _c(chunk_ids, np.int32)
     ctx = _c(ctx_len, np.int32)
@@ -127,10 +130,17 @@ def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len:
     if counts is not None:
         counts = _c(counts, np.int32)
         cn = counts.ctypes.data
+    sg, sgl, S_max = 0, 0, 0
+    if seg_kv is not None:
+        seg_kv = _c(seg_kv, np.uint16)
+        seg_len = _c(seg_len, np.int32)
+        assert seg_kv.shape[0] == B and seg_kv.shape[1] == 2 and seg_kv.shape[2] == Hkv and seg_kv.shape[4] == d
+        sg, sgl, S_max = seg_kv.ctypes.data, seg_len.ctypes.data, seg_kv.shape[3]
     out = np.empty((B, Hq, d), dtype=np.float64)
-    wts = np.empty((B, Hq, k * T), dtype=np.float64) if want_weights else None
+    wts = np.empty((B, Hq, k * T + S_max), dtype=np.float64) if want_weights else None
     rc = lib().oracle_gather_attend(q.ctypes.data, kv.ctypes.data, C_store, chunk_ids.ctypes.data, sl, cn,
-                                    ctx.ctypes.data, B, Hq, Hkv, d, k, T, float(sm_scale), out.ctypes.data,
+                                    ctx.ctypes.data, sg, sgl, S_max, B, Hq, Hkv, d, k, T, float(sm_scale),
+                                    out.ctypes.data,
                                     wts.ctypes.data if wts is not None else 0)
     if rc != 0:
         raise ValueError(f"oracle attention rejected its arguments (rc={rc})")

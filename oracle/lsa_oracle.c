@@ -125,78 +125,93 @@ int oracle_topk_f64(const double* keys, int64_t R, int64_t C, int64_t k, int32_t
  *    are those of the listed chunks: list entry j names chunk chunk_ids[b][j]
  *    stored at position slots[b][j] of the store (slots == NULL: the chunk's
  *    own index); token t of that chunk is at context position
- *    chunk_ids[b][j]*T + t and is used iff that position < ctx_len[b].
+ *    chunk_ids[b][j]*T + t and is used iff that position < ctx_len[b] and
+ *    j < counts[b] (counts may be NULL: all k entries).  If seg_kv is not
+ *    NULL the first seg_len[b] tokens of the resident segment
+ *    seg_kv[b][K|V][g][0..S_max) join them (the local window and decoded
+ *    tokens, always kept).
  *      z  = (q[b][h] . K[token]) * sm_scale
  *      w  = exp(z - max z)
  *      out[b][h] = sum_token w * V[token] / sum_token w
- *    counts (may be NULL) limits request b to its first counts[b] entries.
  *    If `weights` is not NULL it receives the normalised softmax weight of
- *    every (list entry, token) pair, [B][Hq][k*T], 0 for unused tokens.
+ *    every (list entry, token) pair, [B][Hq][k*T + S_max] (segment token t at
+ *    k*T + t), 0 for unused tokens.
  *    Returns 0, -1 on bad arguments, -3 if a request has no usable token. */
 int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                         const int32_t* slots, const int32_t* counts, const int32_t* ctx_len, int64_t B, int64_t Hq,
+                         const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                         const uint16_t* seg_kv, const int32_t* seg_len, int64_t S_max, int64_t B, int64_t Hq,
                          int64_t Hkv, int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || k < 1 || T < 1) return -1;
+    if (seg_kv && (!seg_len || S_max < 1)) return -1;
     const int64_t group = Hq / Hkv;
-    const int64_t tile = T * d;              /* one (K|V, head) tile        */
+    const int64_t tile = T * d;              /* one (K|V, head) tile          */
     const int64_t chunk = 2 * Hkv * tile;    /* one chunk, K and V, all heads */
+    const int64_t n_slot = k * T + (seg_kv ? S_max : 0);
     int status = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < Hq; ++h) {
             const int64_t g = h / group;
             const uint16_t* qh = q + (b * Hq + h) * d;
-            double* z = (double*)malloc(sizeof(double) * (size_t)(k * T));
-            unsigned char* use = (unsigned char*)malloc((size_t)(k * T));
-            double m = -INFINITY;
-            int64_t n_used = 0;
+            /* the token list: K and V row of every used token, and its slot in `weights` */
+            const uint16_t** Kr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_slot);
+            const uint16_t** Vr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_slot);
+            int64_t* where = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_slot);
+            double* z = (double*)malloc(sizeof(double) * (size_t)n_slot);
+            int64_t n = 0;
             const int64_t kb = counts ? counts[b] : k;
-            for (int64_t j = 0; j < k; ++j) {
+            for (int64_t j = 0; j < k && j < kb; ++j) {
                 const int64_t c = chunk_ids[b * k + j];
                 const int64_t p = slots ? slots[b * k + j] : c;
                 const uint16_t* K = kv + (b * C_store + p) * chunk + (0 * Hkv + g) * tile;
-                for (int64_t t = 0; t < T; ++t) {
-                    const int64_t e = j * T + t;
-                    use[e] = j < kb && (c * T + t) < (int64_t)ctx_len[b];
-                    z[e] = 0.0;
-                    if (!use[e]) continue;
-                    double dot = 0.0;
-                    for (int64_t i = 0; i < d; ++i) dot += bf16_to_double(qh[i]) * bf16_to_double(K[t * d + i]);
-                    z[e] = dot * sm_scale;
-                    if (z[e] > m) m = z[e];
-                    ++n_used;
+                const uint16_t* V = kv + (b * C_store + p) * chunk + (1 * Hkv + g) * tile;
+                for (int64_t t = 0; t < T; ++t)
+                    if (c * T + t < (int64_t)ctx_len[b]) {
+                        Kr[n] = K + t * d;
+                        Vr[n] = V + t * d;
+                        where[n++] = j * T + t;
+                    }
+            }
+            if (seg_kv) {
+                const uint16_t* K = seg_kv + ((b * 2 + 0) * Hkv + g) * S_max * d;
+                const uint16_t* V = seg_kv + ((b * 2 + 1) * Hkv + g) * S_max * d;
+                for (int64_t t = 0; t < seg_len[b] && t < S_max; ++t) {
+                    Kr[n] = K + t * d;
+                    Vr[n] = V + t * d;
+                    where[n++] = k * T + t;
                 }
             }
             double* o = out + (b * Hq + h) * d;
             for (int64_t i = 0; i < d; ++i) o[i] = 0.0;
-            if (n_used == 0) {
+            if (n == 0) {
 #pragma omp atomic write
                 status = -3;
             } else {
+                double m = -INFINITY;
+                for (int64_t e = 0; e < n; ++e) {
+                    double dot = 0.0;
+                    for (int64_t i = 0; i < d; ++i) dot += bf16_to_double(qh[i]) * bf16_to_double(Kr[e][i]);
+                    z[e] = dot * sm_scale;
+                    if (z[e] > m) m = z[e];
+                }
                 double l = 0.0;
-                for (int64_t e = 0; e < k * T; ++e) {
-                    if (!use[e]) continue;
+                for (int64_t e = 0; e < n; ++e) {
                     z[e] = exp(z[e] - m); /* z now holds the unnormalised weight */
                     l += z[e];
                 }
-                for (int64_t j = 0; j < k; ++j) {
-                    const int64_t c = chunk_ids[b * k + j];
-                    const int64_t p = slots ? slots[b * k + j] : c;
-                    const uint16_t* V = kv + (b * C_store + p) * chunk + (1 * Hkv + g) * tile;
-                    for (int64_t t = 0; t < T; ++t) {
-                        const int64_t e = j * T + t;
-                        if (!use[e]) continue;
-                        for (int64_t i = 0; i < d; ++i) o[i] += z[e] * bf16_to_double(V[t * d + i]);
-                    }
-                }
+                for (int64_t e = 0; e < n; ++e)
+                    for (int64_t i = 0; i < d; ++i) o[i] += z[e] * bf16_to_double(Vr[e][i]);
                 for (int64_t i = 0; i < d; ++i) o[i] /= l;
                 if (weights) {
-                    double* wrow = weights + (b * Hq + h) * k * T;
-                    for (int64_t e = 0; e < k * T; ++e) wrow[e] = use[e] ? z[e] / l : 0.0;
+                    double* wrow = weights + (b * Hq + h) * n_slot;
+                    for (int64_t e = 0; e < n_slot; ++e) wrow[e] = 0.0;
+                    for (int64_t e = 0; e < n; ++e) wrow[where[e]] = z[e] / l;
                 }
             }
+            free(Kr);
+            free(Vr);
+            free(where);
             free(z);
-            free(use);
         }
     return status;
 }

@@ -94,8 +94,9 @@ def test_attend_validation(lsa, lib):
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["q"], a["kv"], a["C"], a["ids"], a["slots"], 0, a["ctx"], a["B"], a["Hq"], a["Hkv"], a["d"],
-                 a["k"], a["scale"], a["ws"], a["wsb"], a["ns"], a["out"], 0)
+        return f(a["q"], a["kv"], a["C"], a["ids"], a["slots"], 0, a["ctx"], a.get("seg", 0), a.get("seg_len", 0),
+                 a.get("S_max", 0), a["B"], a["Hq"], a["Hkv"], a["d"], a["k"], a["scale"], a["ws"], a["wsb"],
+                 a["ns"], a["out"], 0)
 
     assert call(q=0) == 1
     assert call(Hq=60) == 1 and "multiple" in _err(lib)
@@ -106,6 +107,8 @@ def test_attend_validation(lsa, lib):
     assert call(scale=float("nan")) == 1
     assert call(ns=-1) == 1
     assert call(out=BOGUS + 4) == 1 and "alignment" in _err(lib)
+    assert call(seg=BOGUS) == 1 and "segment" in _err(lib)
+    assert call(seg=BOGUS, seg_len=BOGUS, S_max=100) == 1 and "multiple of 64" in _err(lib)
     need = lsa.lsa_gather_attend_workspace_size(2, 64, 8, 128, 4, 2)
     assert need > 0
     assert call(ns=2) == 3 and "workspace" in _err(lib)

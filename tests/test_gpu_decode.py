@@ -155,3 +155,48 @@ def test_decode_threshold_selection(oracle_lib):
                                                W.ctx_lens(w)[b:b + 1], w.Hkv, w.sm_scale,
                                                slots=np.arange(len(idsb), dtype=np.int32)[None])
                 check_attention(o[t][b].cpu().numpy(), ref[0], f"threshold interval {it} request {b} step {t}")
+
+
+def test_decode_with_local_window_and_decoded_tokens(oracle_lib):
+    """Recalled history chunks + the resident local window, which grows by one
+    freshly decoded token per step (the caller writes the token's K/V and
+    bumps seg_len between steps); history chunks overlapping the window are
+    excluded from the indexer's scan by construction (ctx_len = history)."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"]
+    W_len, S_max, steps = 1024, 1024 + 128, 6
+    hist = w.N - W_len                       # tokens of the offloadable history
+    C_hist = hist // 64
+    dev = torch.device("cuda")
+    K = W.indexer_keys(w)[:, :C_hist].copy()  # only history chunks are scored
+    kv = W.device_kv_store(w, dev)
+    seg = synth.normal_bf16((w.B, 2, w.Hkv, S_max, w.d), 5, synth.stream(synth.TAG_MISC, 3200))
+    seg_d = to_dev_bf16(seg)
+    seg_len = torch.full((w.B,), W_len, dtype=torch.int32, device=dev)
+    ctx = torch.full((w.B,), hist, dtype=torch.int32, device=dev)
+    dec = LsaDecoder(k_idx=to_dev(K), ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv[:, :C_hist].contiguous(),
+                     seg_kv=seg_d, seg_len=seg_len)
+    q_idx = W.indexer_query(w, 0)
+    _, _, ids_ref = oracle_lib.select(q_idx, K, w.k, w.alpha)
+    kv_host = None
+    for t in range(steps):
+        q = W.attn_query(w, t)
+        out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        if t == 0:
+            dec.reselect(to_dev(q_idx), 0)
+        dec.attend(to_dev_bf16(q), 0, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(dec.sel_ids[0].cpu().numpy(), ids_ref)
+        n_seg = W_len + t
+        for b in (0, w.B - 1):
+            chunks = W.kv_chunks(w, b, ids_ref[b])[None]
+            ref = oracle_lib.gather_attend(q[b:b + 1], chunks, ids_ref[b:b + 1], np.array([hist]), w.Hkv,
+                                           w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None],
+                                           seg_kv=seg[b:b + 1], seg_len=np.array([n_seg], dtype=np.int32))
+            check_attention(out[b].cpu().numpy(), ref[0], f"window step {t} request {b}")
+        seg_len += 1  # the token just decoded joins the window

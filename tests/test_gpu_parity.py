@@ -234,6 +234,33 @@ def test_attend_counts_parity(lsa, oracle_lib, synth_lib, n_split):
     check_attention(out[live], ref, "counts")
 
 
+@pytest.mark.parametrize("S,seg_lens,counts,n_split", [
+    (8192, [8192, 8000, 1, 0], [12, 12, 12, 12], 0),   # a full 8K window, partial blocks, empty
+    (256, [200, 256, 64, 65], [3, 0, 12, 7], 3),       # a request with the window only
+    (128, [128, 1, 127, 2], [12, 12, 12, 12], 1),      # no split
+])
+def test_attend_segment_parity(lsa, oracle_lib, synth_lib, S, seg_lens, counts, n_split):
+    """Recalled chunks plus the resident local window / decoded tokens in
+    one softmax."""
+    B, Hq, Hkv, d, C, k = 4, 64, 8, 128, 30, 12
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=60, qscale=2.0)
+    seg = synth_lib.normal_bf16((B, 2, Hkv, S, d), 61, synth_lib.stream(synth_lib.TAG_MISC, 2700 + S))
+    ids = _ids(synth_lib, B, C, k, seed=62)
+    counts = np.array(counts, dtype=np.int32)
+    seg_len = np.array(seg_lens, dtype=np.int32)
+    ctx = np.full(B, C * 64 - 17, dtype=np.int32)
+    out = lsa.lsa_gather_attend(to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx), 1 / math.sqrt(d),
+                                n_split=n_split, counts=to_dev(counts), seg_kv=to_dev_bf16(seg),
+                                seg_len=to_dev(seg_len)).cpu().numpy()
+    live = [b for b in range(B) if counts[b] > 0 or seg_len[b] > 0]
+    ref = oracle_lib.gather_attend(q[live], kv[live], ids[live], ctx[live], Hkv, 1 / math.sqrt(d),
+                                   counts=counts[live], seg_kv=seg[live], seg_len=seg_len[live])
+    check_attention(out[live], ref, "segment")
+    for b in range(B):
+        if b not in live:
+            assert (out[b] == 0).all()
+
+
 def test_attend_no_valid_token_gives_zero(lsa, synth_lib):
     q, kv = _problem(synth_lib, 2, 8, 1, 64, 4, seed=3)
     ids = np.array([[2, 3], [0, 1]], dtype=np.int32)

@@ -457,3 +457,36 @@ def test_attention_counts_truncate_lists(oracle_lib, synth_lib):
     for b in range(B):
         ref = oracle_lib.gather_attend(q[b:b + 1], kv[b:b + 1], ids[b:b + 1, :counts[b]], ctx[b:b + 1], Hkv, 0.125)
         np.testing.assert_allclose(out[b], ref[0], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- resident segment (local window)
+
+def test_segment_joins_chunks_in_one_softmax(oracle_lib, synth_lib):
+    """Chunks plus a resident segment equal dense SDPA over the concatenated
+    tokens; with no chunk in use (counts = 0) the segment alone is dense
+    attention over it; the weights of both parts sum to 1."""
+    import torch
+    B, Hq, Hkv, d, C, S = 2, 16, 2, 64, 5, 128
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=16, qscale=3.0)
+    seg = synth_lib.normal_bf16((B, 2, Hkv, S, d), 16, synth_lib.stream(synth_lib.TAG_MISC, 2600))
+    seg_len = np.array([100, 1], dtype=np.int32)
+    ids = np.array([[0, 3], [1, 4]], dtype=np.int32)
+    ctx = np.array([C * 64 - 30, C * 64], dtype=np.int32)
+    out, w = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125, seg_kv=seg, seg_len=seg_len, want_weights=True)
+    np.testing.assert_allclose(w.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+    for b in range(B):
+        toks = [c * 64 + t for c in ids[b] for t in range(64) if c * 64 + t < ctx[b]]
+        K = np.concatenate([f32(kv[b, :, 0]).transpose(1, 0, 2, 3).reshape(Hkv, C * 64, d)[:, toks],
+                            f32(seg[b, 0, :, :seg_len[b]])], axis=1)
+        V = np.concatenate([f32(kv[b, :, 1]).transpose(1, 0, 2, 3).reshape(Hkv, C * 64, d)[:, toks],
+                            f32(seg[b, 1, :, :seg_len[b]])], axis=1)
+        Q = torch.from_numpy(f32(q[b]).astype(np.float64)).reshape(1, Hq, 1, d)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q, torch.from_numpy(K.astype(np.float64))[None], torch.from_numpy(V.astype(np.float64))[None],
+            scale=0.125, enable_gqa=True).reshape(Hq, d).numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=1e-12, atol=1e-14)
+    # segment only
+    only = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125, counts=np.zeros(B, dtype=np.int32),
+                                    seg_kv=seg, seg_len=seg_len)
+    np.testing.assert_allclose(only[1], np.tile(f32(seg[1, 1, :, 0]).astype(np.float64).repeat(Hq // Hkv, 0)
+                                                .reshape(Hq, d), 1), rtol=0, atol=0)
