@@ -38,31 +38,35 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def configure(L):
+    """Declare the C signatures on a loaded oracle library."""
+    i64, vp, dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+    L.oracle_index_logits.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+    L.oracle_index_logits.restype = None
+    L.oracle_index_scores.argtypes = [vp, i64, ctypes.c_float, vp]
+    L.oracle_index_scores.restype = None
+    L.oracle_topk_i64.argtypes = [vp, i64, i64, i64, vp]
+    L.oracle_topk_i64.restype = ctypes.c_int
+    L.oracle_topk_f64.argtypes = [vp, i64, i64, i64, vp]
+    L.oracle_topk_f64.restype = ctypes.c_int
+    L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl,
+                                       vp, vp]
+    L.oracle_gather_attend.restype = ctypes.c_int
+    L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
+    L.oracle_fetch_chunks.restype = ctypes.c_int
+    L.oracle_pool_assign.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, vp]
+    L.oracle_pool_assign.restype = ctypes.c_int
+    L.oracle_threshold_i64.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+    L.oracle_threshold_i64.restype = ctypes.c_int
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
-        i64, vp, dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
-        L.oracle_index_logits.argtypes = [vp, vp, i64, i64, i64, i64, vp]
-        L.oracle_index_logits.restype = None
-        L.oracle_index_scores.argtypes = [vp, i64, ctypes.c_float, vp]
-        L.oracle_index_scores.restype = None
-        L.oracle_topk_i64.argtypes = [vp, i64, i64, i64, vp]
-        L.oracle_topk_i64.restype = ctypes.c_int
-        L.oracle_topk_f64.argtypes = [vp, i64, i64, i64, vp]
-        L.oracle_topk_f64.restype = ctypes.c_int
-        L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl,
-                                           vp, vp]
-        L.oracle_gather_attend.restype = ctypes.c_int
-        L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
-        L.oracle_fetch_chunks.restype = ctypes.c_int
-        L.oracle_pool_assign.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, vp]
-        L.oracle_pool_assign.restype = ctypes.c_int
-        L.oracle_threshold_i64.argtypes = [vp, i64, i64, i64, i64, vp, vp]
-        L.oracle_threshold_i64.restype = ctypes.c_int
-        _lib = L
+        _lib = configure(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
