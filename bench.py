@@ -56,10 +56,11 @@ def attend_bytes_per_launch(w) -> int:
     return kv + q + out + ids
 
 
-def step_bytes(w) -> int:
-    """Algorithmic bytes of one decode step: the attention launch plus the
-    indexer scan (every key byte once) amortised over tau steps."""
-    return attend_bytes_per_launch(w) + (w.B * w.C * w.d_idx) // w.tau
+def step_bytes(w, layers: int = 1) -> int:
+    """Algorithmic bytes of one decode step: one attention launch per layer
+    plus the indexer scan (every key byte once, one scan shared by all
+    layers) amortised over tau steps."""
+    return layers * attend_bytes_per_launch(w) + (w.B * w.C * w.d_idx) // w.tau
 
 
 def kernel_sha() -> str:
@@ -80,7 +81,7 @@ def traffic_for_current_kernel(w):
     return t.get("hbm_bytes_per_launch")
 
 
-def setup(w, n_split: int):
+def setup(w, n_split: int, layers: int = 1):
     import torch
 
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
@@ -91,8 +92,14 @@ def setup(w, n_split: int):
     K = torch.from_numpy(W.indexer_keys(w)).to(dev)
     ctx = torch.from_numpy(W.ctx_lens(w)).to(dev)
     kv = W.device_kv_store(w, dev)
-    dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split, device=dev)
-    log(f"[bench] inputs placed in HBM in {time.time() - t0:.1f}s (K/V {kv.numel() * 2 / 1e9:.2f} GB)")
+    if layers > 1:  # further layers: the same synthetic recipe, each its own store
+        stores = [kv] + [W.device_kv_store(w.replace(seed=w.seed + 1000 * l), dev) for l in range(1, layers)]
+        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=stores, n_split=n_split,
+                         device=dev)
+    else:
+        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split, device=dev)
+    log(f"[bench] inputs placed in HBM in {time.time() - t0:.1f}s (K/V {layers * kv.numel() * 2 / 1e9:.2f} GB, "
+        f"{layers} layer(s))")
     return dec
 
 
@@ -110,9 +117,15 @@ def make_queries(w, n_steps: int):
 
 
 def enqueue_steps(dec, w, q_all, qidx, n_steps, out):
+    L = len(dec.layers) if dec.layers is not None else 1
     for i in range((n_steps + w.tau - 1) // w.tau):
         ts = range(i * w.tau, min((i + 1) * w.tau, n_steps))
-        dec.run_interval(i, qidx[i], [q_all[t] for t in ts], [out] * len(ts))
+        if L == 1:
+            dec.run_interval(i, qidx[i], [q_all[t] for t in ts], [out] * len(ts))
+        else:  # layer l at step t uses query (t + 7 l) of the generated set: distinct per layer
+            n_q = q_all.shape[0]
+            dec.run_interval(i, qidx[i], [[q_all[(t + 7 * l) % n_q] for l in range(L)] for t in ts],
+                             [[out] * L for _ in ts])
 
 
 def capture(dec, w, q_all, qidx, n_steps, out):
@@ -333,6 +346,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--layers", type=int, default=1, help="layers sharing one selection (HBM-resident only)")
     ap.add_argument("--fetch", default="pull", choices=("pull", "memcpy"), help="host-tier fetch method")
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
     ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
@@ -370,7 +384,7 @@ def main():
         host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
                         False if args.no_delta else None)
         return
-    dec = setup(w, args.n_split)
+    dec = setup(w, args.n_split, args.layers)
     n_q = max(args.steps, args.warmup, w.tau)
     q_all, qidx = make_queries(w, n_q)
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
@@ -422,7 +436,8 @@ def main():
         f"{achieved:.0f} GB/s algorithmic")
     traffic = traffic_for_current_kernel(w)
 
-    sb = step_bytes(w)
+    sb = step_bytes(w, args.layers)
+    layer_txt = "one layer" if args.layers == 1 else f"{args.layers} layers sharing one selection"
     result = {
         "metric": METRIC,
         "value": round(steps_s, 2),
@@ -437,7 +452,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.name} context decode, one layer: batch {w.B}, {w.Hq} query / {w.Hkv} KV heads, "
+            "workload": (f"{w.name} context decode, {layer_txt}: batch {w.B}, {w.Hq} query / {w.Hkv} KV heads, "
                          f"head dim {w.d}, {w.N} tokens = {w.C} chunks of {w.T}, top-{w.k} chunks "
                          f"re-selected every {w.tau} steps, int8 indexer dim {w.d_idx}"),
             "global_batch": w.B,

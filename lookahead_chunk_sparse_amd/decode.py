@@ -1,4 +1,4 @@
-"""Decode schedule for one attention layer on one GPU.
+"""Decode schedule for one attention layer (or several sharing a selection) on one GPU.
 
 Every tau = 64 decode steps the memory indexer scores all chunks against the
 current indexer query and the top-k chunks are re-selected; every step
@@ -28,6 +28,14 @@ pages' sigmoid gating (selection="threshold": chunks whose score passes 0.5,
 i.e. logit > 0, at most k of them; 2.1 Architecture and 2.4 Configuration of
 the summary), whose budget varies per request.
 
+Several layers can share one selection (kv given as a list of per-layer
+stores): each interval runs one indexer scan and selection, then every step
+attends over the same chunks in every layer.  Reusing one layer's selection
+in the following layers is how the indexer cost is amortised across depth
+(the "Daily Papers" listing for the query "lightning indexer": the LongCat
+LSA abstract's cross-layer indexing, and the Multi-layer Indexer and
+IndexCache abstracts, which reuse a top-k across consecutive layers).
+
 This module only orders calls into liblsa.so on HIP streams and records
 events; it computes nothing itself.
 """
@@ -49,11 +57,12 @@ def selection_for_step(t: int, tau: int = TAU, lag: int = 0) -> int:
 
 
 class LsaDecoder:
-    """Decode state of one layer: indexer keys, K/V placement, selection buffers.
+    """Decode state: indexer keys, K/V placement, selection buffers.
 
     k_idx    device int8 [B][C][d_idx]
     ctx_len  device int32 [B]
-    kv       device bf16 [B][C][2][Hkv][64][d]        (HBM-resident store), or
+    kv       device bf16 [B][C][2][Hkv][64][d]        (HBM-resident store; a list
+                                                        of such: one per layer), or
     host_kv  pinned bf16 [B][C][2][Hkv][64][d]        (host tier; pool of k slots x 2)
     """
 
@@ -66,6 +75,11 @@ class LsaDecoder:
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
         self.ctx_len = ctx_len
+        self.layers = list(kv) if isinstance(kv, (list, tuple)) else None
+        if self.layers is not None:
+            if host_kv is not None:
+                raise NotImplementedError("several layers are implemented for the HBM-resident store")
+            kv = self.layers[0]
         # resident segment: the local window and the decoded tokens, always in
         # HBM and attended with the recalled chunks (ctx_len then bounds only
         # the offloadable history); the caller appends to it and bumps seg_len
@@ -137,7 +151,7 @@ class LsaDecoder:
             lsa_topk_chunks(self.logits.view(self.B, self.C), self.k, chunk_ids=ids, stream=stream)
         return ids
 
-    def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None, layer: int = 0) -> torch.Tensor:
         """One decode step's attention with selection `sel` (on the host tier
         with the delta fetch, the selection's pool slots must have been
         assigned, as run_interval does)."""
@@ -147,7 +161,8 @@ class LsaDecoder:
             return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
                                      workspace=self.workspace, n_split=self.n_split, out=out,
                                      seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
-        return lsa_gather_attend(q, self.kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
+        kv = self.layers[layer] if self.layers is not None else self.kv
+        return lsa_gather_attend(q, kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
                                  n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2],
                                  seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
 
@@ -159,7 +174,11 @@ class LsaDecoder:
         if not self.lag:
             self.reselect(q_idx, i)
             for q, o in zip(qs, outs):
-                self.attend(q, i, o)
+                if self.layers is None:
+                    self.attend(q, i, o)
+                else:  # q[l] and o[l] per layer; one selection for all layers
+                    for layer in range(len(self.layers)):
+                        self.attend(q[layer], i, o[layer], layer=layer)
             return
         main = torch.cuda.current_stream()
         self.reselect(q_idx, i)

@@ -200,3 +200,46 @@ def test_decode_with_local_window_and_decoded_tokens(oracle_lib):
                                            seg_kv=seg[b:b + 1], seg_len=np.array([n_seg], dtype=np.int32))
             check_attention(out[b].cpu().numpy(), ref[0], f"window step {t} request {b}")
         seg_len += 1  # the token just decoded joins the window
+
+
+def test_decode_layers_share_one_selection(oracle_lib):
+    """Three layers, one indexer scan per interval: every layer attends over
+    the chunks that scan selected, with its own K/V and its own query."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"]
+    L, n_steps = 3, 70  # crosses one re-selection
+    dev = torch.device("cuda")
+    K = W.indexer_keys(w)
+    layer_w = [w.replace(seed=w.seed + 1000 * l) for l in range(L)]
+    stores = [W.device_kv_store(lw, dev) for lw in layer_w]
+    dec = LsaDecoder(k_idx=to_dev(K), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k, alpha=w.alpha, kv=stores)
+    check_t = (0, 63, 64, 69)
+    qh = {(t, l): synth.normal_bf16((w.B, w.Hq, w.d), 5, synth.stream(synth.TAG_MISC, 3300 + 10 * t + l))
+          for t in check_t for l in range(L)}
+    keep = {key: torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for key in qh}
+    scratch = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+    filler = to_dev_bf16(W.attn_query(w, 1))
+    sels = []
+    for i in range(2):
+        ts = range(i * w.tau, min((i + 1) * w.tau, n_steps))
+        qs = [[to_dev_bf16(qh[(t, l)]) if (t, l) in qh else filler for l in range(L)] for t in ts]
+        outs = [[keep.get((t, l), scratch) for l in range(L)] for t in ts]
+        dec.run_interval(i, to_dev(W.indexer_query(w, i)), qs, outs)
+        torch.cuda.synchronize()
+        sels.append(dec.sel_ids[i % 2].cpu().numpy().copy())
+    for i in range(2):
+        _, _, ref_ids = oracle_lib.select(W.indexer_query(w, i), K, w.k, w.alpha)
+        assert np.array_equal(sels[i], ref_ids), f"selection {i}"
+    ctx = W.ctx_lens(w)
+    for (t, l), o in keep.items():
+        ids = sels[t // w.tau]
+        for b in (0, w.B - 1):
+            chunks = W.kv_chunks(layer_w[l], b, ids[b])[None]
+            ref = oracle_lib.gather_attend(qh[(t, l)][b:b + 1], chunks, ids[b:b + 1], ctx[b:b + 1], w.Hkv,
+                                           w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None])
+            check_attention(o[b].cpu().numpy(), ref[0], f"layer {l} step {t} request {b}")
