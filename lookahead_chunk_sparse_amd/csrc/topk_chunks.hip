@@ -5,12 +5,13 @@
 // highest are kept; ties go to the lower chunk index).
 //
 // One 1024-thread workgroup per row; thread t keeps logits [t*KPT, (t+1)*KPT)
-// in registers as order-preserving unsigned keys (logit XOR 0x80000000).
-//  1. Radix select, one bit per pass, from the most significant bit where the
-//     row's keys differ (a block-wide AND/OR finds the common leading bits):
-//     a pass counts the keys of the current bucket whose next bit is set
-//     (cross-lane reduction per wave, then LDS across the 16 waves) and
-//     descends into the half that holds the k-th largest key.  The result is that key v* and
+// in registers as order-preserving unsigned keys (logit XOR 0x80000000),
+// offset by the row's smallest key so that only the bits spanning the row's
+// range remain (logits of both signs would otherwise differ in every bit).
+//  1. Radix select, 8 bits per pass from the top of the range: the keys of
+//     the current bucket are counted per digit into an LDS histogram
+//     (ds_add), then one wave finds, by a suffix scan over the 256 bins, the
+//     digit that holds the k-th largest key.  The result is that key v* and
 //     `need`, the number of keys equal to v* that belong to the selection.
 //  2. Ordered compaction: keys > v* are taken; keys == v* are taken while
 //     their rank among equal keys, in index order, is below `need`.  Two
@@ -65,16 +66,19 @@ __device__ inline int block_excl_scan(int v, int* sm, int lane, int wave) {
     return before + incl - v;
 }
 
-__device__ inline uint32_t wave_or(uint32_t v) {
+__device__ inline uint32_t wave_min(uint32_t v) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v |= (uint32_t)__shfl_xor((int)v, off);
+    for (int off = 32; off > 0; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off));
     return v;
 }
-__device__ inline uint32_t wave_and(uint32_t v) {
+__device__ inline uint32_t wave_max(uint32_t v) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v &= (uint32_t)__shfl_xor((int)v, off);
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
     return v;
 }
+
+constexpr int kDigitBits = 8;
+constexpr int kBins = 1 << kDigitBits;
 
 // Threshold mode (counts != nullptr): the row keeps the chunks whose logit
 // exceeds `thr`, at most k of them (the first k in the same order when more
@@ -84,36 +88,37 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ out, int32_t thr,
                                                         int32_t* __restrict__ counts) {
     __shared__ int sm_i[kWaves];
-    __shared__ uint32_t sm_or[kWaves], sm_and[kWaves];
+    __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
+    __shared__ int sm_hist[kBins];
+    __shared__ int sm_pick[2];  // digit chosen by the pass, keys still needed
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int32_t* row = logits + (int64_t)blockIdx.x * C;
     int32_t* dst = out + (int64_t)blockIdx.x * k;
     const int base = tid * KPT;
 
     uint32_t key[KPT];
-    uint32_t lor = 0u, land = 0xFFFFFFFFu;
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const int idx = base + e;
         key[e] = idx < C ? ((uint32_t)row[idx] ^ 0x80000000u) : 0u;
         if (idx < C) {
-            lor |= key[e];
-            land &= key[e];
+            lmin = min(lmin, key[e]);
+            lmax = max(lmax, key[e]);
         }
     }
-    lor = wave_or(lor);
-    land = wave_and(land);
+    lmin = wave_min(lmin);
+    lmax = wave_max(lmax);
     if (lane == 0) {
-        sm_or[wave] = lor;
-        sm_and[wave] = land;
+        sm_min[wave] = lmin;
+        sm_max[wave] = lmax;
     }
     __syncthreads();
-    lor = 0u;
-    land = 0xFFFFFFFFu;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        lor |= sm_or[w];
-        land &= sm_and[w];
+        kmin = min(kmin, sm_min[w]);
+        kmax = max(kmax, sm_max[w]);
     }
 
     // --- how many to keep ---
@@ -130,30 +135,56 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
         if (kk == 0) return;  // uniform: every thread saw the same sum
     }
 
-    // --- radix select over the bits where keys differ ---
-    uint32_t prefix = land;  // correct on every common bit
-    int need = kk;
-    const uint32_t diff = lor ^ land;
-    if (diff != 0u) {
-        const int top = 31 - __builtin_clz(diff);
-        uint32_t mask = top == 31 ? 0u : ~((2u << top) - 1u);  // bits above `top`
-        prefix &= mask;
-        for (int bit = top; bit >= 0; --bit) {
-            const uint32_t bitv = 1u << bit;
-            const uint32_t cand = prefix | bitv;
-            const uint32_t mb = mask | bitv;
-            int cnt = 0;
+    // --- radix select on key - kmin, 8 bits per pass ---
+    // Keys of padding slots (index >= C) are never counted.
+    uint32_t rel[KPT];
 #pragma unroll
-            for (int e = 0; e < KPT; ++e) cnt += (base + e < C) && ((key[e] & mb) == cand);
-            cnt = block_sum(cnt, sm_i, lane, wave);
-            if (cnt >= need)
-                prefix = cand;
-            else
-                need -= cnt;
-            mask = mb;
+    for (int e = 0; e < KPT; ++e) rel[e] = key[e] - kmin;  // < 2^nb for valid keys
+    const uint32_t range = kmax - kmin;
+    const int nb = range == 0u ? 0 : 32 - __builtin_clz(range);
+    uint64_t prefix = 0;  // digits chosen so far, as the value of key - kmin above bit `hi`
+    int need = kk;
+    for (int hi = nb; hi > 0; hi -= kDigitBits) {
+        const int w = hi < kDigitBits ? hi : kDigitBits;
+        const int sh = hi - w;
+        for (int j = tid; j < kBins; j += kThreads) sm_hist[j] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const uint64_t r = rel[e];
+            if (base + e < C && (r >> hi) == prefix)
+                atomicAdd(&sm_hist[(int)((r >> sh) & ((1u << w) - 1u))], 1);
         }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l holds bins 4l..4l+3; exclusive suffix sum over lanes
+            int h[4], sl = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = sm_hist[4 * lane + j];
+                sl += h[j];
+            }
+            int suf = sl;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int u = __shfl_down(suf, off);
+                if (lane + off < 64) suf += u;
+            }
+            int above = suf - sl;  // keys of the bucket in higher digits
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                if (above < need && need <= above + h[j]) {  // exactly one (lane, j) matches
+                    sm_pick[0] = 4 * lane + j;
+                    sm_pick[1] = need - above;
+                }
+                above += h[j];
+            }
+        }
+        __syncthreads();
+        prefix = (prefix << w) | (uint64_t)sm_pick[0];
+        need = sm_pick[1];
     }
-    const uint32_t vstar = prefix;
+    const uint32_t vstar = kmin + (uint32_t)prefix;
 
     // --- ordered compaction ---
     int n_gt = 0, n_eq = 0;
