@@ -285,6 +285,25 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
     print(json.dumps(res), flush=True)
 
 
+def copy_bandwidth(n_bytes: int = 1 << 30, reps: int = 20) -> float:
+    """GB/s of a plain device copy (torch's copy kernel) of n_bytes, counting
+    the bytes read and the bytes written, event-timed over reps copies."""
+    import torch
+    a = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        b.copy_(a)
+    end.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n_bytes * reps / (start.elapsed_time(end) * 1e-3) / 1e9
+    del a, b
+    return gbs
+
+
 def copy_calibration(n_bytes: int, reps: int):
     """A plain device-to-device copy of known size (for counter scaling)."""
     import torch
@@ -435,6 +454,8 @@ def main():
     log(f"[bench] attention launch: mean {mean_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
     traffic = traffic_for_current_kernel(w)
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy (torch, 1 GiB, read + write bytes): {copy_gbs:.0f} GB/s")
 
     sb = step_bytes(w, args.layers)
     layer_txt = "one layer" if args.layers == 1 else f"{args.layers} layers sharing one selection"
@@ -464,6 +485,8 @@ def main():
             "step_bytes": sb,
             "step_GBs": round(sb * steps_s / 1e9, 1),
             "step_frac_of_hbm_peak": round(sb * steps_s / 1e9 / HBM_PEAK_GBS, 4),
+            "copy_GBs": round(copy_gbs, 1),
+            "step_frac_of_copy": round(sb * steps_s / 1e9 / copy_gbs, 4),
         },
         "roofline": {
             "bound": "hbm",
