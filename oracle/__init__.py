@@ -50,8 +50,10 @@ def configure(L):
     L.oracle_topk_f64.argtypes = [vp, i64, i64, i64, vp]
     L.oracle_topk_f64.restype = ctypes.c_int
     L.oracle_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl,
-                                       vp, vp]
+                                       vp, vp, vp, vp, i64]
     L.oracle_gather_attend.restype = ctypes.c_int
+    L.oracle_topk_tokens.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
+    L.oracle_topk_tokens.restype = ctypes.c_int
     L.oracle_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64]
     L.oracle_fetch_chunks.restype = ctypes.c_int
     L.oracle_pool_assign.argtypes = [vp, vp, i64, vp, i64, i64, i64, vp, vp]
@@ -112,11 +114,14 @@ def topk_chunks(keys: np.ndarray, k: int) -> np.ndarray:
 def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len: np.ndarray, Hkv: int,
                   sm_scale: float, slots: np.ndarray | None = None, T: int = 64,
                   want_weights: bool = False, counts: np.ndarray | None = None,
-                  seg_kv: np.ndarray | None = None, seg_len: np.ndarray | None = None):
+                  seg_kv: np.ndarray | None = None, seg_len: np.ndarray | None = None,
+                  tok: np.ndarray | None = None, tok_counts: np.ndarray | None = None):
     """q uint16 (bf16 bits) [B][Hq][d]; kv uint16 [B][C_store][2][Hkv][T][d];
     chunk_ids int32 [B][k]; ctx_len int [B]; slots int32 [B][k] or None;
     counts int32 [B] (entries used per request) or None; seg_kv uint16
-    [B][2][Hkv][S_max][d] with seg_len int [B] (resident tokens) or None.
+    [B][2][Hkv][S_max][d] with seg_len int [B] (resident tokens) or None;
+    tok int32 [B][k_tok] (list positions j*T + t of the tokens to use) with
+    tok_counts int32 [B] or None: None uses every token of the used entries.
     Returns out float64 [B][Hq][d] (and weights [B][Hq][k*T + S_max] if asked)."""
     q, kv = _c(q, np.uint16), _c(kv, np.uint16)
     chunk_ids = _c(chunk_ids, np.int32)
@@ -140,15 +145,47 @@ def gather_attend(q: np.ndarray, kv: np.ndarray, chunk_ids: np.ndarray, ctx_len:
         seg_len = _c(seg_len, np.int32)
         assert seg_kv.shape[0] == B and seg_kv.shape[1] == 2 and seg_kv.shape[2] == Hkv and seg_kv.shape[4] == d
         sg, sgl, S_max = seg_kv.ctypes.data, seg_len.ctypes.data, seg_kv.shape[3]
+    tk, tkc, k_tok = 0, 0, 0
+    if tok is not None:
+        tok = _c(tok, np.int32)
+        assert tok.shape[0] == B
+        tk, k_tok = tok.ctypes.data, tok.shape[1]
+        if tok_counts is not None:
+            tok_counts = _c(tok_counts, np.int32)
+            tkc = tok_counts.ctypes.data
     out = np.empty((B, Hq, d), dtype=np.float64)
     wts = np.empty((B, Hq, k * T + S_max), dtype=np.float64) if want_weights else None
     rc = lib().oracle_gather_attend(q.ctypes.data, kv.ctypes.data, C_store, chunk_ids.ctypes.data, sl, cn,
                                     ctx.ctypes.data, sg, sgl, S_max, B, Hq, Hkv, d, k, T, float(sm_scale),
                                     out.ctypes.data,
-                                    wts.ctypes.data if wts is not None else 0)
+                                    wts.ctypes.data if wts is not None else 0, tk, tkc, k_tok)
     if rc != 0:
         raise ValueError(f"oracle attention rejected its arguments (rc={rc})")
     return (out, wts) if want_weights else out
+
+
+def topk_tokens(scores: np.ndarray, chunk_ids: np.ndarray, ctx_len: np.ndarray, k_tok: int,
+                counts: np.ndarray | None = None, T: int = 64):
+    """Token selection inside the recalled chunks: scores float32 [B][k*T]
+    (list position j*T + t = token t of chunk_ids[b][j]) -> (tok int32
+    [B][k_tok], ascending usable positions padded with -1; tok_counts int32
+    [B])."""
+    scores = _c(scores, np.float32)
+    chunk_ids = _c(chunk_ids, np.int32)
+    ctx = _c(ctx_len, np.int32)
+    B, k = chunk_ids.shape
+    assert scores.shape == (B, k * T)
+    cn = 0
+    if counts is not None:
+        counts = _c(counts, np.int32)
+        cn = counts.ctypes.data
+    tok = np.empty((B, k_tok), dtype=np.int32)
+    tc = np.empty(B, dtype=np.int32)
+    rc = lib().oracle_topk_tokens(scores.ctypes.data, chunk_ids.ctypes.data, cn, ctx.ctypes.data, B, k, T, k_tok,
+                                  tok.ctypes.data, tc.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle token selection rejected its arguments (rc={rc})")
+    return tok, tc
 
 
 def threshold_chunks(logits: np.ndarray, k_max: int, logit_threshold: int = 0):

@@ -39,6 +39,12 @@
  *     already recalled need fetching): a chunk kept from the previous
  *     selection keeps its slot; the r-th new chunk in ascending id order takes
  *     the r-th lowest slot the previous selection does not hold.
+ *  8. Token selection inside the recalled chunks (summary 2.1 Architecture:
+ *     after the chunk recall, the model's own token-level scores pick a
+ *     fine-grained top-k among the recalled entries only).  The scores are an
+ *     input: the pages do not give the scoring function.  Same order as item
+ *     3 over the usable tokens of the recalled chunks, by list position.
+ *     Item 4 then attends over exactly the listed tokens.
  *
  * Layouts (row-major):
  *   q_idx  int8   [B][nq][d_idx]        K_idx int8 [B][C][d_idx]
@@ -133,6 +139,11 @@ int oracle_topk_f64(const double* keys, int64_t R, int64_t C, int64_t k, int32_t
  *      z  = (q[b][h] . K[token]) * sm_scale
  *      w  = exp(z - max z)
  *      out[b][h] = sum_token w * V[token] / sum_token w
+ *    If `tok` is not NULL only the listed tokens of the chunks are used:
+ *    tok[b][0..tok_counts[b]) (all k_tok when tok_counts is NULL) are list
+ *    positions p = j*T + t, each naming token t of list entry j; a position
+ *    whose entry is unused or whose token is at or past ctx_len[b] is left
+ *    out.  The resident segment, if any, is used in full as above.
  *    If `weights` is not NULL it receives the normalised softmax weight of
  *    every (list entry, token) pair, [B][Hq][k*T + S_max] (segment token t at
  *    k*T + t), 0 for unused tokens.
@@ -140,13 +151,16 @@ int oracle_topk_f64(const double* keys, int64_t R, int64_t C, int64_t k, int32_t
 int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
                          const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
                          const uint16_t* seg_kv, const int32_t* seg_len, int64_t S_max, int64_t B, int64_t Hq,
-                         int64_t Hkv, int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights) {
+                         int64_t Hkv, int64_t d, int64_t k, int64_t T, double sm_scale, double* out, double* weights,
+                         const int32_t* tok, const int32_t* tok_counts, int64_t k_tok) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || k < 1 || T < 1) return -1;
     if (seg_kv && (!seg_len || S_max < 1)) return -1;
+    if (tok && k_tok < 1) return -1;
     const int64_t group = Hq / Hkv;
     const int64_t tile = T * d;              /* one (K|V, head) tile          */
     const int64_t chunk = 2 * Hkv * tile;    /* one chunk, K and V, all heads */
     const int64_t n_slot = k * T + (seg_kv ? S_max : 0);
+    const int64_t n_list = (tok && k_tok > k * T ? k_tok : k * T) + (seg_kv ? S_max : 0);
     int status = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int64_t b = 0; b < B; ++b)
@@ -154,13 +168,30 @@ int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store,
             const int64_t g = h / group;
             const uint16_t* qh = q + (b * Hq + h) * d;
             /* the token list: K and V row of every used token, and its slot in `weights` */
-            const uint16_t** Kr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_slot);
-            const uint16_t** Vr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_slot);
-            int64_t* where = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_slot);
-            double* z = (double*)malloc(sizeof(double) * (size_t)n_slot);
+            const uint16_t** Kr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_list);
+            const uint16_t** Vr = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)n_list);
+            int64_t* where = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_list);
+            double* z = (double*)malloc(sizeof(double) * (size_t)n_list);
             int64_t n = 0;
-            const int64_t kb = counts ? counts[b] : k;
-            for (int64_t j = 0; j < k && j < kb; ++j) {
+            const int64_t kb = counts ? (counts[b] < k ? counts[b] : k) : k;
+            if (tok) {
+                /* the listed tokens: list position p = j*T + t names token t
+                   of list entry j; positions outside the used entries or at
+                   or past the context length are left out */
+                const int64_t tc = tok_counts ? tok_counts[b] : k_tok;
+                for (int64_t u = 0; u < tc && u < k_tok; ++u) {
+                    const int64_t pos = tok[b * k_tok + u];
+                    if (pos < 0 || pos >= kb * T) continue;
+                    const int64_t j = pos / T, t = pos % T;
+                    const int64_t c = chunk_ids[b * k + j];
+                    if (c * T + t >= (int64_t)ctx_len[b]) continue;
+                    const int64_t p = slots ? slots[b * k + j] : c;
+                    Kr[n] = kv + (b * C_store + p) * chunk + (0 * Hkv + g) * tile + t * d;
+                    Vr[n] = kv + (b * C_store + p) * chunk + (1 * Hkv + g) * tile + t * d;
+                    where[n++] = pos;
+                }
+            }
+            for (int64_t j = 0; !tok && j < kb; ++j) {
                 const int64_t c = chunk_ids[b * k + j];
                 const int64_t p = slots ? slots[b * k + j] : c;
                 const uint16_t* K = kv + (b * C_store + p) * chunk + (0 * Hkv + g) * tile;
@@ -205,7 +236,7 @@ int oracle_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store,
                 if (weights) {
                     double* wrow = weights + (b * Hq + h) * n_slot;
                     for (int64_t e = 0; e < n_slot; ++e) wrow[e] = 0.0;
-                    for (int64_t e = 0; e < n; ++e) wrow[where[e]] = z[e] / l;
+                    for (int64_t e = 0; e < n; ++e) wrow[where[e]] += z[e] / l;
                 }
             }
             free(Kr);
@@ -295,4 +326,49 @@ int oracle_threshold_i64(const int64_t* keys, int64_t R, int64_t C, int64_t thr,
         counts[r] = (int32_t)kk;
     }
     return 0;
+}
+
+/* 8. Token selection inside the recalled chunks.  List position p = j*T + t
+ *    (token t of list entry j) is usable iff j < counts[b] (all k entries
+ *    when counts is NULL) and chunk_ids[b][j]*T + t < ctx_len[b].  Among the
+ *    usable positions, p precedes p' when score[p] > score[p'] (compared as
+ *    values: -0 equals +0), or the scores are equal and p < p'.  With
+ *    kt = min(k_tok, number usable), position p is kept iff fewer than kt
+ *    usable positions precede it.  tok[b] receives the kept positions in
+ *    ascending order, then -1 up to k_tok; tok_counts[b] = kt.
+ *    scores float [B][k*T].  Returns 0; -1 on bad sizes or a NaN score. */
+int oracle_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts, const int32_t* ctx_len,
+                       int64_t B, int64_t k, int64_t T, int64_t k_tok, int32_t* tok, int32_t* tok_counts) {
+    if (B < 1 || k < 1 || T < 1 || k_tok < 1) return -1;
+    const int64_t n = k * T;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        const float* row = scores + b * n;
+        const int64_t kb = counts ? (counts[b] < 0 ? 0 : counts[b] < k ? counts[b] : k) : k;
+        unsigned char* usable = (unsigned char*)malloc((size_t)n);
+        int64_t n_use = 0;
+        for (int64_t p = 0; p < n; ++p) {
+            const int64_t j = p / T, t = p % T;
+            usable[p] = j < kb && (int64_t)chunk_ids[b * k + j] * T + t < (int64_t)ctx_len[b];
+            if (usable[p] && isnan(row[p])) {
+#pragma omp atomic write
+                status = -1;
+            }
+            n_use += usable[p];
+        }
+        const int64_t kt = k_tok < n_use ? k_tok : n_use;
+        int64_t n_out = 0;
+        for (int64_t p = 0; p < n; ++p) {
+            if (!usable[p]) continue;
+            int64_t before = 0;
+            for (int64_t p2 = 0; p2 < n; ++p2)
+                if (usable[p2] && (row[p2] > row[p] || (row[p2] == row[p] && p2 < p))) ++before;
+            if (before < kt) tok[b * k_tok + n_out++] = (int32_t)p;
+        }
+        for (int64_t u = n_out; u < k_tok; ++u) tok[b * k_tok + u] = -1;
+        tok_counts[b] = (int32_t)n_out;
+        free(usable);
+    }
+    return status;
 }

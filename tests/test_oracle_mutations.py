@@ -44,7 +44,7 @@ MUTATIONS = [
      ["test_attention_closed_forms", "test_all_chunks_equals_dense_sdpa"]),
     ("slots ignored", "const int64_t p = slots ? slots[b * k + j] : c;\n                const uint16_t* K = kv",
      "const int64_t p = c;\n                const uint16_t* K = kv", ["test_chunk_order_and_slots"]),
-    ("counts ignored", "const int64_t kb = counts ? counts[b] : k;", "const int64_t kb = k;",
+    ("counts ignored", "const int64_t kb = counts ? (counts[b] < k ? counts[b] : k) : k;", "const int64_t kb = k;",
      ["test_attention_counts_truncate_lists", "test_segment_joins_chunks_in_one_softmax"]),
     ("segment V from K", "const uint16_t* V = seg_kv + ((b * 2 + 1) * Hkv + g) * S_max * d;",
      "const uint16_t* V = seg_kv + ((b * 2 + 0) * Hkv + g) * S_max * d;", ["test_segment_joins_chunks_in_one_softmax"]),
@@ -57,6 +57,16 @@ MUTATIONS = [
     ("threshold inclusive", "for (int64_t c = 0; c < C; ++c) above += row[c] > thr;",
      "for (int64_t c = 0; c < C; ++c) above += row[c] >= thr;",
      ["test_threshold_vs_brute_force", "test_threshold_zero_is_sigmoid_half"]),
+    ("token tie to higher position", "if (usable[p2] && (row[p2] > row[p] || (row[p2] == row[p] && p2 < p))) ++before;",
+     "if (usable[p2] && (row[p2] > row[p] || (row[p2] == row[p] && p2 > p))) ++before;",
+     ["test_token_select_vs_brute_force", "test_token_select_special_cases"]),
+    ("token usable ignores context",
+     "usable[p] = j < kb && (int64_t)chunk_ids[b * k + j] * T + t < (int64_t)ctx_len[b];", "usable[p] = j < kb;",
+     ["test_token_select_vs_brute_force", "test_token_select_special_cases"]),
+    ("token list keeps tokens past context", "if (c * T + t >= (int64_t)ctx_len[b]) continue;", "",
+     ["test_token_attention_equals_sdpa_over_listed_tokens"]),
+    ("token list ignores entry count", "if (pos < 0 || pos >= kb * T) continue;", "if (pos < 0 || pos >= k * T) continue;",
+     ["test_token_attention_equals_sdpa_over_listed_tokens"]),
 ]
 
 

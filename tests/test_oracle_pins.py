@@ -490,3 +490,104 @@ def test_segment_joins_chunks_in_one_softmax(oracle_lib, synth_lib):
                                     seg_kv=seg, seg_len=seg_len)
     np.testing.assert_allclose(only[1], np.tile(f32(seg[1, 1, :, 0]).astype(np.float64).repeat(Hq // Hkv, 0)
                                                 .reshape(Hq, d), 1), rtol=0, atol=0)
+
+
+# ------------------------------------------------------------------ token selection inside recalled chunks
+
+def brute_tokens(scores, ids, ctx, k_tok, counts=None, T=64):
+    """Python's sorted() on (-score, position) over the usable positions."""
+    B, n = scores.shape
+    out = np.full((B, k_tok), -1, dtype=np.int32)
+    cnt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        kb = ids.shape[1] if counts is None else min(max(int(counts[b]), 0), ids.shape[1])
+        use = [p for p in range(n) if p // T < kb and int(ids[b, p // T]) * T + p % T < int(ctx[b])]
+        keep = sorted(sorted(use, key=lambda p: (-float(scores[b, p]), p))[:k_tok])
+        out[b, :len(keep)] = keep
+        cnt[b] = len(keep)
+    return out, cnt
+
+
+def _token_scores(synth_lib, B, n, seed):
+    """bf16-rounded normals (many exact ties) with signed zeros and infinities planted."""
+    s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), seed, synth_lib.stream(synth_lib.TAG_MISC, 1400)))
+    s = np.round(s * 4) / 4  # coarser still: long runs of equal scores
+    s[:, 3::17] = 0.0
+    s[:, 5::19] = -0.0
+    s[:, 7::41] = np.inf
+    s[:, 11::43] = -np.inf
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("T,k,k_tok", [(4, 5, 3), (4, 5, 7), (8, 6, 20), (64, 3, 50), (64, 3, 192), (4, 3, 100)])
+def test_token_select_vs_brute_force(oracle_lib, synth_lib, T, k, k_tok):
+    B, C = 4, 12
+    scores = _token_scores(synth_lib, B, k * T, seed=T + k)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 5, synth_lib.stream(synth_lib.TAG_MISC, 1410 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.array([C * T, ids[1, -1] * T + T // 2, ids[2, 1] * T + 1, 0], dtype=np.int32)  # full, partial, short, none
+    counts = np.array([k, k, k - 1, k], dtype=np.int32)
+    for cn in (None, counts):
+        got, gc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=cn, T=T)
+        ref, rc = brute_tokens(scores, ids, ctx, k_tok, counts=cn, T=T)
+        assert np.array_equal(gc, rc) and np.array_equal(got, ref), (T, k, k_tok, cn)
+
+
+def test_token_select_special_cases(oracle_lib):
+    """Equal scores keep the lowest positions; a budget above the usable
+    count keeps every usable token; signed zeros are equal scores."""
+    T, k = 4, 3
+    ids = np.array([[2, 5, 9]], dtype=np.int32)
+    ctx = np.array([9 * T + 2], dtype=np.int32)  # tokens 0, 1 of the last chunk are usable
+    flat = np.zeros((1, k * T), dtype=np.float32)
+    tok, tc = oracle_lib.topk_tokens(flat, ids, ctx, 5, T=T)
+    assert tok.tolist() == [[0, 1, 2, 3, 4]] and tc.tolist() == [5]
+    tok, tc = oracle_lib.topk_tokens(flat, ids, ctx, 40, T=T)
+    assert tc.tolist() == [10] and tok[0, :10].tolist() == list(range(10)) and (tok[0, 10:] == -1).all()
+    z = np.array([[0.0, -0.0, 0.0, -0.0] * 3], dtype=np.float32)
+    tok, _ = oracle_lib.topk_tokens(z, ids, ctx, 3, T=T)
+    assert tok.tolist() == [[0, 1, 2]]
+    ranked = np.arange(k * T, dtype=np.float32)[None]  # later positions score higher
+    tok, tc = oracle_lib.topk_tokens(ranked, ids, ctx, 3, T=T)
+    assert tok.tolist() == [[7, 8, 9]] and tc.tolist() == [3]  # 10, 11 are past the context
+
+
+def test_token_attention_equals_sdpa_over_listed_tokens(oracle_lib, synth_lib):
+    """Attention over a token list is dense SDPA over exactly those tokens;
+    listed positions of unused entries or past the context are dropped."""
+    import torch
+    B, Hq, Hkv, d, C, T, k = 2, 16, 2, 64, 6, 64, 3
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=21, qscale=4.0)
+    ids = np.array([[1, 4, 5], [0, 2, 3]], dtype=np.int32)
+    ctx = np.array([5 * T + 10, C * T], dtype=np.int32)
+    counts = np.array([3, 2], dtype=np.int32)
+    tok = np.array([[130, 5, 64, 140, 63, 129, 200, -1],      # 140 is position 5*64+12 >= ctx: dropped
+                    [3, 70, 127, 128, 190, 0, 1, 2]], dtype=np.int32)  # 128, 190 name unused entry 2
+    tok_counts = np.array([7, 8], dtype=np.int32)
+    out = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d), counts=counts, tok=tok,
+                                   tok_counts=tok_counts)
+    for b in range(B):
+        keep = [int(p) for p in tok[b, :tok_counts[b]]
+                if 0 <= p < counts[b] * T and ids[b, p // T] * T + p % T < ctx[b]]
+        pos = [int(ids[b, p // T]) * T + p % T for p in keep]
+        Kall = f32(kv[b, :, 0]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, pos]
+        Vall = f32(kv[b, :, 1]).transpose(1, 0, 2, 3).reshape(Hkv, C * T, d)[:, pos]
+        Q = torch.from_numpy(f32(q[b]).astype(np.float64)).reshape(1, Hq, 1, d)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            Q, torch.from_numpy(Kall.astype(np.float64))[None], torch.from_numpy(Vall.astype(np.float64))[None],
+            scale=1 / math.sqrt(d), enable_gqa=True)
+        np.testing.assert_allclose(out[b], o.reshape(Hq, d).numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_token_attention_all_tokens_equals_chunk_attention(oracle_lib, synth_lib):
+    """Listing every token of the used entries reduces to chunk attention,
+    output and weights alike; the list order does not matter."""
+    B, Hq, Hkv, d, C, T = 2, 8, 1, 64, 5, 64
+    q, kv = _random_problem(synth_lib, B, Hq, Hkv, d, C, seed=22, qscale=2.0)
+    ids = np.array([[0, 2, 4], [1, 3, 4]], dtype=np.int32)
+    ctx = np.array([C * T - 30, C * T], dtype=np.int32)
+    ref, wref = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125, want_weights=True)
+    perm = np.stack([np.random.default_rng(b).permutation(3 * T) for b in range(B)]).astype(np.int32)
+    got, wgot = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125, want_weights=True, tok=perm)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(wgot, wref, rtol=1e-12, atol=1e-15)
