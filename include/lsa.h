@@ -131,6 +131,34 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
                                 int32_t* chunk_ids, int32_t* counts, hipStream_t stream);
 
 /*
+ * lsa_topk_tokens -- the token-level second stage inside the recalled chunks.
+ *
+ * Defined by: after the chunk recall, the model's native token-level scoring
+ * picks a fine-grained top-k among the recalled entries only, not over the
+ * whole context (paperlayer.ai summary, 2.1 Architecture).  The pages give
+ * no formula for those token scores, so they are an input here.  List
+ * position p = j*64 + t names token t of list entry j (chunk
+ * chunk_ids[b][j]); it competes iff j < counts[b] (all k when counts is
+ * NULL) and chunk_ids[b][j]*64 + t < ctx_len[b].  Among the competing
+ * positions the first min(k_tok, competing) of the order "score descending,
+ * then position ascending" are kept (scores compare as values: -0 equals
+ * +0), written in ascending position order into tok[b][0..tok_counts[b]),
+ * the rest of the row set to -1.  The set is unique: bit-exact.
+ *
+ *  scores      device fp32 [B][k*64], no NaN among competing positions
+ *  chunk_ids   device int32 [B][k]
+ *  counts      device int32 [B] entries in use, or NULL (all k)
+ *  ctx_len     device int32 [B]
+ *  B >= 1, 1 <= k <= 1024 (k*64 <= 65536), k_tok >= 1
+ *  tok         device int32 [B][k_tok] output: list positions
+ *  tok_counts  device int32 [B] output: positions kept per request
+ * All pointers need 4-byte alignment.
+ */
+lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts,
+                           const int32_t* ctx_len, int32_t B, int32_t k, int32_t k_tok, int32_t* tok,
+                           int32_t* tok_counts, hipStream_t stream);
+
+/*
  * Number of bytes of workspace lsa_gather_attend needs for these sizes and
  * this split count (n_split = 0: the library's own choice).  Returns 0 when
  * no workspace is needed, (size_t)-1 when the arguments are invalid.
@@ -202,6 +230,38 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
                              int32_t Hq, int32_t Hkv,
                              int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
                              int32_t n_split, float* out, hipStream_t stream);
+
+/*
+ * lsa_gather_attend_tokens -- lsa_gather_attend over a listed subset of the
+ * chunk tokens (the output of lsa_topk_tokens).
+ *
+ * Defined by: the same attention as lsa_gather_attend, with the chunk tokens
+ * restricted to those the token-level top-k kept (paperlayer.ai summary, 2.1
+ * Architecture: the fine-grained entries picked from the recalled subset,
+ * combined with the sliding-window KV).  The chunk tokens are
+ *     { chunk_ids[b][j]*64 + t : p = j*64 + t in tok[b][0..tok_counts[b]),
+ *       j < counts[b], that position < ctx_len[b] }
+ * each listed position counted once per listing (positions outside the used
+ * entries or past ctx_len are left out); the resident segment, if given, is
+ * attended in full as in lsa_gather_attend.  Every other argument has the
+ * meaning it has there.
+ *
+ *  tok         device int32 [B][k_tok] list positions (ascending is the
+ *              efficient order; any order gives the same result up to
+ *              rounding)
+ *  tok_counts  device int32 [B] positions in use, or NULL (all k_tok)
+ *  k_tok >= 1
+ *  kv          the store of lsa_gather_attend; C_store * 2*Hkv*64 < 2^31
+ *  workspace   lsa_gather_attend_workspace_size(B, Hq, Hkv, d, ceil(k_tok/64),
+ *              n_split) bytes; n_split splits the token list (0 = library
+ *              choice for ceil(k_tok/64) blocks of 64 listed tokens)
+ */
+lsa_status lsa_gather_attend_tokens(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                                    const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                                    const int32_t* tok, const int32_t* tok_counts, int32_t k_tok,
+                                    const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t d, int32_t k, float sm_scale, void* workspace,
+                                    size_t workspace_bytes, int32_t n_split, float* out, hipStream_t stream);
 
 /*
  * lsa_fetch_chunks -- host-tier fetch of the selected chunks into HBM.

@@ -10,11 +10,14 @@ has not been built: there is no CPU fallback.
 """
 from ._binding import (CHUNK_TOKENS, EXPORTS, LIB_PATH, LsaError, alloc_workspace, load_library,
                        lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend, lsa_gather_attend_default_splits,
+                       lsa_gather_attend_tokens,
                        lsa_gather_attend_workspace_size, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
-                       lsa_topk_chunks)
+                       lsa_topk_chunks, lsa_topk_tokens)
 
 load_library()
 
 __all__ = ["CHUNK_TOKENS", "EXPORTS", "LIB_PATH", "LsaError", "alloc_workspace", "load_library",
            "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_gather_attend", "lsa_gather_attend_default_splits",
-           "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks"]
+           "lsa_gather_attend_tokens",
+           "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks",
+           "lsa_topk_tokens"]

@@ -24,8 +24,9 @@ CHUNK_TOKENS = 64
 
 # Every symbol include/lsa.h declares.
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
-           "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits", "lsa_gather_attend",
-           "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_pool_assign")
+           "lsa_topk_tokens", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
+           "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
+           "lsa_pool_assign")
 
 
 class LsaError(RuntimeError):
@@ -61,6 +62,11 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz,
                                     i32, vp, vp]
     L.lsa_gather_attend.restype = ctypes.c_int
+    L.lsa_topk_tokens.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.lsa_topk_tokens.restype = ctypes.c_int
+    L.lsa_gather_attend_tokens.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                           i32, f32, vp, sz, i32, vp, vp]
+    L.lsa_gather_attend_tokens.restype = ctypes.c_int
     L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
     L.lsa_fetch_chunks.restype = ctypes.c_int
     L.lsa_fetch_chunks_pull.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
@@ -143,6 +149,28 @@ def lsa_threshold_chunks(logits: torch.Tensor, k_max: int, logit_threshold: int 
     return chunk_ids, counts
 
 
+def lsa_topk_tokens(scores: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor, k_tok: int,
+                    counts: torch.Tensor | None = None, tok=None, tok_counts=None, stream=None):
+    """scores fp32 [B][k*64] over the list positions of the recalled chunks
+    chunk_ids int32 [B][k] -> (tok int32 [B][k_tok] ascending positions padded
+    with -1, tok_counts int32 [B])."""
+    _need(scores, torch.float32, "scores", 2)
+    _need(chunk_ids, torch.int32, "chunk_ids", 2)
+    _need(ctx_len, torch.int32, "ctx_len", 1)
+    B, k = chunk_ids.shape
+    if tuple(scores.shape) != (B, k * CHUNK_TOKENS):
+        raise ValueError(f"scores shape {tuple(scores.shape)} is not [B][k*64] = [{B}][{k * CHUNK_TOKENS}]")
+    if counts is not None:
+        _need(counts, torch.int32, "counts", 1)
+    if tok is None:
+        tok = torch.empty((B, k_tok), dtype=torch.int32, device=scores.device)
+    if tok_counts is None:
+        tok_counts = torch.empty(B, dtype=torch.int32, device=scores.device)
+    _check(load_library().lsa_topk_tokens(_ptr(scores), _ptr(chunk_ids), _ptr(counts), _ptr(ctx_len), B, k, k_tok,
+                                          _ptr(tok), _ptr(tok_counts), _stream(stream)))
+    return tok, tok_counts
+
+
 def lsa_gather_attend_workspace_size(B: int, Hq: int, Hkv: int, d: int, k: int, n_split: int = 0) -> int:
     n = load_library().lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
     if n == ctypes.c_size_t(-1).value:
@@ -166,11 +194,14 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
                       sm_scale: float | None = None, slots: torch.Tensor | None = None, workspace=None,
                       n_split: int = 0, out=None, counts: torch.Tensor | None = None,
                       seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None,
-                      stream=None) -> torch.Tensor:
+                      stream=None, tok: torch.Tensor | None = None,
+                      tok_counts: torch.Tensor | None = None) -> torch.Tensor:
     """q bf16 [B][Hq][d]; kv bf16 [B][C_store][2][Hkv][64][d]; chunk_ids int32 [B][k];
     ctx_len int32 [B]; slots int32 [B][k] or None; counts int32 [B] or None;
     seg_kv bf16 [B][2][Hkv][S_max][d] (resident window) with seg_len int32 [B],
-    or None.  Returns fp32 [B][Hq][d]."""
+    or None.  With tok int32 [B][k_tok] (list positions, as lsa_topk_tokens
+    writes them) and tok_counts int32 [B] or None, the call is
+    lsa_gather_attend_tokens.  Returns fp32 [B][Hq][d]."""
     _need(q, torch.bfloat16, "q", 3)
     _need(kv, torch.bfloat16, "kv", 6)
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
@@ -197,19 +228,43 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
         if seg_kv.shape[0] != B or seg_kv.shape[1] != 2 or seg_kv.shape[2] != Hkv or seg_kv.shape[4] != d:
             raise ValueError(f"seg_kv shape {tuple(seg_kv.shape)} does not match [B][2][Hkv][S_max][d]")
         S_max = seg_kv.shape[3]
+    k_tok = 0
+    if tok is not None:
+        _need(tok, torch.int32, "tok", 2)
+        if tok.shape[0] != B:
+            raise ValueError("tok batch size mismatch")
+        k_tok = tok.shape[1]
+        if tok_counts is not None:
+            _need(tok_counts, torch.int32, "tok_counts", 1)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = alloc_workspace(B, Hq, Hkv, d, k, n_split, device=q.device)
+        entries = k if tok is None else (k_tok + CHUNK_TOKENS - 1) // CHUNK_TOKENS
+        workspace = alloc_workspace(B, Hq, Hkv, d, entries, n_split, device=q.device)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if tok is not None:
+        _check(load_library().lsa_gather_attend_tokens(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
+                                                       _ptr(counts), _ptr(ctx_len), _ptr(tok), _ptr(tok_counts),
+                                                       k_tok, _ptr(seg_kv), _ptr(seg_len), S_max, B, Hq, Hkv, d, k,
+                                                       sm_scale, _ptr(workspace), ws_bytes, n_split, _ptr(out),
+                                                       _stream(stream)))
+        return out
     _check(load_library().lsa_gather_attend(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
                                             _ptr(counts), _ptr(ctx_len), _ptr(seg_kv), _ptr(seg_len), S_max, B, Hq,
                                             Hkv, d, k, sm_scale,
                                             _ptr(workspace), ws_bytes,
                                             n_split, _ptr(out), _stream(stream)))
     return out
+
+
+def lsa_gather_attend_tokens(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor,
+                             tok: torch.Tensor, tok_counts: torch.Tensor | None = None, **kw) -> torch.Tensor:
+    """Attention over the listed tokens of the recalled chunks (tok int32
+    [B][k_tok] list positions, tok_counts int32 [B] or None); the other
+    arguments as for lsa_gather_attend.  Returns fp32 [B][Hq][d]."""
+    return lsa_gather_attend(q, kv, chunk_ids, ctx_len, tok=tok, tok_counts=tok_counts, **kw)
 
 
 def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_kv: torch.Tensor,

@@ -29,6 +29,12 @@
 //    16 significant bits of the softmax weights; all accumulation is fp32.
 //  * Online softmax per wave in the log2 domain; the 4 waves merge through
 //    LDS at the end; splits merge in a second small kernel.
+//  * Token-list mode (TOK): after the chunk recall, a token-level top-k
+//    keeps only some tokens of the recalled chunks (paperlayer.ai summary,
+//    2.1 Architecture).  The workgroup's list is then blocks of 64 listed
+//    tokens; each token's K/V row index is staged in LDS (-1: masked) and
+//    every lane loads its own rows, 64 contiguous bytes per lane and row
+//    instead of whole 16 KB tiles.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -47,6 +53,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kSliceTokens = 16;
 constexpr int kListCache = 512;  // list entries staged in LDS at a time
+constexpr int kTokCache = 32;    // token blocks (of 64 rows) staged in LDS at a time
 
 template <int D>
 struct VRow;  // one lane's share of one V row: D/16 bf16 values
@@ -98,6 +105,19 @@ __device__ inline void load_slice(Slice<D>& s, const uint16_t* ktile, const uint
     }
 }
 
+// Same register layout as load_slice, from per-row addresses: krow is the K
+// row of this lane's A row, vrow[r] the V row of its token 4r + lane/16.
+template <int D>
+__device__ inline void load_slice_rows(Slice<D>& s, const uint16_t* krow, const uint16_t* const* vrow, int lane) {
+    const int n = lane & 15, i = lane >> 4;
+    const uint16_t* kp = krow + 8 * i;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) s.k[st] = *reinterpret_cast<const uint4*>(kp + 32 * st);
+    constexpr int DPL = D / 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s.v[r] = load_vrow<D>(vrow[r] + DPL * n);
+}
+
 __device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 __device__ inline float bf16_value(short b) { return (float)__builtin_bit_cast(__bf16, b); }
 
@@ -108,12 +128,13 @@ __device__ inline void vrow_mask(VRow<128>& r, bool ok) { r.v = select4(ok, r.v)
 __device__ inline void vrow_mask(VRow<64>& r, bool ok) { r.v = ok ? r.v : make_uint2(0, 0); }
 
 // Online-softmax update of one wave with one 16-token slice; tokens at or
-// past `nvalid` (chunk-relative) are masked.  Straight-line code except for
+// past `nvalid` (chunk-relative), and token 4r + lane/16 when bit r of
+// `vmask` is clear, are masked.  Straight-line code except for
 // the rescale of O, which only runs when some head's running max grows and
 // issues no memory operation, so the loads in flight are never waited on
 // early.
 template <int D>
-__device__ inline void process_slice(Slice<D>& sl, int nvalid, int first_tok, int i, const bf16x8* qb,
+__device__ inline void process_slice(Slice<D>& sl, int nvalid, uint32_t vmask, int first_tok, int i, const bf16x8* qb,
                                      float scale_log2, float& m_run, float& l_run, f32x4* oacc) {
     constexpr int KS = D / 32;
     constexpr int DPL = D / 16;
@@ -127,7 +148,7 @@ __device__ inline void process_slice(Slice<D>& sl, int nvalid, int first_tok, in
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const bool ok = first_tok + 4 * r + i < nvalid;
+        const bool ok = first_tok + 4 * r + i < nvalid && ((vmask >> r) & 1u);
         sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
         vrow_mask(sl.v[r], ok);
     }
@@ -185,7 +206,7 @@ __device__ inline void merge_waves(const float (*sm_m)[16], const float (*sm_l)[
     }
 }
 
-template <int D, int NBUF>
+template <int D, int NBUF, bool TOK>
 __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     constexpr int KS = D / 32;   // QK MFMA steps over d
     constexpr int DPL = D / 16;  // PV MFMAs (d values per lane per V row)
@@ -212,7 +233,17 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
         const int sl = a.seg_len[b];
         seg_len = sl < 0 ? 0 : sl > a.S_max ? a.S_max : sl;
     }
-    const int64_t total = kb + (seg_len + kChunkTokens - 1) / kChunkTokens;
+    // list entries before the segment: chunks, or blocks of 64 listed tokens
+    int64_t n_main = kb, n_tok = 0;
+    if constexpr (TOK) {
+        n_tok = a.k_tok;
+        if (a.tok_counts) {
+            const int64_t tc = a.tok_counts[b];
+            n_tok = tc < 0 ? 0 : tc > a.k_tok ? a.k_tok : tc;
+        }
+        n_main = (n_tok + kChunkTokens - 1) / kChunkTokens;
+    }
+    const int64_t total = n_main + (seg_len + kChunkTokens - 1) / kChunkTokens;
     const int64_t j0 = ((int64_t)s * total) / a.n_split;
     const int64_t j1 = ((int64_t)(s + 1) * total) / a.n_split;
     const int ctx = a.ctx[b];
@@ -248,8 +279,14 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     // formed from the kernel's own buffer arguments stay in the global
     // address space, whose loads only count against vmcnt.
     constexpr int kSegBit = 1 << 16;
-    __shared__ int64_t sm_off[kListCache];
-    __shared__ int sm_nv[kListCache];
+    constexpr int kCache = TOK ? kTokCache : kListCache;
+    __shared__ int64_t sm_off[TOK ? 1 : kListCache];
+    __shared__ int sm_nv[kCache];
+    // TOK: row index of every staged token, in D-element rows from the
+    // K base of its source (-1: masked)
+    __shared__ int sm_row[TOK ? kTokCache * kChunkTokens : 1];
+    const int32_t* tok_b = TOK ? a.tok + (int64_t)b * a.k_tok : nullptr;
+    const int rows_per_chunk = 2 * a.Hkv * kChunkTokens;
     const int32_t* pos_src = a.slots ? a.slots + (int64_t)b * a.k : ids;
     const uint16_t* seg_b =
         a.seg_kv ? a.seg_kv + ((int64_t)b * 2 * a.Hkv + g) * (int64_t)a.S_max * D : kv_b;  // kv_b: never used
@@ -259,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     // buf[e % NBUF]; NBUF - 1 entries are in flight while one is processed.
     Slice<D> buf[NBUF];
     int nv[NBUF];
+    uint32_t vm[NBUF];
     // Loads are counted in issue order (vmcnt), so the groups of loads are
     // kept in program order: a buffer's loads must be older than those of
     // every buffer issued after it for the waits to stay partial.
@@ -266,16 +304,60 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
         const int f = sm_nv[e];
         const bool in_seg = (f & kSegBit) != 0;
         nv[bi] = f & (kSegBit - 1);
-        const uint16_t* kt = (in_seg ? seg_b : kv_b) + sm_off[e];
-        const uint16_t* vt = kt + (in_seg ? seg_v_off : v_off);
-        __builtin_amdgcn_sched_barrier(0);
-        load_slice<D>(buf[bi], kt, vt, wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TOK) {
+            const uint16_t* bp = in_seg ? seg_b : kv_b;
+            const int64_t vo = in_seg ? seg_v_off : v_off;
+            const int* rows = sm_row + e * kChunkTokens + wave * kSliceTokens;
+            const int rk = rows[4 * (n & 3) + (n >> 2)];
+            const uint16_t* vrow[4];
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rv = rows[4 * r + i];
+                m |= (uint32_t)(rv >= 0) << r;
+                vrow[r] = bp + vo + (int64_t)(rv < 0 ? 0 : rv) * D;  // masked rows read row 0, never used
+            }
+            vm[bi] = m;
+            const uint16_t* krow = bp + (int64_t)(rk < 0 ? 0 : rk) * D;
+            __builtin_amdgcn_sched_barrier(0);
+            load_slice_rows<D>(buf[bi], krow, vrow, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            vm[bi] = 0xFu;
+            const uint16_t* kt = (in_seg ? seg_b : kv_b) + sm_off[e];
+            const uint16_t* vt = kt + (in_seg ? seg_v_off : v_off);
+            __builtin_amdgcn_sched_barrier(0);
+            load_slice<D>(buf[bi], kt, vt, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    for (int64_t seg = j0; seg < j1; seg += kListCache) {
-        const int segn = (int)(j1 - seg < kListCache ? j1 - seg : kListCache);
+    for (int64_t seg = j0; seg < j1; seg += kCache) {
+        const int segn = (int)(j1 - seg < kCache ? j1 - seg : kCache);
         __syncthreads();  // the previous segment's entries are no longer read
-        for (int e = threadIdx.x; e < segn; e += kThreads) {
+        if constexpr (TOK) {
+            for (int x = threadIdx.x; x < segn * kChunkTokens; x += kThreads) {
+                const int e = x / kChunkTokens, t = x % kChunkTokens;
+                const int64_t jb = seg + e;
+                int row = -1;
+                if (jb < n_main) {
+                    const int64_t u = jb * kChunkTokens + t;
+                    if (u < n_tok) {
+                        const int64_t p = tok_b[u];
+                        if (p >= 0 && p < kb * kChunkTokens) {
+                            const int64_t j = p / kChunkTokens, tt = p % kChunkTokens;
+                            if ((int64_t)ids[j] * kChunkTokens + tt < ctx)
+                                row = (int)((int64_t)pos_src[j] * rows_per_chunk + tt);
+                        }
+                    }
+                } else {
+                    const int64_t sidx = (jb - n_main) * kChunkTokens + t;
+                    if (sidx < seg_len) row = (int)sidx;
+                }
+                sm_row[x] = row;
+                if (t == 0) sm_nv[e] = kChunkTokens | (jb < n_main ? 0 : kSegBit);
+            }
+        }
+        for (int e = threadIdx.x; !TOK && e < segn; e += kThreads) {
             const int64_t j = seg + e;
             int64_t v;
             int flag = 0;
@@ -299,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
         auto step = [&](int e, int u) {
             const int ep = e + NBUF - 1;
             issue(ep < segn ? ep : segn - 1, (u + NBUF - 1) % NBUF);
-            process_slice<D>(buf[u], nv[u], first_tok, i, qb, a.scale_log2, m_run, l_run, oacc);
+            process_slice<D>(buf[u], nv[u], vm[u], first_tok, i, qb, a.scale_log2, m_run, l_run, oacc);
         };
 #pragma unroll
         for (int u = 0; u < NBUF - 1; ++u) issue(u < segn ? u : segn - 1, u);
@@ -445,13 +527,21 @@ void attend_workspace_carve(AttendArgs& a, void* workspace) {
     a.part_ml = reinterpret_cast<float*>(p);
 }
 
+template <int D, bool TOK>
+void launch_split_mode(const AttendArgs& a, dim3 grid, hipStream_t stream) {
+    switch (a.depth) {
+        case 2: hipLaunchKernelGGL((attend_split_kernel<D, 2, TOK>), grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((attend_split_kernel<D, 4, TOK>), grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((attend_split_kernel<D, 3, TOK>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+}
+
 template <int D>
 void launch_split(const AttendArgs& a, dim3 grid, hipStream_t stream) {
-    switch (a.depth) {
-        case 2: hipLaunchKernelGGL((attend_split_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((attend_split_kernel<D, 4>), grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL((attend_split_kernel<D, 3>), grid, dim3(kThreads), 0, stream, a); break;
-    }
+    if (a.tok)
+        launch_split_mode<D, true>(a, grid, stream);
+    else
+        launch_split_mode<D, false>(a, grid, stream);
 }
 
 hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream) {

@@ -117,6 +117,26 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k) {
     return lsa::attend_default_splits(B, Hkv, k);
 }
 
+lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts,
+                           const int32_t* ctx_len, int32_t B, int32_t k, int32_t k_tok, int32_t* tok,
+                           int32_t* tok_counts, hipStream_t stream) {
+    if (!scores || !chunk_ids || !ctx_len || !tok || !tok_counts)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "scores, chunk_ids, ctx_len, tok and tok_counts are required");
+    if (B < 1 || k < 1 || k_tok < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B=%d k=%d k_tok=%d must all be >= 1", B, k, k_tok);
+    if ((int64_t)k * lsa::kChunkTokens > lsa::kTopkMaxC)
+        return fail(LSA_ERR_UNSUPPORTED, "k=%d: at most %d list positions (k <= %d)", k, lsa::kTopkMaxC,
+                    lsa::kTopkMaxC / lsa::kChunkTokens);
+    if ((int64_t)B * k * lsa::kChunkTokens >= ((int64_t)1 << 31) || (int64_t)B * k_tok >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B*k*64 and B*k_tok must be < 2^31");
+    if (!aligned(scores, 4) || !aligned(chunk_ids, 4) || !aligned(ctx_len, 4) || !aligned(tok, 4) ||
+        !aligned(tok_counts, 4) || (counts && !aligned(counts, 4)))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "all pointers need 4-byte alignment");
+    hipError_t e = lsa::launch_topk_tokens(scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, stream);
+    if (e != hipSuccess) return hip_fail(e, "token top-k launch");
+    return ok();
+}
+
 size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k, int32_t n_split) {
     if (check_attend_shape(B, Hq, Hkv, d, k) != LSA_OK || n_split < 0) return (size_t)-1;
     if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
@@ -124,12 +144,12 @@ size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
     return lsa::attend_workspace_bytes(B, Hkv, Hq / Hkv, d, n_split);
 }
 
-lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
-                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
-                             const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
-                             int32_t Hq, int32_t Hkv,
-                             int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
-                             int32_t n_split, float* out, hipStream_t stream) {
+static lsa_status gather_attend_impl(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                                     const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                                     const int32_t* tok, const int32_t* tok_counts, int32_t k_tok,
+                                     const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
+                                     int32_t Hq, int32_t Hkv, int32_t d, int32_t k, float sm_scale, void* workspace,
+                                     size_t workspace_bytes, int32_t n_split, float* out, hipStream_t stream) {
     if (!q || !kv || !chunk_ids || !ctx_len || !out)
         return fail(LSA_ERR_INVALID_ARGUMENT, "q, kv, chunk_ids, ctx_len and out are required");
     lsa_status st = check_attend_shape(B, Hq, Hkv, d, k);
@@ -142,8 +162,20 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
                     "a segment needs seg_len, S_max a positive multiple of 64 (S_max=%d) and 16-byte alignment", S_max);
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
         return fail(LSA_ERR_INVALID_ARGUMENT, "q, kv and out need 16-byte alignment");
-    if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
-    if (n_split > k) n_split = k;
+    // list entries split across workgroups: chunks, or blocks of 64 listed tokens
+    int32_t entries = k;
+    if (tok) {
+        if (k_tok < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "k_tok=%d must be >= 1", k_tok);
+        if ((int64_t)B * k_tok >= ((int64_t)1 << 31)) return fail(LSA_ERR_INVALID_ARGUMENT, "B*k_tok must be < 2^31");
+        if (C_store * 2 * Hkv * lsa::kChunkTokens >= ((int64_t)1 << 31))
+            return fail(LSA_ERR_UNSUPPORTED, "token lists need C_store*2*Hkv*64 < 2^31 (C_store=%lld)",
+                        (long long)C_store);
+        if (!aligned(tok, 4) || (tok_counts && !aligned(tok_counts, 4)))
+            return fail(LSA_ERR_INVALID_ARGUMENT, "tok and tok_counts need 4-byte alignment");
+        entries = (k_tok + lsa::kChunkTokens - 1) / lsa::kChunkTokens;
+    }
+    if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, entries);
+    if (n_split > entries) n_split = entries;
     const int G = Hq / Hkv;
     const size_t need = lsa::attend_workspace_bytes(B, Hkv, G, d, n_split);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -162,6 +194,9 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     a.seg_kv = seg_kv;
     a.seg_len = seg_kv ? seg_len : nullptr;
     a.S_max = seg_kv ? S_max : 0;
+    a.tok = tok;
+    a.tok_counts = tok ? tok_counts : nullptr;
+    a.k_tok = tok ? k_tok : 0;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -178,6 +213,28 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
     hipError_t e = lsa::launch_gather_attend(a, stream);
     if (e != hipSuccess) return hip_fail(e, "gather-attend launch");
     return ok();
+}
+
+lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                             const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                             const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
+                             int32_t Hq, int32_t Hkv,
+                             int32_t d, int32_t k, float sm_scale, void* workspace, size_t workspace_bytes,
+                             int32_t n_split, float* out, hipStream_t stream) {
+    return gather_attend_impl(q, kv, C_store, chunk_ids, slots, counts, ctx_len, nullptr, nullptr, 0, seg_kv, seg_len,
+                              S_max, B, Hq, Hkv, d, k, sm_scale, workspace, workspace_bytes, n_split, out, stream);
+}
+
+lsa_status lsa_gather_attend_tokens(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
+                                    const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,
+                                    const int32_t* tok, const int32_t* tok_counts, int32_t k_tok,
+                                    const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t d, int32_t k, float sm_scale, void* workspace,
+                                    size_t workspace_bytes, int32_t n_split, float* out, hipStream_t stream) {
+    if (!tok) return fail(LSA_ERR_INVALID_ARGUMENT, "tok is required");
+    return gather_attend_impl(q, kv, C_store, chunk_ids, slots, counts, ctx_len, tok, tok_counts, k_tok, seg_kv,
+                              seg_len, S_max, B, Hq, Hkv, d, k, sm_scale, workspace, workspace_bytes, n_split, out,
+                              stream);
 }
 
 lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,

@@ -18,6 +18,11 @@ constexpr int kTopkMaxC = 65536;
 // counts == nullptr: top-k; else keep logits > thr, at most k, counts[r] = kept
 hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
                        hipStream_t stream);
+// token stage: top k_tok of the usable list positions of each row's recalled
+// chunks by float score; ascending, -1 padded, tok_counts[r] = kept
+hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, const int32_t* list_counts,
+                              const int32_t* ctx, int R, int n_list, int k_tok, int32_t* tok, int32_t* tok_counts,
+                              hipStream_t stream);
 
 // ---- gathered GQA decode attention ----
 struct AttendArgs {
@@ -31,6 +36,9 @@ struct AttendArgs {
     const uint16_t* seg_kv; // [B][2][Hkv][S_max][d] resident segment, or nullptr
     const int32_t* seg_len; // [B] tokens in the segment
     int S_max;
+    const int32_t* tok;        // [B][k_tok] list positions j*64 + t to attend, or nullptr (every token)
+    const int32_t* tok_counts; // [B] listed positions in use, or nullptr (all k_tok)
+    int k_tok;
     int B, Hq, Hkv, G, d, k, n_split;
     int depth;              // chunks in flight per wave + 1 (register ring size)
     float scale_log2;       // sm_scale * log2(e)

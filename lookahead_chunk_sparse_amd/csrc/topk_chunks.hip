@@ -4,19 +4,26 @@
 // Introduction and 2.1 Architecture: only the chunks the indexer ranks
 // highest are kept; ties go to the lower chunk index).
 //
-// One 1024-thread workgroup per row; thread t keeps logits [t*KPT, (t+1)*KPT)
-// in registers as order-preserving unsigned keys (logit XOR 0x80000000),
+// One 1024-thread workgroup per row; wave w keeps positions
+// [64*KPT*w, 64*KPT*(w+1)) in registers, lane l every 64th of them from l
+// (coalesced loads), as order-preserving unsigned keys (logit XOR 0x80000000),
 // offset by the row's smallest key so that only the bits spanning the row's
 // range remain (logits of both signs would otherwise differ in every bit).
 //  1. Radix select, 8 bits per pass from the top of the range: the keys of
 //     the current bucket are counted per digit into an LDS histogram
-//     (ds_add), then one wave finds, by a suffix scan over the 256 bins, the
-//     digit that holds the k-th largest key.  The result is that key v* and
+//     (ds_add, 16 copies against same-word conflicts), then one wave finds,
+//     by a suffix scan over the 256 bins, the digit that holds the k-th
+//     largest key.  The result is that key v* and
 //     `need`, the number of keys equal to v* that belong to the selection.
 //  2. Ordered compaction: keys > v* are taken; keys == v* are taken while
-//     their rank among equal keys, in index order, is below `need`.  Two
-//     block-wide exclusive scans (equal-key ranks, output offsets) in thread
-//     order, which is index order, make the output ascending.
+//     their rank among equal keys, in index order, is below `need`.  Ranks
+//     in index order come from ballots within a wave (slot by slot) and from
+//     scans of the per-wave totals across waves, so the output is ascending.
+//
+// The same select serves the token-level stage: after the chunk recall the
+// model's own token scores pick a fine-grained top-k among the recalled
+// tokens only (same summary, 2.1 Architecture); there the keys are float
+// scores over the list positions of the recalled chunks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,44 +34,6 @@ namespace {
 
 constexpr int kThreads = kTopkThreads;
 constexpr int kWaves = kThreads / 64;
-
-__device__ inline int wave_sum(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-
-__device__ inline int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_up(v, off);
-        if (lane >= off) v += u;
-    }
-    return v;
-}
-
-// Block-wide sum; `sm` holds kWaves ints.  Two barriers so sm can be reused.
-__device__ inline int block_sum(int v, int* sm, int lane, int wave) {
-    v = wave_sum(v);
-    if (lane == 0) sm[wave] = v;
-    __syncthreads();
-    int t = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += sm[w];
-    __syncthreads();
-    return t;
-}
-
-// Block-wide exclusive scan in thread order.
-__device__ inline int block_excl_scan(int v, int* sm, int lane, int wave) {
-    const int incl = wave_incl_scan(v, lane);
-    if (lane == 63) sm[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += sm[w];
-    __syncthreads();
-    return before + incl - v;
-}
 
 __device__ inline uint32_t wave_min(uint32_t v) {
 #pragma unroll
@@ -79,67 +48,143 @@ __device__ inline uint32_t wave_max(uint32_t v) {
 
 constexpr int kDigitBits = 8;
 constexpr int kBins = 1 << kDigitBits;
+// Copies of the histogram: lane l counts into copy l % kCopies, so lanes
+// whose keys share a bin hit kCopies different words (scores crowd into a
+// few bins, and same-word LDS atomics serialise).
+constexpr int kCopies = 16;
 
-// Threshold mode (counts != nullptr): the row keeps the chunks whose logit
-// exceeds `thr`, at most k of them (the first k in the same order when more
-// pass); the output row is padded with -1 and counts[row] = chunks kept.
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restrict__ logits, int C, int k,
-                                                        int32_t* __restrict__ out, int32_t thr,
-                                                        int32_t* __restrict__ counts) {
+// Order-preserving unsigned key of a float score: equal values give equal
+// keys (-0 is taken as +0), larger values larger keys.  NaN is not a score.
+__device__ inline uint32_t score_key(float x) {
+    const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One row per workgroup.  Three modes:
+//  * budget (counts == nullptr, !TOK): the first k of C int32 logits;
+//  * threshold (counts != nullptr, !TOK): the logits above thr, at most k;
+//    the row is padded with -1 and counts[row] = chunks kept;
+//  * tokens (TOK): float scores of the C = 64 * n_list list positions of a
+//    row's recalled chunks; only usable positions compete (entry j < the
+//    row's list count, context position ids[j]*64 + t < ctx); at most k are
+//    kept, -1 padding, counts[row] = kept.
+struct TopkArgs {
+    const int32_t* logits;      // [R][C] (budget / threshold)
+    const float* scores;        // [R][C] (tokens)
+    const int32_t* list_ids;    // [R][n_list] recalled chunk ids (tokens)
+    const int32_t* list_counts; // [R] entries in use, may be null (tokens)
+    const int32_t* ctx;         // [R] context length (tokens)
+    int n_list;
+    int C, k;
+    int32_t thr;
+    int32_t* out;     // [R][k]
+    int32_t* counts;  // [R] or null (budget)
+};
+
+template <int KPT, bool TOK>
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int sm_i[kWaves];
+    __shared__ int sm_j[kWaves];
+    __shared__ int sm_avail[kWaves];
     __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
-    __shared__ int sm_hist[kBins];
+    __shared__ __align__(16) int sm_hist[kBins * kCopies];  // [bin][copy]
+    __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[2];  // digit chosen by the pass, keys still needed
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t* row = logits + (int64_t)blockIdx.x * C;
-    int32_t* dst = out + (int64_t)blockIdx.x * k;
-    const int base = tid * KPT;
+    const int C = a.C, k = a.k;
+    int32_t* dst = a.out + (int64_t)blockIdx.x * k;
+    // wave w owns positions [w*64*KPT, (w+1)*64*KPT); slot e of lane l is
+    // position w*64*KPT + 64*e + l, so every load instruction reads 64
+    // consecutive positions
+    const int wbase = wave * 64 * KPT;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < lane
 
+    // A position competes iff ok(e): in token mode key 0 marks the others (no
+    // float score maps to 0), otherwise the position must lie in the row.
     uint32_t key[KPT];
+    auto ok = [&](int e) { return TOK ? key[e] != 0u : wbase + 64 * e + lane < C; };
+    // Loads are unconditional, from clamped in-bounds indices, and all issued
+    // before any is used: loads under a branch each wait for their data.
+    if constexpr (TOK) {
+        // slot e of wave w is exactly list entry j = w*KPT + e (64 tokens)
+        const float* row = a.scores + (int64_t)blockIdx.x * C;
+        const int32_t* ids = a.list_ids + (int64_t)blockIdx.x * a.n_list;
+        int kb = a.n_list;
+        if (a.list_counts) {
+            const int cnt = a.list_counts[blockIdx.x];
+            kb = cnt < 0 ? 0 : cnt > a.n_list ? a.n_list : cnt;
+        }
+        const int64_t ctx = a.ctx[blockIdx.x];
+        // lane e < KPT loads the id of the wave's slot e (KPT <= 64)
+        const int jl = wave * KPT + lane;
+        const int32_t cidv = ids[jl < a.n_list ? jl : a.n_list - 1];
+        float sc[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int idx = wbase + 64 * e + lane;
+            sc[e] = row[idx < C ? idx : C - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int j = wave * KPT + e;
+            const int32_t cid = __builtin_amdgcn_readlane(cidv, e);
+            const bool use = j < kb && (int64_t)cid * kChunkTokens + lane < ctx;
+            key[e] = use ? score_key(sc[e]) : 0u;
+        }
+    } else {
+        const int32_t* row = a.logits + (int64_t)blockIdx.x * C;
+        int32_t lg[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int idx = wbase + 64 * e + lane;
+            lg[e] = row[idx < C ? idx : C - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = ((uint32_t)lg[e] ^ 0x80000000u);  // positions >= C: never ok
+    }
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const int idx = base + e;
-        key[e] = idx < C ? ((uint32_t)row[idx] ^ 0x80000000u) : 0u;
-        if (idx < C) {
+    for (int e = 0; e < KPT; ++e)
+        if (ok(e)) {
             lmin = min(lmin, key[e]);
             lmax = max(lmax, key[e]);
         }
+    // keys that may be kept: all competing ones (budget, tokens) or those
+    // above the threshold; counted per wave with the min / max
+    const bool capped = TOK || a.counts != nullptr;
+    int avail = 0;
+    if (capped) {
+        const uint32_t tkey = TOK ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) avail += __popcll(__ballot(ok(e) && (TOK || key[e] > tkey)));
     }
     lmin = wave_min(lmin);
     lmax = wave_max(lmax);
     if (lane == 0) {
         sm_min[wave] = lmin;
         sm_max[wave] = lmax;
+        sm_avail[wave] = avail;
     }
     __syncthreads();
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    avail = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
         kmin = min(kmin, sm_min[w]);
         kmax = max(kmax, sm_max[w]);
+        avail += sm_avail[w];
     }
 
     // --- how many to keep ---
     int kk = k;
-    if (counts) {
-        const uint32_t tkey = (uint32_t)thr ^ 0x80000000u;
-        int above = 0;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) above += (base + e < C) && (key[e] > tkey);
-        above = block_sum(above, sm_i, lane, wave);
-        kk = above < k ? above : k;
-        if (tid == 0) counts[blockIdx.x] = kk;
+    if (capped) {
+        kk = avail < k ? avail : k;
+        if (tid == 0) a.counts[blockIdx.x] = kk;
         for (int j = kk + tid; j < k; j += kThreads) dst[j] = -1;
         if (kk == 0) return;  // uniform: every thread saw the same sum
     }
 
     // --- radix select on key - kmin, 8 bits per pass ---
-    // Keys of padding slots (index >= C) are never counted.
-    uint32_t rel[KPT];
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) rel[e] = key[e] - kmin;  // < 2^nb for valid keys
     const uint32_t range = kmax - kmin;
     const int nb = range == 0u ? 0 : 32 - __builtin_clz(range);
     uint64_t prefix = 0;  // digits chosen so far, as the value of key - kmin above bit `hi`
@@ -147,13 +192,27 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
     for (int hi = nb; hi > 0; hi -= kDigitBits) {
         const int w = hi < kDigitBits ? hi : kDigitBits;
         const int sh = hi - w;
-        for (int j = tid; j < kBins; j += kThreads) sm_hist[j] = 0;
+        for (int j = tid; j < kBins * kCopies; j += kThreads) sm_hist[j] = 0;
         __syncthreads();
+        const int copy = lane % kCopies;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const uint64_t r = rel[e];
-            if (base + e < C && (r >> hi) == prefix)
-                atomicAdd(&sm_hist[(int)((r >> sh) & ((1u << w) - 1u))], 1);
+            const uint64_t r = key[e] - kmin;
+            if (ok(e) && (r >> hi) == prefix) {
+                const int bin = (int)((r >> sh) & ((1u << w) - 1u));
+                atomicAdd(&sm_hist[bin * kCopies + copy], 1);
+            }
+        }
+        __syncthreads();
+        {
+            // every thread sums 4 copies of bin tid/4; 4 neighbouring lanes
+            // complete the bin
+            static_assert(kThreads == 4 * kBins && kCopies == 16, "copy reduction layout");
+            const int4 v = *reinterpret_cast<const int4*>(&sm_hist[4 * tid]);
+            int t = (v.x + v.y) + (v.z + v.w);
+            t += __shfl_xor(t, 1);
+            t += __shfl_xor(t, 2);
+            if ((tid & 3) == 0) sm_tot[tid >> 2] = t;
         }
         __syncthreads();
         if (wave == 0) {
@@ -161,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
             int h[4], sl = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                h[j] = sm_hist[4 * lane + j];
+                h[j] = sm_tot[4 * lane + j];
                 sl += h[j];
             }
             int suf = sl;
@@ -187,41 +246,60 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const int32_t* __restric
     const uint32_t vstar = kmin + (uint32_t)prefix;
 
     // --- ordered compaction ---
+    // Per wave: keys > v* and keys == v*; in position order the waves come
+    // one after the other, so exclusive scans over the wave totals give each
+    // wave the equal keys and the outputs before it.
     int n_gt = 0, n_eq = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        const bool valid = base + e < C;
-        n_gt += valid && key[e] > vstar;
-        n_eq += valid && key[e] == vstar;
+        n_gt += __popcll(__ballot(ok(e) && key[e] > vstar));
+        n_eq += __popcll(__ballot(ok(e) && key[e] == vstar));
     }
-    const int eq_before = block_excl_scan(n_eq, sm_i, lane, wave);
-    int take_eq = need - eq_before;
-    take_eq = take_eq < 0 ? 0 : take_eq > n_eq ? n_eq : take_eq;
-    int pos = block_excl_scan(n_gt + take_eq, sm_i, lane, wave);
+    if (lane == 0) {
+        sm_i[wave] = n_gt;
+        sm_j[wave] = n_eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0;
+    for (int w = 0; w < wave; ++w) {
+        gt_before += sm_i[w];
+        eq_before += sm_j[w];
+    }
+    // equal keys are taken in position order: min(eq_before, need) of them precede
+    int pos = gt_before + (eq_before < need ? eq_before : need);
     int eq_seen = eq_before;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        const int idx = base + e;
-        if (idx >= C) continue;
-        // pos < kk holds by construction (|{> v*}| + need == kk); the test
+        const bool gt = ok(e) && key[e] > vstar;
+        const bool eq = ok(e) && key[e] == vstar;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + __popcll(eqm & below) < need);
+        const uint64_t tm = __ballot(take);
+        const int p = pos + __popcll(tm & below);
+        // p < kk holds by construction (|{> v*}| + need == kk); the test
         // keeps every store inside the row even so.
-        if (key[e] > vstar) {
-            if (pos < kk) dst[pos] = idx;
-            ++pos;
-        } else if (key[e] == vstar) {
-            if (eq_seen < need) {
-                if (pos < kk) dst[pos] = idx;
-                ++pos;
-            }
-            ++eq_seen;
-        }
+        if (take && p < kk) dst[p] = wbase + 64 * e + lane;
+        pos += __popcll(tm);
+        eq_seen += __popcll(eqm);
     }
 }
 
-template <int KPT>
-hipError_t launch(const int32_t* logits, int R, int C, int k, int32_t* ids, int32_t thr, int32_t* counts,
-                  hipStream_t stream) {
-    hipLaunchKernelGGL(topk_kernel<KPT>, dim3((unsigned)R), dim3(kThreads), 0, stream, logits, C, k, ids, thr, counts);
+template <bool TOK>
+hipError_t launch(const TopkArgs& a, int R, hipStream_t stream) {
+    const int kpt = (a.C + kThreads - 1) / kThreads;
+    const dim3 grid((unsigned)R), block(kThreads);
+    if (kpt <= 1) hipLaunchKernelGGL((topk_kernel<1, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 2) hipLaunchKernelGGL((topk_kernel<2, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 4) hipLaunchKernelGGL((topk_kernel<4, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 8) hipLaunchKernelGGL((topk_kernel<8, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 12) hipLaunchKernelGGL((topk_kernel<12, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 16) hipLaunchKernelGGL((topk_kernel<16, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 20) hipLaunchKernelGGL((topk_kernel<20, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 24) hipLaunchKernelGGL((topk_kernel<24, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 32) hipLaunchKernelGGL((topk_kernel<32, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 48) hipLaunchKernelGGL((topk_kernel<48, TOK>), grid, block, 0, stream, a);
+    else if (kpt <= 64) hipLaunchKernelGGL((topk_kernel<64, TOK>), grid, block, 0, stream, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -229,15 +307,30 @@ hipError_t launch(const int32_t* logits, int R, int C, int k, int32_t* ids, int3
 
 hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
                        hipStream_t stream) {
-    const int kpt = (C + kThreads - 1) / kThreads;
-    if (kpt <= 1) return launch<1>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 2) return launch<2>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 4) return launch<4>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 8) return launch<8>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 16) return launch<16>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 32) return launch<32>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    if (kpt <= 64) return launch<64>(logits, R, C, k, chunk_ids, thr, counts, stream);
-    return hipErrorInvalidValue;
+    TopkArgs a{};
+    a.logits = logits;
+    a.C = C;
+    a.k = k;
+    a.thr = thr;
+    a.out = chunk_ids;
+    a.counts = counts;
+    return launch<false>(a, R, stream);
+}
+
+hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, const int32_t* list_counts,
+                              const int32_t* ctx, int R, int n_list, int k_tok, int32_t* tok, int32_t* tok_counts,
+                              hipStream_t stream) {
+    TopkArgs a{};
+    a.scores = scores;
+    a.list_ids = list_ids;
+    a.list_counts = list_counts;
+    a.ctx = ctx;
+    a.n_list = n_list;
+    a.C = n_list * kChunkTokens;
+    a.k = k_tok;
+    a.out = tok;
+    a.counts = tok_counts;
+    return launch<true>(a, R, stream);
 }
 
 }  // namespace lsa

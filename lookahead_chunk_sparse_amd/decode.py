@@ -28,6 +28,12 @@ pages' sigmoid gating (selection="threshold": chunks whose score passes 0.5,
 i.e. logit > 0, at most k of them; 2.1 Architecture and 2.4 Configuration of
 the summary), whose budget varies per request.
 
+A token-level second stage (token_topk=k_tok) keeps, at every step, only
+the k_tok best tokens of the recalled chunks by the model's own token scores,
+passed to attend() (summary 2.1 Architecture: the native token-level top-k
+runs over the recalled subset only; the pages give no scoring formula, so
+the scores are an input), and attends over those tokens.
+
 Several layers can share one selection (kv given as a list of per-layer
 stores): each interval runs one indexer scan and selection, then every step
 attends over the same chunks in every layer.  Reusing one layer's selection
@@ -45,8 +51,8 @@ import math
 
 import torch
 
-from ._binding import (alloc_workspace, lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend, lsa_index_score,
-                       lsa_pool_assign, lsa_threshold_chunks, lsa_topk_chunks)
+from ._binding import (CHUNK_TOKENS, alloc_workspace, lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend,
+                       lsa_index_score, lsa_pool_assign, lsa_threshold_chunks, lsa_topk_chunks, lsa_topk_tokens)
 
 TAU = 64
 
@@ -70,7 +76,8 @@ class LsaDecoder:
                  kv: torch.Tensor | None = None, host_kv: torch.Tensor | None = None, tau: int = TAU,
                  n_split: int = 0, sm_scale: float | None = None, fetch: str = "pull", fetch_grid: int = 0,
                  delta: bool | None = None, selection: str = "topk", logit_threshold: int = 0,
-                 seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None, device="cuda"):
+                 seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None, token_topk: int = 0,
+                 device="cuda"):
         if (kv is None) == (host_kv is None):
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
@@ -119,7 +126,14 @@ class LsaDecoder:
         self.sel_ids = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
         self.sel_counts = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(2)] \
             if selection == "threshold" else [None, None]
-        self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
+        self.k_tok = int(token_topk)
+        if self.k_tok:
+            self.tok = torch.empty((B, self.k_tok), dtype=torch.int32, device=dev)
+            self.tok_counts = torch.empty(B, dtype=torch.int32, device=dev)
+            entries = (self.k_tok + CHUNK_TOKENS - 1) // CHUNK_TOKENS
+            self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, entries, n_split, device=dev)
+        else:
+            self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
         if self.lag:
             if self.delta:
                 one = torch.empty((B, 2 * k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
@@ -151,31 +165,43 @@ class LsaDecoder:
             lsa_topk_chunks(self.logits.view(self.B, self.C), self.k, chunk_ids=ids, stream=stream)
         return ids
 
-    def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None, layer: int = 0) -> torch.Tensor:
+    def attend(self, q: torch.Tensor, sel: int, out: torch.Tensor, stream=None, layer: int = 0,
+               token_scores: torch.Tensor | None = None) -> torch.Tensor:
         """One decode step's attention with selection `sel` (on the host tier
         with the delta fetch, the selection's pool slots must have been
-        assigned, as run_interval does)."""
+        assigned, as run_interval does).  With the token stage, token_scores
+        (fp32 [B][k*64], the step's scores of the recalled tokens by list
+        position) pick the k_tok tokens attended over."""
         ids = self.sel_ids[sel % 2]
+        tok = {}
+        if self.k_tok:
+            if token_scores is None:
+                raise ValueError("the token stage needs this step's token_scores")
+            lsa_topk_tokens(token_scores, ids, self.ctx_len, self.k_tok, counts=self.sel_counts[sel % 2],
+                            tok=self.tok, tok_counts=self.tok_counts, stream=stream)
+            tok = dict(tok=self.tok, tok_counts=self.tok_counts)
         if self.lag:
             slots = self.sel_slots[sel % 2] if self.delta else self.slots
             return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
                                      workspace=self.workspace, n_split=self.n_split, out=out,
-                                     seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
+                                     seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream, **tok)
         kv = self.layers[layer] if self.layers is not None else self.kv
         return lsa_gather_attend(q, kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
                                  n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2],
-                                 seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream)
+                                 seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream, **tok)
 
     # ---- one interval ------------------------------------------------------
-    def run_interval(self, i: int, q_idx: torch.Tensor, qs, outs) -> None:
+    def run_interval(self, i: int, q_idx: torch.Tensor, qs, outs, token_scores=None) -> None:
         """Enqueue interval i: its re-selection and len(qs) attention steps.
         qs[j] is the bf16 [B][Hq][d] query of step i*tau + j; outs[j] receives
-        its fp32 output (the same tensor may be passed for every step)."""
+        its fp32 output (the same tensor may be passed for every step);
+        token_scores[j] is step j's token scores when the token stage is on."""
+        ts = token_scores if token_scores is not None else [None] * len(qs)
         if not self.lag:
             self.reselect(q_idx, i)
-            for q, o in zip(qs, outs):
+            for q, o, sc in zip(qs, outs, ts):
                 if self.layers is None:
-                    self.attend(q, i, o)
+                    self.attend(q, i, o, token_scores=sc)
                 else:  # q[l] and o[l] per layer; one selection for all layers
                     for layer in range(len(self.layers)):
                         self.attend(q[layer], i, o[layer], layer=layer)
@@ -195,8 +221,8 @@ class LsaDecoder:
             self._fetch(0)
         src = max(i - 1, 0)
         main.wait_event(self.fetch_done[src % 2])
-        for q, o in zip(qs, outs):
-            self.attend(q, src, o)
+        for q, o, sc in zip(qs, outs, ts):
+            self.attend(q, src, o, token_scores=sc)
         if i >= 1:
             self._fetch(i)  # overlaps the steps just enqueued
         self.attn_done.record(main)

@@ -116,6 +116,28 @@ def test_attend_validation(lsa, lib):
     assert call(ns=2, ws=BOGUS + 16, wsb=need) == 3 and "256-byte" in _err(lib)
 
 
+def test_token_stage_validation(lib):
+    f = lib.lsa_topk_tokens
+    # scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, stream
+    assert f(0, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, 0, 0) == 1 and "tok_counts" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 0, BOGUS, BOGUS, 0) == 1 and "k_tok=0" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 1025, 8, BOGUS, BOGUS, 0) == 2 and "k <= 1024" in _err(lib)
+    assert f(BOGUS + 2, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1 and "alignment" in _err(lib)
+    g = lib.lsa_gather_attend_tokens
+    # q, kv, C, ids, slots, counts, ctx, tok, tok_counts, k_tok, seg, seg_len, S_max, B, Hq, Hkv, d, k, scale,
+    # ws, ws_bytes, n_split, out, stream
+    args = [BOGUS, BOGUS, 16, BOGUS, 0, 0, BOGUS, BOGUS, 0, 128, 0, 0, 0, 2, 64, 8, 128, 4, 0.088, 0, 0, 1, BOGUS, 0]
+    a = list(args); a[7] = 0
+    assert g(*a) == 1 and "tok is required" in _err(lib)
+    a = list(args); a[9] = 0
+    assert g(*a) == 1 and "k_tok=0" in _err(lib)
+    a = list(args); a[2] = 1 << 22
+    assert g(*a) == 2 and "C_store" in _err(lib)
+    a = list(args); a[21] = 2  # two splits of the 2 token blocks need a workspace
+    assert g(*a) == 3 and "workspace" in _err(lib)
+
+
 def test_workspace_size_rules(lsa):
     # one split needs no workspace; the partials grow with the split count
     assert lsa.lsa_gather_attend_workspace_size(16, 64, 8, 128, 276, 1) == 0

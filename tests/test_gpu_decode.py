@@ -243,3 +243,52 @@ def test_decode_layers_share_one_selection(oracle_lib):
             ref = oracle_lib.gather_attend(qh[(t, l)][b:b + 1], chunks, ids[b:b + 1], ctx[b:b + 1], w.Hkv,
                                            w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None])
             check_attention(o[b].cpu().numpy(), ref[0], f"layer {l} step {t} request {b}")
+
+
+def test_decode_token_stage_128k(oracle_lib):
+    """The two-stage selection at the 128K workload's full size: chunks by the
+    memory indexer every 64 steps, then at every step the 2048 best tokens
+    of the recalled chunks by a per-step token score, attended over in the
+    benchmark's launch configuration."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["128k"]
+    k_tok, steps, reqs = 2048, (0, 1, 64, 65), [0, 9]
+    dev = torch.device("cuda")
+    say(f"token stage 128k: B={w.B} k={w.k} k_tok={k_tok}")
+    K = W.indexer_keys(w)
+    dec = LsaDecoder(k_idx=to_dev(K), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k, alpha=w.alpha,
+                     kv=W.device_kv_store(w, dev), token_topk=k_tok)
+    scores = {t: synth.bf16_bits_to_f32(synth.normal_bf16((w.B, w.k * 64), 5, synth.stream(synth.TAG_MISC, 4100 + t)))
+              for t in steps}
+    outs, toks, sels = {}, {}, {}
+    for i in range(2):
+        ts = [t for t in steps if t // w.tau == i]
+        o = [torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for _ in ts]
+        qs = [to_dev_bf16(W.attn_query(w, t)) for t in ts]
+        dec.reselect(to_dev(W.indexer_query(w, i)), i)
+        for t, q, oo in zip(ts, qs, o):
+            dec.attend(q, i, oo, token_scores=to_dev(np.ascontiguousarray(scores[t], dtype=np.float32)))
+            toks[t] = (dec.tok.cpu().numpy().copy(), dec.tok_counts.cpu().numpy().copy())
+            outs[t] = oo
+        torch.cuda.synchronize()
+        sels[i] = dec.sel_ids[i % 2].cpu().numpy().copy()
+    say("  GPU run done")
+    ctx = W.ctx_lens(w)
+    for t in steps:
+        ids = sels[t // w.tau]
+        _, _, ref_ids = oracle_lib.select(W.indexer_query(w, t // w.tau), K, w.k, w.alpha)
+        assert np.array_equal(ids, ref_ids)
+        ref_tok, ref_tc = oracle_lib.topk_tokens(scores[t][reqs], ids[reqs], ctx[reqs], k_tok)
+        assert np.array_equal(toks[t][0][reqs], ref_tok) and np.array_equal(toks[t][1][reqs], ref_tc), t
+        out = outs[t].cpu().numpy()
+        for n, b in enumerate(reqs):
+            chunks = W.kv_chunks(w, b, ids[b])[None]
+            ref = oracle_lib.gather_attend(W.attn_query(w, t)[b:b + 1], chunks, ids[b:b + 1], ctx[b:b + 1], w.Hkv,
+                                           w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None],
+                                           tok=ref_tok[n:n + 1], tok_counts=ref_tc[n:n + 1])
+            check_attention(out[b], ref[0], f"token stage step {t} request {b}")

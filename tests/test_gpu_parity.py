@@ -297,6 +297,110 @@ def test_attend_deterministic(lsa, synth_lib):
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------------------ token-level stage
+
+def _token_scores(synth_lib, B, n, seed):
+    """bf16-rounded normals coarsened to quarters (long runs of equal scores),
+    with signed zeros and infinities planted."""
+    s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), seed, synth_lib.stream(synth_lib.TAG_MISC, 4000)))
+    s = np.round(s * 4) / 4
+    s[:, 3::17] = 0.0
+    s[:, 5::19] = -0.0
+    s[:, 7::41] = np.inf
+    s[:, 11::43] = -np.inf
+    return np.ascontiguousarray(s, dtype=np.float32)
+
+
+@pytest.mark.parametrize("B,C,k,k_tok", [
+    (4, 12, 5, 7),        # tiny
+    (4, 12, 5, 400),      # budget above the usable tokens: padding
+    (3, 64, 40, 600),
+    (4, 2048, 276, 2048),  # the 128K recall, a 2048-token budget
+    (2, 4096, 1024, 2048),  # the largest list: 65536 positions
+])
+def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
+    say("token top-k", B, C, k, k_tok)
+    scores = _token_scores(synth_lib, B, k * 64, seed=k)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4010 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    ctx[0] = ids[0, -1] * 64 + 17                  # the last listed chunk is partial
+    if B > 2:
+        ctx[2] = ids[2, k // 2] * 64               # half the list lies past the context
+    counts = np.full(B, k, dtype=np.int32)
+    counts[1] = max(1, k - 3)
+    for cn in (None, counts):
+        tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok,
+                                      counts=None if cn is None else to_dev(cn))
+        ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=cn)
+        assert np.array_equal(tc.cpu().numpy(), rc), (B, C, k, k_tok)
+        assert np.array_equal(tok.cpu().numpy(), ref), (B, C, k, k_tok)
+
+
+TOKEN_CASES = [
+    # B, Hq, Hkv, d, C, k, k_tok, n_split, with slots, segment length (0: none)
+    (2, 64, 8, 128, 30, 12, 100, 0, False, 0),
+    (2, 64, 8, 128, 30, 12, 64, 1, False, 0),
+    (3, 64, 8, 128, 40, 20, 700, 5, True, 0),
+    (2, 16, 2, 64, 20, 8, 130, 2, False, 0),
+    (2, 64, 8, 128, 30, 12, 300, 3, False, 200),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,C,k,k_tok,n_split,use_slots,seg_n", TOKEN_CASES)
+def test_attend_tokens_parity(lsa, oracle_lib, synth_lib, B, Hq, Hkv, d, C, k, k_tok, n_split, use_slots, seg_n):
+    """Attention over listed tokens: unsorted lists with invalid entries
+    (-1, positions of unused entries, tokens past the context), ragged
+    counts, a compact pool with slots, a resident segment."""
+    say("token attend", B, Hq, Hkv, d, C, k, k_tok, n_split, use_slots, seg_n)
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=70 + k_tok, qscale=4.0)
+    ids = _ids(synth_lib, B, C, k, seed=71)
+    counts = np.full(B, k, dtype=np.int32)
+    counts[-1] = k - 2
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    ctx[0] = ids[0, -1] * 64 + 30
+    rng = np.random.default_rng(k_tok)
+    tok = np.stack([rng.permutation(k * 64)[:k_tok] if k_tok <= k * 64 else rng.integers(0, k * 64, k_tok)
+                    for _ in range(B)]).astype(np.int32)
+    tok[:, 1] = -1
+    tok[:, 2] = k * 64 + 5
+    tok_counts = np.full(B, k_tok, dtype=np.int32)
+    tok_counts[0] = max(1, k_tok - 37)
+    store, slots = kv, None
+    if use_slots:  # a compact pool in permuted slot order
+        perm = np.array([[(j * 7) % k for j in range(k)]] * B, dtype=np.int32)
+        store = np.zeros((B, k, 2, Hkv, 64, d), dtype=np.uint16)
+        for b in range(B):
+            store[b, perm[b]] = kv[b, ids[b]]
+        slots = perm
+    seg = seg_len = None
+    kw = {}
+    if seg_n:
+        seg = synth_lib.normal_bf16((B, 2, Hkv, 256, d), 72, synth_lib.stream(synth_lib.TAG_MISC, 4020))
+        seg_len = np.array([seg_n, 1] + [0] * (B - 2), dtype=np.int32)
+        kw = dict(seg_kv=to_dev_bf16(seg), seg_len=to_dev(seg_len))
+    out = lsa.lsa_gather_attend_tokens(to_dev_bf16(q), to_dev_bf16(store), to_dev(ids), to_dev(ctx), to_dev(tok),
+                                       to_dev(tok_counts), sm_scale=1 / math.sqrt(d), n_split=n_split,
+                                       counts=to_dev(counts), slots=None if slots is None else to_dev(slots), **kw)
+    ref = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d), counts=counts, tok=tok,
+                                   tok_counts=tok_counts, seg_kv=seg, seg_len=seg_len)
+    say("  ", check_attention(out.cpu().numpy(), ref, "token attend"))
+
+
+def test_attend_tokens_all_listed_equals_chunk_attention(lsa, synth_lib):
+    """Listing every token of the chunks reproduces chunk attention up to
+    rounding order (same tokens, blocks of 64 listed rows instead of tiles)."""
+    B, Hq, Hkv, d, C, k = 2, 64, 8, 128, 30, 10
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=80)
+    ids = _ids(synth_lib, B, C, k, seed=81)
+    ctx = np.array([ids[0, -1] * 64 + 9, C * 64], dtype=np.int32)
+    args = (to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx))
+    a = lsa.lsa_gather_attend(*args, n_split=1).cpu().numpy()
+    tok = np.tile(np.arange(k * 64, dtype=np.int32), (B, 1))
+    t = lsa.lsa_gather_attend_tokens(*args, to_dev(tok), None, n_split=1).cpu().numpy()
+    np.testing.assert_allclose(t, a, rtol=0, atol=2e-6)
+
+
 # ------------------------------------------------------------------ fetch
 
 def test_fetch_byte_exact(lsa, oracle_lib, synth_lib):
