@@ -285,6 +285,121 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
     print(json.dumps(res), flush=True)
 
 
+def token_attend_bytes(w, k_tok: int) -> int:
+    """Algorithmic HBM bytes of one token-list attention launch: the K and V
+    rows of the k_tok listed tokens of every (request, KV head), the bf16
+    queries, the fp32 outputs, the token list and the chunk ids."""
+    kv = w.B * w.Hkv * k_tok * 2 * w.d * 2
+    return kv + w.B * w.Hq * w.d * (2 + 4) + w.B * k_tok * 4 + w.B * w.k * 4
+
+
+def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
+    """Two-stage selection: chunks by the memory indexer every tau steps,
+    then at every step the k_tok best tokens of the recalled chunks by a
+    per-step token score (synthetic, bf16-rounded normals; the model's own
+    token scorer is not on the path), attended over.  hipGraph replay of
+    exactly `steps` steps after `warmup` steps."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd import lsa_gather_attend_default_splits, lsa_topk_tokens
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    dec = LsaDecoder(k_idx=torch.from_numpy(W.indexer_keys(w)).to(dev), ctx_len=torch.from_numpy(W.ctx_lens(w)).to(dev),
+                     Hq=w.Hq, k=w.k, alpha=w.alpha, kv=W.device_kv_store(w, dev), n_split=n_split, token_topk=k_tok,
+                     device=dev)
+    n_pool = 16  # distinct per-step token-score tensors, used in turn
+    pool = [torch.from_numpy(synth.bf16_bits_to_f32(synth.normal_bf16((w.B, w.k * 64), w.seed,
+                                                                      synth.stream(synth.TAG_MISC, 5000 + i))))
+            .to(dev) for i in range(n_pool)]
+    log(f"[bench] inputs placed in HBM in {time.time() - t0:.1f}s")
+    n_q = max(steps, warmup, w.tau)
+    q_all, qidx = make_queries(w, n_q)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+
+    def enqueue(n):
+        for i in range((n + w.tau - 1) // w.tau):
+            ts = range(i * w.tau, min((i + 1) * w.tau, n))
+            dec.run_interval(i, qidx[i], [q_all[t] for t in ts], [out] * len(ts),
+                             token_scores=[pool[t % n_pool] for t in ts])
+
+    def graph(n):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            enqueue(min(n, w.tau))
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            enqueue(n)
+        return g
+
+    if warmup:
+        graph(warmup).replay()
+    g = graph(steps)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    steps_s = 1000.0 / ms_per_step
+
+    # the two per-step kernels, event-timed on the stream they run on
+    stream = torch.cuda.current_stream()
+    dec.reselect(qidx[0], 0)
+    ids = dec.sel_ids[0]
+
+    def timed(fn, n=100):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for j in range(5):
+            fn(j)
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(j)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) for a, b in evs)
+
+    topk_ms = timed(lambda j: lsa_topk_tokens(pool[j % n_pool], ids, dec.ctx_len, k_tok, tok=dec.tok,
+                                              tok_counts=dec.tok_counts))
+    lsa_topk_tokens(pool[0], ids, dec.ctx_len, k_tok, tok=dec.tok, tok_counts=dec.tok_counts)
+    from lookahead_chunk_sparse_amd import lsa_gather_attend
+    att_ms = timed(lambda j: lsa_gather_attend(q_all[j % n_q], dec.kv, ids, dec.ctx_len, dec.sm_scale,
+                                               workspace=dec.workspace, n_split=dec.n_split, out=out, tok=dec.tok,
+                                               tok_counts=dec.tok_counts))
+    a_bytes = token_attend_bytes(w, k_tok)
+    achieved = a_bytes / (att_ms * 1e-3) / 1e9
+    entries = (k_tok + 63) // 64
+    splits = dec.n_split or lsa_gather_attend_default_splits(w.B, w.Hkv, entries)
+    step_b = a_bytes + w.B * w.k * 64 * 4 + (w.B * w.C * w.d_idx) // w.tau  # + token scores read by the top-k
+    print(json.dumps({
+        "metric": METRIC, "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name} context decode, two-stage selection: batch {w.B}, {w.Hq} query / {w.Hkv} KV "
+                         f"heads, head dim {w.d}, top-{w.k} of {w.C} chunks every {w.tau} steps, then the top "
+                         f"{k_tok} of their {w.k * 64} tokens by a per-step token score"),
+            "global_batch": w.B, "seq_len": w.N, "retained_chunks": w.k, "retained_tokens": k_tok,
+            "n_split": splits, "timing": "hipGraph replay of all steps", "tokens_per_s": round(steps_s * w.B, 1),
+            "step_bytes": step_b, "step_GBs": round(step_b * steps_s / 1e9, 1),
+            "token_topk_us": round(topk_ms * 1e3, 2), "token_attend_us": round(att_ms * 1e3, 2),
+        },
+        "roofline": {"bound": "hbm", "kernel": "gather-attend over listed tokens (split kernel + combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": a_bytes,
+                     "mean_launch_us": round(att_ms * 1e3, 2)},
+    }), flush=True)
+
+
 def copy_bandwidth(n_bytes: int = 1 << 30, reps: int = 20) -> float:
     """GB/s of a plain device copy (torch's copy kernel) of n_bytes, counting
     the bytes read and the bytes written, event-timed over reps copies."""
@@ -365,6 +480,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--token-topk", type=int, default=0, metavar="K_TOK",
+                    help="two-stage selection: attend over the K_TOK best tokens of the recalled chunks")
     ap.add_argument("--layers", type=int, default=1, help="layers sharing one selection (HBM-resident only)")
     ap.add_argument("--fetch", default="pull", choices=("pull", "memcpy"), help="host-tier fetch method")
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
@@ -399,6 +516,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.drift:
         w = w.replace(drift=True, n_golden=min(w.n_golden, w.C // max(1, (args.steps + args.warmup) // w.tau + 1)))
+    if args.token_topk:
+        token_stage_bench(w, args.steps, args.warmup, args.token_topk, args.n_split)
+        return
     if w.host_tier:
         host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
                         False if args.no_delta else None)

@@ -105,3 +105,49 @@ def test_host_tier_graph_replays_match_eager():
         for i in range(3):
             for t in range(per):
                 assert np.array_equal(outs[i][t].cpu().numpy(), eager[i][t]), f"replay {rep}, interval {i}, step {t}"
+
+
+def test_token_stage_graph_replays_match_eager():
+    """Chunk selection, then per step the token top-k and the token-list
+    attention, captured in one graph: every replay gives the eager bits."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"]
+    dev = torch.device("cuda")
+    dec = LsaDecoder(k_idx=to_dev(W.indexer_keys(w)), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k,
+                     alpha=w.alpha, kv=W.device_kv_store(w, dev), token_topk=300)
+    steps = 6
+    qs = [to_dev_bf16(W.attn_query(w, t)) for t in range(steps)]
+    sc = [to_dev(np.ascontiguousarray(synth.bf16_bits_to_f32(
+        synth.normal_bf16((w.B, w.k * 64), 3, synth.stream(synth.TAG_MISC, 5100 + t))), dtype=np.float32))
+        for t in range(steps)]
+    qidx = to_dev(W.indexer_query(w, 0))
+    outs = [torch.zeros((w.B, w.Hq, w.d), dtype=torch.float32, device=dev) for _ in range(steps)]
+    dec.run_interval(0, qidx, qs, outs, token_scores=sc)
+    torch.cuda.synchronize()
+    eager = [o.cpu().numpy().copy() for o in outs]
+    tok_eager = dec.tok.cpu().numpy().copy()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dec.run_interval(0, qidx, qs, outs, token_scores=sc)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device=dev)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        dec.tok.fill_(-7)
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(dec.tok.cpu().numpy(), tok_eager), f"replay {rep}: token list"
+        for t in range(steps):
+            assert np.array_equal(outs[t].cpu().numpy(), eager[t]), f"replay {rep}, step {t}"
