@@ -253,8 +253,9 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
  *  k_tok >= 1
  *  kv          the store of lsa_gather_attend; C_store * 2*Hkv*64 < 2^31
  *  workspace   lsa_gather_attend_workspace_size(B, Hq, Hkv, d, ceil(k_tok/64),
- *              n_split) bytes; n_split splits the token list (0 = library
- *              choice for ceil(k_tok/64) blocks of 64 listed tokens)
+ *              n_split) bytes; n_split splits the token list into contiguous
+ *              parts (0 = library choice for ceil(k_tok/64) blocks of 64
+ *              listed tokens)
  */
 lsa_status lsa_gather_attend_tokens(const uint16_t* q, const uint16_t* kv, int64_t C_store, const int32_t* chunk_ids,
                                     const int32_t* slots, const int32_t* counts, const int32_t* ctx_len,

@@ -288,6 +288,30 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     const int32_t* tok_b = TOK ? a.tok + (int64_t)b * a.k_tok : nullptr;
     const int rows_per_chunk = 2 * a.Hkv * kChunkTokens;
     const int32_t* pos_src = a.slots ? a.slots + (int64_t)b * a.k : ids;
+    // TOK: the request's list (chunk ids, store positions) staged in LDS once
+    // when it fits; the staging of every round then looks positions up there
+    constexpr int kTokPerThread = kTokCache * kChunkTokens / kThreads;
+    constexpr int kIdCache = 1024;
+    __shared__ int sm_cid[TOK ? kIdCache : 1];
+    __shared__ int sm_pos[TOK ? kIdCache : 1];
+    const bool list_in_lds = TOK && kb <= kIdCache;
+    // listed positions of a staging round, loaded clamped and unconditionally;
+    // the first round's loads are issued here, before the list staging, so
+    // the two round trips overlap
+    int32_t pv[TOK ? kTokPerThread : 1];
+    auto load_positions = [&](int64_t seg) {
+#pragma unroll
+        for (int r = 0; r < kTokPerThread; ++r) {
+            const int64_t u = seg * kChunkTokens + threadIdx.x + r * kThreads;
+            pv[r] = tok_b[u < a.k_tok ? u : a.k_tok - 1];
+        }
+    };
+    if (TOK && j0 < j1) load_positions(j0);
+    if (list_in_lds)
+        for (int j = threadIdx.x; j < kb; j += kThreads) {
+            sm_cid[j] = ids[j];
+            sm_pos[j] = pos_src[j];
+        }  // read after the first barrier of the staging loop
     const uint16_t* seg_b =
         a.seg_kv ? a.seg_kv + ((int64_t)b * 2 * a.Hkv + g) * (int64_t)a.S_max * D : kv_b;  // kv_b: never used
     const int64_t seg_v_off = (int64_t)a.Hkv * a.S_max * D;
@@ -335,19 +359,25 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
         const int segn = (int)(j1 - seg < kCache ? j1 - seg : kCache);
         __syncthreads();  // the previous segment's entries are no longer read
         if constexpr (TOK) {
-            for (int x = threadIdx.x; x < segn * kChunkTokens; x += kThreads) {
+            // Each thread stages kTokPerThread tokens: the listed positions
+            // (loaded already for the first round), looked up in the list
+            // staged in LDS.
+            if (seg != j0) load_positions(seg);
+#pragma unroll
+            for (int r = 0; r < kTokPerThread; ++r) {
+                const int x = threadIdx.x + r * kThreads;
+                if (x >= segn * kChunkTokens) break;
                 const int e = x / kChunkTokens, t = x % kChunkTokens;
                 const int64_t jb = seg + e;
                 int row = -1;
                 if (jb < n_main) {
                     const int64_t u = jb * kChunkTokens + t;
-                    if (u < n_tok) {
-                        const int64_t p = tok_b[u];
-                        if (p >= 0 && p < kb * kChunkTokens) {
-                            const int64_t j = p / kChunkTokens, tt = p % kChunkTokens;
-                            if ((int64_t)ids[j] * kChunkTokens + tt < ctx)
-                                row = (int)((int64_t)pos_src[j] * rows_per_chunk + tt);
-                        }
+                    const int64_t p = pv[r];
+                    if (u < n_tok && p >= 0 && p < kb * kChunkTokens) {
+                        const int j = (int)(p / kChunkTokens), tt = (int)(p % kChunkTokens);
+                        const int64_t cid = list_in_lds ? sm_cid[j] : ids[j];
+                        const int64_t pos = list_in_lds ? sm_pos[j] : pos_src[j];
+                        if (cid * kChunkTokens + tt < ctx) row = (int)(pos * rows_per_chunk + tt);
                     }
                 } else {
                     const int64_t sidx = (jb - n_main) * kChunkTokens + t;
