@@ -292,3 +292,50 @@ def test_decode_token_stage_128k(oracle_lib):
                                            w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None],
                                            tok=ref_tok[n:n + 1], tok_counts=ref_tc[n:n + 1])
             check_attention(out[b], ref[0], f"token stage step {t} request {b}")
+
+
+def test_decode_token_stage_on_host_tier(oracle_lib):
+    """Token stage over the host tier's HBM pool: the listed positions name
+    entries of the selection in use (lag 1), whose K/V sit at the delta
+    fetch's pool slots; the third interval attends a delta-fetched selection."""
+    import torch
+
+    import synth
+    from lookahead_chunk_sparse_amd.decode import LsaDecoder
+    from synth import workloads as W
+
+    w = W.WORKLOADS["32k"].replace(host_tier=True)
+    k_tok = 500
+    dev = torch.device("cuda")
+    K = W.indexer_keys(w)
+    dec = LsaDecoder(k_idx=to_dev(K), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k, alpha=w.alpha,
+                     host_kv=W.pinned_kv_store(w), token_topk=k_tok)
+    plan = {0: [0, 1], 1: [64], 2: [128, 129]}  # interval -> steps
+    outs, toks = {}, {}
+    for i, ts in plan.items():
+        src = max(i - 1, 0)  # lag 1
+        for n, t in enumerate(ts):
+            q = to_dev_bf16(W.attn_query(w, t))
+            sc = synth.bf16_bits_to_f32(synth.normal_bf16((w.B, w.k * 64), 6, synth.stream(synth.TAG_MISC, 4200 + t)))
+            o = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+            if n == 0:  # the interval's re-selection, fetch and first step
+                dec.run_interval(i, to_dev(W.indexer_query(w, i)), [q], [o], token_scores=[to_dev(sc)])
+            else:       # a further step of the same interval
+                dec.attend(q, src, o, token_scores=to_dev(sc))
+            torch.cuda.synchronize()
+            toks[t] = (src, sc, dec.tok.cpu().numpy().copy(), dec.tok_counts.cpu().numpy().copy())
+            outs[t] = o
+    dec.join()
+    torch.cuda.synchronize()
+    ctx = W.ctx_lens(w)
+    for t, (src, scores, tok, tc) in toks.items():
+        _, _, ids = oracle_lib.select(W.indexer_query(w, src), K, w.k, w.alpha)
+        ref_tok, ref_tc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok)
+        assert np.array_equal(tok, ref_tok) and np.array_equal(tc, ref_tc), t
+        out = outs[t].cpu().numpy()
+        for b in range(w.B):
+            chunks = W.kv_chunks(w, b, ids[b])[None]
+            ref = oracle_lib.gather_attend(W.attn_query(w, t)[b:b + 1], chunks, ids[b:b + 1], ctx[b:b + 1], w.Hkv,
+                                           w.sm_scale, slots=np.arange(w.k, dtype=np.int32)[None],
+                                           tok=ref_tok[b:b + 1], tok_counts=ref_tc[b:b + 1])
+            check_attention(out[b], ref[0], f"host-tier token stage step {t} request {b}")

@@ -505,3 +505,29 @@ def test_fetch_rejects_pageable(lsa):
     pool = torch.zeros((1, 2, 2, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(lsa.LsaError, match="pinned"):
         lsa.lsa_fetch_chunks(host, torch.tensor([[0, 1]], dtype=torch.int32), pool)
+
+
+def test_concurrent_streams_match_serial(lsa, synth_lib):
+    """Calls on two HIP streams with their own workspaces, interleaved and
+    running concurrently, give the bits of the same calls run one at a time
+    (the library keeps no mutable state between calls)."""
+    import torch
+    B, Hq, Hkv, d, C, k = 4, 64, 8, 128, 40, 24
+    probs = []
+    for seed in (90, 91):
+        q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=seed)
+        ids = _ids(synth_lib, B, C, k, seed=seed + 10)
+        probs.append((to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(np.full(B, C * 64, dtype=np.int32))))
+    serial = [lsa.lsa_gather_attend(*p, n_split=3).cpu().numpy() for p in probs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [lsa.alloc_workspace(B, Hq, Hkv, d, k, 3) for _ in streams]
+    outs = [[torch.empty((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(6)] for _ in streams]
+    torch.cuda.synchronize()
+    for rep in range(6):
+        for sidx, st in enumerate(streams):
+            lsa.lsa_gather_attend(*probs[sidx], n_split=3, workspace=wss[sidx], out=outs[sidx][rep],
+                                  stream=st)
+    torch.cuda.synchronize()
+    for sidx in range(2):
+        for rep in range(6):
+            assert np.array_equal(outs[sidx][rep].cpu().numpy(), serial[sidx]), (sidx, rep)
