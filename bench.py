@@ -419,6 +419,48 @@ def copy_bandwidth(n_bytes: int = 1 << 30, reps: int = 20) -> float:
     return gbs
 
 
+def read_ceiling(kv, tile_bytes: int = 16384, n_read: int = 1 << 30) -> dict:
+    """Best read bandwidth of randomly placed whole tiles of `kv` (the K/V
+    store itself, tiles of one (chunk, K|V, head)): the attention's access
+    pattern without its arithmetic, with the measurement-only kernel of
+    libtileread.so, over a few grid / unroll shapes."""
+    import ctypes
+
+    import torch
+
+    from lookahead_chunk_sparse_amd import build as B
+    if not os.path.exists(B.MEASURE_LIB_PATH):
+        raise ImportError(f"{B.MEASURE_LIB_PATH} is not built")
+    L = ctypes.CDLL(B.MEASURE_LIB_PATH)
+    L.lsa_measure_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_all = kv.numel() * kv.element_size() // tile_bytes
+    n_tiles = min(n_all, n_read // tile_bytes)
+    g = torch.Generator().manual_seed(0)
+    off = (torch.randperm(n_all, generator=g)[:n_tiles].to(torch.int64) * (tile_bytes // 16)).to(kv.device)
+    assert int(off.max()) + tile_bytes // 16 <= kv.numel() * kv.element_size() // 16  # every tile inside the store
+    stream = torch.cuda.current_stream()
+    best = (0.0, None)
+    for grid in (512, 1024, 2048):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=kv.device)
+        for unroll in (2, 4):
+            args = (kv.data_ptr(), off.data_ptr(), n_tiles, tile_bytes // 16, sink.data_ptr(), grid, unroll,
+                    stream.cuda_stream)
+            if L.lsa_measure_tile_read(*args) != 0:
+                raise RuntimeError("tile-read launch failed")
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(10):
+                L.lsa_measure_tile_read(*args)
+            end.record(stream)
+            torch.cuda.synchronize()
+            gbs = n_tiles * tile_bytes * 10 / (start.elapsed_time(end) * 1e-3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, (grid, unroll))
+    return {"GBs": round(best[0], 1), "tile_bytes": tile_bytes, "grid": best[1][0], "unroll": best[1][1]}
+
+
 def copy_calibration(n_bytes: int, reps: int):
     """A plain device-to-device copy of known size (for counter scaling)."""
     import torch
@@ -576,6 +618,8 @@ def main():
     traffic = traffic_for_current_kernel(w)
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy (torch, 1 GiB, read + write bytes): {copy_gbs:.0f} GB/s")
+    ceiling = read_ceiling(dec.kv)
+    log(f"[bench] read ceiling, random 16 KB tiles of the K/V store: {ceiling['GBs']:.0f} GB/s")
 
     sb = step_bytes(w, args.layers)
     layer_txt = "one layer" if args.layers == 1 else f"{args.layers} layers sharing one selection"
@@ -607,6 +651,10 @@ def main():
             "step_frac_of_hbm_peak": round(sb * steps_s / 1e9 / HBM_PEAK_GBS, 4),
             "copy_GBs": round(copy_gbs, 1),
             "step_frac_of_copy": round(sb * steps_s / 1e9 / copy_gbs, 4),
+            "read_ceiling_GBs": ceiling["GBs"],
+            "read_ceiling": f"random {ceiling['tile_bytes'] // 1024} KB tiles of the K/V store, "
+                            f"grid {ceiling['grid']}, unroll {ceiling['unroll']}",
+            "attention_frac_of_read_ceiling": round(achieved / ceiling["GBs"], 4),
         },
         "roofline": {
             "bound": "hbm",

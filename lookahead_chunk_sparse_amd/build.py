@@ -1,4 +1,6 @@
-"""Build the HIP library liblsa.so in-tree for gfx950 (hipcc, no torch)."""
+"""Build the HIP library liblsa.so in-tree for gfx950 (hipcc, no torch), and
+the measurement-only libtileread.so that bench.py uses to state the HBM read
+ceiling of the attention's access pattern."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblsa.so")
 SOURCES = ["lsa_abi.hip", "index_score.hip", "topk_chunks.hip", "gather_attend.hip", "fetch_pull.hip",
            "pool_assign.hip"]
+MEASURE_SOURCES = ["measure/tile_read.hip"]
+MEASURE_LIB_PATH = os.path.join(HERE, "libtileread.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are kept out of the device code.
@@ -20,9 +24,9 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out_path: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out_path + ".tmp"
     cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -34,8 +38,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(verbose: bool = False) -> str:
+    _compile(MEASURE_SOURCES, MEASURE_LIB_PATH, verbose)
+    return _compile(SOURCES, LIB_PATH, verbose)
 
 
 if __name__ == "__main__":
