@@ -98,7 +98,8 @@ lsa_status lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, int32_t B, 
  * chunk order.  The set is unique, so the output is bit-exact.
  *
  *  logits     device int32 [R][C]   (any int32 values)
- *  R >= 1, 1 <= C <= 65536, 1 <= k <= C
+ *  R >= 1, 1 <= C <= 2^30, 1 <= k <= C (rows up to 65536 chunks keep their
+ *  keys in registers; longer ones stream from memory in every pass)
  *  chunk_ids  device int32 [R][k]   output, ascending within each row
  *  stream     HIP stream
  */
@@ -123,7 +124,7 @@ lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t 
  * integer logit whose score does not exceed s.
  *
  *  logits      device int32 [R][C]
- *  R >= 1, 1 <= C <= 65536, 1 <= k_max <= C
+ *  R >= 1, 1 <= C <= 2^30, 1 <= k_max <= C
  *  chunk_ids   device int32 [R][k_max] output
  *  counts      device int32 [R] output, chunks kept per row (0..k_max)
  */
@@ -149,7 +150,7 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
  *  chunk_ids   device int32 [B][k]
  *  counts      device int32 [B] entries in use, or NULL (all k)
  *  ctx_len     device int32 [B]
- *  B >= 1, 1 <= k <= 1024 (k*64 <= 65536), k_tok >= 1
+ *  B >= 1, k >= 1 with k*64 <= 2^30, k_tok >= 1
  *  tok         device int32 [B][k_tok] output: list positions
  *  tok_counts  device int32 [B] output: positions kept per request
  * All pointers need 4-byte alignment.

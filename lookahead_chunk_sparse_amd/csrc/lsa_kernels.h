@@ -14,7 +14,8 @@ hipError_t launch_index_score(const int8_t* q_idx, const int8_t* k_idx, int B, i
 
 // ---- top-k chunk selection ----
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkMaxC = 65536;
+constexpr int kTopkRegisterMaxC = 65536;  // longer rows take the streaming kernel
+constexpr int kTopkMaxC = 1 << 30;
 // counts == nullptr: top-k; else keep logits > thr, at most k, counts[r] = kept
 hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
                        hipStream_t stream);

@@ -26,6 +26,7 @@
 // scores over the list positions of the recalled chunks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "lsa_kernels.h"
 
@@ -52,6 +53,49 @@ constexpr int kBins = 1 << kDigitBits;
 // whose keys share a bin hit kCopies different words (scores crowd into a
 // few bins, and same-word LDS atomics serialise).
 constexpr int kCopies = 16;
+
+// After a histogram pass (and its barrier): sums the copies of every bin
+// and picks the digit holding the need-th largest key of the bucket;
+// sm_pick = {digit, keys still needed within it}.  Ends with a barrier.
+__device__ inline void pick_digit(const int* sm_hist, int* sm_tot, int* sm_pick, int tid, int lane, int wave,
+                                  int need) {
+    {
+        // every thread sums 4 copies of bin tid/4; 4 neighbouring lanes
+        // complete the bin
+        static_assert(kThreads == 4 * kBins && kCopies == 16, "copy reduction layout");
+        const int4 v = *reinterpret_cast<const int4*>(&sm_hist[4 * tid]);
+        int t = (v.x + v.y) + (v.z + v.w);
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        if ((tid & 3) == 0) sm_tot[tid >> 2] = t;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // lane l holds bins 4l..4l+3; exclusive suffix sum over lanes
+        int h[4], sl = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = sm_tot[4 * lane + j];
+            sl += h[j];
+        }
+        int suf = sl;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_down(suf, off);
+            if (lane + off < 64) suf += u;
+        }
+        int above = suf - sl;  // keys of the bucket in higher digits
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            if (above < need && need <= above + h[j]) {  // exactly one (lane, j) matches
+                sm_pick[0] = 4 * lane + j;
+                sm_pick[1] = need - above;
+            }
+            above += h[j];
+        }
+    }
+    __syncthreads();
+}
 
 // Order-preserving unsigned key of a float score: equal values give equal
 // keys (-0 is taken as +0), larger values larger keys.  NaN is not a score.
@@ -204,42 +248,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             }
         }
         __syncthreads();
-        {
-            // every thread sums 4 copies of bin tid/4; 4 neighbouring lanes
-            // complete the bin
-            static_assert(kThreads == 4 * kBins && kCopies == 16, "copy reduction layout");
-            const int4 v = *reinterpret_cast<const int4*>(&sm_hist[4 * tid]);
-            int t = (v.x + v.y) + (v.z + v.w);
-            t += __shfl_xor(t, 1);
-            t += __shfl_xor(t, 2);
-            if ((tid & 3) == 0) sm_tot[tid >> 2] = t;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane l holds bins 4l..4l+3; exclusive suffix sum over lanes
-            int h[4], sl = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                h[j] = sm_tot[4 * lane + j];
-                sl += h[j];
-            }
-            int suf = sl;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int u = __shfl_down(suf, off);
-                if (lane + off < 64) suf += u;
-            }
-            int above = suf - sl;  // keys of the bucket in higher digits
-#pragma unroll
-            for (int j = 3; j >= 0; --j) {
-                if (above < need && need <= above + h[j]) {  // exactly one (lane, j) matches
-                    sm_pick[0] = 4 * lane + j;
-                    sm_pick[1] = need - above;
-                }
-                above += h[j];
-            }
-        }
-        __syncthreads();
+        pick_digit(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
         prefix = (prefix << w) | (uint64_t)sm_pick[0];
         need = sm_pick[1];
     }
@@ -284,8 +293,186 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
 }
 
+// Rows too long for the keys to stay in registers (more than 64 per
+// thread): the same select, streaming the row from memory in every phase
+// instead (it stays in L2 between phases).  Wave w owns positions
+// [64*S*w, 64*S*(w+1)), S = slots per wave; slot e of lane l is position
+// 64*S*w + 64e + l, loaded in batches of kBatch slots (clamped,
+// unconditional loads issued before use).
+constexpr int kBatch = 8;
+
+template <bool TOK>
+__global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
+    __shared__ int sm_i[kWaves];
+    __shared__ int sm_j[kWaves];
+    __shared__ int sm_avail[kWaves];
+    __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
+    __shared__ __align__(16) int sm_hist[kBins * kCopies];  // [bin][copy]
+    __shared__ int sm_tot[kBins];
+    __shared__ int sm_pick[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int C = a.C, k = a.k;
+    int32_t* dst = a.out + (int64_t)blockIdx.x * k;
+    const int S = (C + 64 * kWaves - 1) / (64 * kWaves);
+    const int wbase = wave * 64 * S;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    const float* srow = TOK ? a.scores + (int64_t)blockIdx.x * C : nullptr;
+    const int32_t* lrow = TOK ? nullptr : a.logits + (int64_t)blockIdx.x * C;
+    const int32_t* ids = TOK ? a.list_ids + (int64_t)blockIdx.x * a.n_list : nullptr;
+    int kb = 0;
+    int64_t ctx = 0;
+    if constexpr (TOK) {
+        kb = a.n_list;
+        if (a.list_counts) {
+            const int cnt = a.list_counts[blockIdx.x];
+            kb = cnt < 0 ? 0 : cnt > a.n_list ? a.n_list : cnt;
+        }
+        ctx = a.ctx[blockIdx.x];
+    }
+    // body(e, key, ok) for every slot e of this wave, in slot order
+    auto for_each_slot = [&](auto&& body) {
+        for (int e0 = 0; e0 < S; e0 += kBatch) {
+            uint32_t key[kBatch];
+            bool ok[kBatch];
+            if constexpr (TOK) {
+                float v[kBatch];
+                int32_t cid[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int p = wbase + 64 * (e0 + u) + lane;
+                    v[u] = srow[p < C ? p : C - 1];
+                    const int j = wave * S + e0 + u;  // list entry of the slot (position 64j + lane)
+                    cid[u] = ids[j < a.n_list ? j : a.n_list - 1];
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int j = wave * S + e0 + u;
+                    ok[u] = e0 + u < S && j < kb && (int64_t)cid[u] * kChunkTokens + lane < ctx;
+                    key[u] = ok[u] ? score_key(v[u]) : 0u;
+                }
+            } else {
+                int32_t v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int p = wbase + 64 * (e0 + u) + lane;
+                    v[u] = lrow[p < C ? p : C - 1];
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    ok[u] = e0 + u < S && wbase + 64 * (e0 + u) + lane < C;
+                    key[u] = (uint32_t)v[u] ^ 0x80000000u;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (e0 + u < S) body(e0 + u, key[u], ok[u]);  // wave-uniform condition
+        }
+    };
+
+    // --- range and keep count ---
+    const bool capped = TOK || a.counts != nullptr;
+    const uint32_t tkey = TOK ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+    int avail = 0;
+    for_each_slot([&](int, uint32_t key, bool ok) {
+        if (ok) {
+            lmin = min(lmin, key);
+            lmax = max(lmax, key);
+        }
+        if (capped) avail += __popcll(__ballot(ok && (TOK || key > tkey)));
+    });
+    lmin = wave_min(lmin);
+    lmax = wave_max(lmax);
+    if (lane == 0) {
+        sm_min[wave] = lmin;
+        sm_max[wave] = lmax;
+        sm_avail[wave] = avail;
+    }
+    __syncthreads();
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    avail = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        kmin = min(kmin, sm_min[w]);
+        kmax = max(kmax, sm_max[w]);
+        avail += sm_avail[w];
+    }
+    int kk = k;
+    if (capped) {
+        kk = avail < k ? avail : k;
+        if (tid == 0) a.counts[blockIdx.x] = kk;
+        for (int j = kk + tid; j < k; j += kThreads) dst[j] = -1;
+        if (kk == 0) return;  // uniform
+    }
+
+    // --- radix select on key - kmin, 8 bits per pass ---
+    const uint32_t range = kmax - kmin;
+    const int nb = range == 0u ? 0 : 32 - __builtin_clz(range);
+    uint64_t prefix = 0;
+    int need = kk;
+    const int copy = lane % kCopies;
+    for (int hi = nb; hi > 0; hi -= kDigitBits) {
+        const int w = hi < kDigitBits ? hi : kDigitBits;
+        const int sh = hi - w;
+        for (int j = tid; j < kBins * kCopies; j += kThreads) sm_hist[j] = 0;
+        __syncthreads();
+        for_each_slot([&](int, uint32_t key, bool ok) {
+            const uint64_t r = key - kmin;
+            if (ok && (r >> hi) == prefix) atomicAdd(&sm_hist[(int)((r >> sh) & ((1u << w) - 1u)) * kCopies + copy], 1);
+        });
+        __syncthreads();
+        pick_digit(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
+        prefix = (prefix << w) | (uint64_t)sm_pick[0];
+        need = sm_pick[1];
+    }
+    const uint32_t vstar = kmin + (uint32_t)prefix;
+
+    // --- ordered compaction ---
+    int n_gt = 0, n_eq = 0;
+    for_each_slot([&](int, uint32_t key, bool ok) {
+        n_gt += __popcll(__ballot(ok && key > vstar));
+        n_eq += __popcll(__ballot(ok && key == vstar));
+    });
+    if (lane == 0) {
+        sm_i[wave] = n_gt;
+        sm_j[wave] = n_eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0;
+    for (int w = 0; w < wave; ++w) {
+        gt_before += sm_i[w];
+        eq_before += sm_j[w];
+    }
+    int pos = gt_before + (eq_before < need ? eq_before : need);
+    int eq_seen = eq_before;
+    for_each_slot([&](int e, uint32_t key, bool ok) {
+        const bool gt = ok && key > vstar;
+        const bool eq = ok && key == vstar;
+        const uint64_t eqm = __ballot(eq);
+        const bool take = gt || (eq && eq_seen + __popcll(eqm & below) < need);
+        const uint64_t tm = __ballot(take);
+        const int p = pos + __popcll(tm & below);
+        if (take && p < kk) dst[p] = wbase + 64 * e + lane;  // p < kk by construction
+        pos += __popcll(tm);
+        eq_seen += __popcll(eqm);
+    });
+}
+
+// Rows longer than this many positions stream from memory (LSA_TOPK_STREAM_MIN_C,
+// read per call, lowers the bound for testing and tuning).
+int stream_min_c() {
+    const char* e = getenv("LSA_TOPK_STREAM_MIN_C");
+    const int v = e ? atoi(e) : 0;
+    return v > 0 ? v : kTopkRegisterMaxC + 1;
+}
+
 template <bool TOK>
 hipError_t launch(const TopkArgs& a, int R, hipStream_t stream) {
+    if (a.C >= stream_min_c()) {
+        hipLaunchKernelGGL((topk_stream_kernel<TOK>), dim3((unsigned)R), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
     const int kpt = (a.C + kThreads - 1) / kThreads;
     const dim3 grid((unsigned)R), block(kThreads);
     if (kpt <= 1) hipLaunchKernelGGL((topk_kernel<1, TOK>), grid, block, 0, stream, a);

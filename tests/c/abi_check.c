@@ -39,7 +39,8 @@ int main(void) {
                   LSA_ERR_INVALID_ARGUMENT);
     bad += expect("pool assign P", lsa_pool_assign(bogus, bogus, 4, bogus, 1, 4, 7, bogus, bogus, NULL),
                   LSA_ERR_INVALID_ARGUMENT);
-    bad += expect("token top-k k", lsa_topk_tokens(bogus, bogus, NULL, bogus, 2, 1025, 8, bogus, bogus, NULL),
+    bad += expect("token top-k k", lsa_topk_tokens(bogus, bogus, NULL, bogus, 2, (1 << 24) + 1, 8, bogus, bogus,
+                                                                   NULL),
                   LSA_ERR_UNSUPPORTED);
     bad += expect("token attend tok", lsa_gather_attend_tokens(bogus, bogus, 4, bogus, NULL, NULL, bogus, NULL, NULL,
                                                                128, NULL, NULL, 0, 2, 64, 8, 128, 4, 0.1f, NULL, 0, 1,

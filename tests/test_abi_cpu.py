@@ -74,7 +74,7 @@ def test_topk_validation(lib):
     assert f(BOGUS, 1, 8, 0, BOGUS, 0) == 1 and "k=0" in _err(lib)
     assert f(BOGUS, 1, 8, 9, BOGUS, 0) == 1
     assert f(BOGUS, 0, 8, 1, BOGUS, 0) == 1
-    assert f(BOGUS, 1, 65537, 1, BOGUS, 0) == 2
+    assert f(BOGUS, 1, (1 << 30) + 1, 1, BOGUS, 0) == 2
 
 
 def test_threshold_validation(lib):
@@ -83,7 +83,7 @@ def test_threshold_validation(lib):
     assert f(BOGUS, 1, 8, 0, 2, BOGUS, 0, 0) == 1 and "counts" in _err(lib)
     assert f(BOGUS, 1, 8, 0, 0, BOGUS, BOGUS, 0) == 1 and "k_max=0" in _err(lib)
     assert f(BOGUS, 1, 8, 0, 9, BOGUS, BOGUS, 0) == 1
-    assert f(BOGUS, 1, 65537, 0, 1, BOGUS, BOGUS, 0) == 2
+    assert f(BOGUS, 1, (1 << 30) + 1, 0, 1, BOGUS, BOGUS, 0) == 2
 
 
 def test_attend_validation(lsa, lib):
@@ -122,7 +122,7 @@ def test_token_stage_validation(lib):
     assert f(0, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1
     assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, 0, 0) == 1 and "tok_counts" in _err(lib)
     assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 0, BOGUS, BOGUS, 0) == 1 and "k_tok=0" in _err(lib)
-    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 1025, 8, BOGUS, BOGUS, 0) == 2 and "k <= 1024" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, (1 << 24) + 1, 8, BOGUS, BOGUS, 0) == 2 and "k <= 16777216" in _err(lib)
     assert f(BOGUS + 2, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1 and "alignment" in _err(lib)
     g = lib.lsa_gather_attend_tokens
     # q, kv, C, ids, slots, counts, ctx, tok, tok_counts, k_tok, seg, seg_len, S_max, B, Hq, Hkv, d, k, scale,

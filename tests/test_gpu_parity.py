@@ -144,6 +144,32 @@ def test_topk_large_rows(lsa, oracle_lib, synth_lib, C):
         assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (C, k)
 
 
+@pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes"])
+@pytest.mark.parametrize("C", [1, 65, 1025, 7813])
+def test_topk_streaming_parity(lsa, oracle_lib, synth_lib, monkeypatch, kind, C):
+    """The streaming kernel (rows read from memory in every pass), forced on
+    rows that would otherwise keep their keys in registers."""
+    monkeypatch.setenv("LSA_TOPK_STREAM_MIN_C", "1")
+    rows = _rows(synth_lib, kind, 2, C, seed=C + 50)
+    dl = to_dev(rows)
+    for k in sorted({1, C, max(1, C // 7), max(1, C - 1)}):
+        got = lsa.lsa_topk_chunks(dl, k).cpu().numpy()
+        assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (kind, C, k)
+    for k_max, thr in ((max(1, C // 3), 0), (C, -5)):
+        ids, counts = lsa.lsa_threshold_chunks(dl, k_max, thr)
+        ref_ids, ref_counts = oracle_lib.threshold_chunks(rows.astype(np.int64), k_max, thr)
+        assert np.array_equal(counts.cpu().numpy(), ref_counts) and np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
+def test_topk_rows_beyond_registers(lsa, oracle_lib, synth_lib):
+    """A row of 100,000 chunks: longer than the register-resident kernel takes."""
+    C = 100000
+    rows = _rows(synth_lib, "narrow", 1, C, seed=7)
+    for k in (1, 10000):
+        got = lsa.lsa_topk_chunks(to_dev(rows), k).cpu().numpy()
+        assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), k
+
+
 @pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes", "none", "all"])
 @pytest.mark.parametrize("C", [1, 64, 1000, 2048, 16384])
 def test_threshold_parity(lsa, oracle_lib, synth_lib, kind, C):
@@ -335,6 +361,35 @@ def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
         ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=cn)
         assert np.array_equal(tc.cpu().numpy(), rc), (B, C, k, k_tok)
         assert np.array_equal(tok.cpu().numpy(), ref), (B, C, k, k_tok)
+
+
+@pytest.mark.parametrize("B,C,k,k_tok", [(4, 12, 5, 7), (3, 64, 40, 600), (4, 2048, 276, 2048)])
+def test_topk_tokens_streaming_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_tok):
+    """Token selection through the streaming kernel, forced on short lists."""
+    monkeypatch.setenv("LSA_TOPK_STREAM_MIN_C", "1")
+    scores = _token_scores(synth_lib, B, k * 64, seed=k + 1)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4030 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    ctx[0] = ids[0, -1] * 64 + 17
+    counts = np.full(B, k, dtype=np.int32)
+    counts[1] = max(1, k - 3)
+    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, counts=to_dev(counts))
+    ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=counts)
+    assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref)
+
+
+def test_topk_tokens_1m_recall(lsa, oracle_lib, synth_lib):
+    """The 1M workload's recall (1638 chunks = 104,832 token positions):
+    beyond the register-resident kernel, so the streaming kernel runs."""
+    B, C, k, k_tok = 2, 16384, 1638, 2048
+    scores = _token_scores(synth_lib, B, k * 64, seed=11)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4040 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.array([C * 64, ids[1, -1] * 64 + 5], dtype=np.int32)
+    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok)
+    ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok)
+    assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref)
 
 
 TOKEN_CASES = [
