@@ -272,10 +272,11 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     float l_run = 0.f;        // this lane's share of the running sum of head n
 
     // The workgroup's list entries (K tile offset, valid tokens, source) are
-    // staged in LDS, up to kListCache entries at a time, so computing a
-    // prefetch address never waits behind the K/V loads in flight.  Entry j
-    // < kb is gathered chunk j; entry kb + m is block m of the segment
-    // (flag kSegBit in sm_nv).  Offsets, not pointers, are staged: addresses
+    // staged in LDS, up to kListCache entries at a time (TOK: the row index
+    // of every token of up to kTokCache blocks), so computing a prefetch
+    // address never waits behind the K/V loads in flight.  Entry j < n_main
+    // is gathered chunk j (TOK: block j of the token list); entry n_main + m
+    // is block m of the segment (flag kSegBit in sm_nv).  Offsets, not pointers, are staged: addresses
     // formed from the kernel's own buffer arguments stay in the global
     // address space, whose loads only count against vmcnt.
     constexpr int kSegBit = 1 << 16;
@@ -291,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     // TOK: the request's list (chunk ids, store positions) staged in LDS once
     // when it fits; the staging of every round then looks positions up there
     constexpr int kTokPerThread = kTokCache * kChunkTokens / kThreads;
+    static_assert(kTokCache * kChunkTokens % kThreads == 0, "whole staging rounds per thread");
     constexpr int kIdCache = 1024;
     __shared__ int sm_cid[TOK ? kIdCache : 1];
     __shared__ int sm_pos[TOK ? kIdCache : 1];
