@@ -205,9 +205,9 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *             attended in the same softmax as the chunks -- the local
  *             sliding window and the freshly decoded tokens the pages always
  *             keep in GPU memory (paperlayer.ai summary, 2.1 Architecture:
- *             recalled entries are combined with the non-offloadable
- *             sliding-window KV; 3 Experiments / Experimental Setup: the
- *             local 8K / decoded window is retained).  Its tokens are not
+ *             the recalled chunks join the local window's KV, which is never
+ *             offloaded; 3 Experiments / Experimental Setup: the local 8K /
+ *             decoded window is retained).  Its tokens are not
  *             chunk tokens: ctx_len bounds only the chunks, so a caller
  *             passes the length of the offloadable history there.
  *  seg_len    device int32 [B]: tokens of the segment in use (<= S_max)

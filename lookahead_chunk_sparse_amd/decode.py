@@ -13,7 +13,7 @@ Two placements of the K/V:
   * Host tier (lag 1): the whole K/V lives in pinned host memory; the chunks
     of selection i are copied into an HBM pool on a side stream while interval
     i decodes with selection i-1 (the handbook page's asynchronous prefetch;
-    the summary's eviction of non-recalled entries to CPU), so the copy
+    in the summary, chunks not recalled leave GPU memory for the CPU), so the copy
     overlaps attention.  Two pool buffers alternate; the first interval waits
     for its own fetch.  The copy is either a device-side gather that reads
     the selected ids on the GPU (fetch="pull", the default: no host round

@@ -1,8 +1,8 @@
 """The five decode workloads and how their synthetic inputs are assembled.
 
 Shapes follow the pages' DeepSeek-V4 GQA description (64 query heads, 8 KV
-heads, head dim 128; sergiiob.dev handbook page, "DeepSeek-V4's specific GQA
-implementation") and the retention budgets the pages report (13.5% average
+heads, head dim 128; sergiiob.dev handbook page, section "Grouped Query
+Attention (GQA) vs. Multi-Head Attention (MHA)") and the retention budgets the pages report (13.5% average
 footprint, 10% at 500K and 1M; paperlayer.ai summary, Abstract and
 "3 Experiments / Main Results").  The evaluation suites the pages measure on
 (LongBench-v2, LongMemEval, RULER, MRCR) are not available; these seeded
