@@ -369,8 +369,9 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
         return statistics.mean(a.elapsed_time(b) for a, b in evs)
 
     topk_ms = timed(lambda j: lsa_topk_tokens(pool[j % n_pool], ids, dec.ctx_len, k_tok, tok=dec.tok,
-                                              tok_counts=dec.tok_counts))
-    lsa_topk_tokens(pool[0], ids, dec.ctx_len, k_tok, tok=dec.tok, tok_counts=dec.tok_counts)
+                                              tok_counts=dec.tok_counts, workspace=dec.tok_workspace))
+    lsa_topk_tokens(pool[0], ids, dec.ctx_len, k_tok, tok=dec.tok, tok_counts=dec.tok_counts,
+                    workspace=dec.tok_workspace)
     from lookahead_chunk_sparse_amd import lsa_gather_attend
     att_ms = timed(lambda j: lsa_gather_attend(q_all[j % n_q], dec.kv, ids, dec.ctx_len, dec.sm_scale,
                                                workspace=dec.workspace, n_split=dec.n_split, out=out, tok=dec.tok,

@@ -153,11 +153,25 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
  *  B >= 1, k >= 1 with k*64 <= 2^30, k_tok >= 1
  *  tok         device int32 [B][k_tok] output: list positions
  *  tok_counts  device int32 [B] output: positions kept per request
- * All pointers need 4-byte alignment.
+ *  workspace   device buffer of lsa_topk_tokens_workspace_size(B, k, k_tok)
+ *              bytes, 256-byte aligned, or NULL.  With it, lists of more
+ *              than 32768 positions are selected by many workgroups per
+ *              request: each slice of the
+ *              list keeps its own top k_tok, then the top k_tok of those
+ *              candidates are taken (the same set, since every position of
+ *              the request's top k_tok is in its slice's).  NULL: one
+ *              workgroup per request.  Scratch only; calls sharing a
+ *              workspace must not overlap in time.
+ * All other pointers need 4-byte alignment.
  */
 lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts,
                            const int32_t* ctx_len, int32_t B, int32_t k, int32_t k_tok, int32_t* tok,
-                           int32_t* tok_counts, hipStream_t stream);
+                           int32_t* tok_counts, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lsa_topk_tokens can use for these sizes: 0 when the
+ * select runs as one workgroup per request anyway, (size_t)-1 when the
+ * arguments are invalid. */
+size_t lsa_topk_tokens_workspace_size(int32_t B, int32_t k, int32_t k_tok);
 
 /*
  * Number of bytes of workspace lsa_gather_attend needs for these sizes and

@@ -12,7 +12,8 @@ from ._binding import (CHUNK_TOKENS, EXPORTS, LIB_PATH, LsaError, alloc_workspac
                        lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend, lsa_gather_attend_default_splits,
                        lsa_gather_attend_tokens,
                        lsa_gather_attend_workspace_size, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
-                       lsa_topk_chunks, lsa_topk_tokens)
+                       lsa_topk_chunks, lsa_topk_tokens, lsa_topk_tokens_workspace_size,
+                       alloc_topk_tokens_workspace)
 
 load_library()
 
@@ -20,4 +21,4 @@ __all__ = ["CHUNK_TOKENS", "EXPORTS", "LIB_PATH", "LsaError", "alloc_workspace",
            "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_gather_attend", "lsa_gather_attend_default_splits",
            "lsa_gather_attend_tokens",
            "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks",
-           "lsa_topk_tokens"]
+           "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "alloc_topk_tokens_workspace"]

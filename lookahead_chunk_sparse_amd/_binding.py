@@ -24,7 +24,7 @@ CHUNK_TOKENS = 64
 
 # Every symbol include/lsa.h declares.
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
-           "lsa_topk_tokens", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
+           "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
            "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
            "lsa_pool_assign")
 
@@ -62,8 +62,10 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz,
                                     i32, vp, vp]
     L.lsa_gather_attend.restype = ctypes.c_int
-    L.lsa_topk_tokens.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    L.lsa_topk_tokens.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.lsa_topk_tokens.restype = ctypes.c_int
+    L.lsa_topk_tokens_workspace_size.argtypes = [i32, i32, i32]
+    L.lsa_topk_tokens_workspace_size.restype = sz
     L.lsa_gather_attend_tokens.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                            i32, f32, vp, sz, i32, vp, vp]
     L.lsa_gather_attend_tokens.restype = ctypes.c_int
@@ -149,11 +151,26 @@ def lsa_threshold_chunks(logits: torch.Tensor, k_max: int, logit_threshold: int 
     return chunk_ids, counts
 
 
+def lsa_topk_tokens_workspace_size(B: int, k: int, k_tok: int) -> int:
+    n = load_library().lsa_topk_tokens_workspace_size(B, k, k_tok)
+    if n == ctypes.c_size_t(-1).value:
+        raise LsaError(1, "invalid sizes for lsa_topk_tokens_workspace_size")
+    return int(n)
+
+
+def alloc_topk_tokens_workspace(B: int, k: int, k_tok: int, device="cuda"):
+    """A workspace tensor for lsa_topk_tokens (None when none is used)."""
+    n = lsa_topk_tokens_workspace_size(B, k, k_tok)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def lsa_topk_tokens(scores: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor, k_tok: int,
-                    counts: torch.Tensor | None = None, tok=None, tok_counts=None, stream=None):
+                    counts: torch.Tensor | None = None, tok=None, tok_counts=None, workspace="auto", stream=None):
     """scores fp32 [B][k*64] over the list positions of the recalled chunks
     chunk_ids int32 [B][k] -> (tok int32 [B][k_tok] ascending positions padded
-    with -1, tok_counts int32 [B])."""
+    with -1, tok_counts int32 [B]).  workspace: a tensor from
+    alloc_topk_tokens_workspace, None (one workgroup per request) or "auto"
+    (allocated here when one is used)."""
     _need(scores, torch.float32, "scores", 2)
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
     _need(ctx_len, torch.int32, "ctx_len", 1)
@@ -166,8 +183,11 @@ def lsa_topk_tokens(scores: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torc
         tok = torch.empty((B, k_tok), dtype=torch.int32, device=scores.device)
     if tok_counts is None:
         tok_counts = torch.empty(B, dtype=torch.int32, device=scores.device)
+    if isinstance(workspace, str):
+        workspace = alloc_topk_tokens_workspace(B, k, k_tok, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().lsa_topk_tokens(_ptr(scores), _ptr(chunk_ids), _ptr(counts), _ptr(ctx_len), B, k, k_tok,
-                                          _ptr(tok), _ptr(tok_counts), _stream(stream)))
+                                          _ptr(tok), _ptr(tok_counts), _ptr(workspace), ws_bytes, _stream(stream)))
     return tok, tok_counts
 
 

@@ -117,9 +117,14 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k) {
     return lsa::attend_default_splits(B, Hkv, k);
 }
 
+size_t lsa_topk_tokens_workspace_size(int32_t B, int32_t k, int32_t k_tok) {
+    if (B < 1 || k < 1 || k_tok < 1 || (int64_t)k * lsa::kChunkTokens > lsa::kTopkMaxC) return (size_t)-1;
+    return lsa::topk_tokens_workspace_bytes(B, k, k_tok);
+}
+
 lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts,
                            const int32_t* ctx_len, int32_t B, int32_t k, int32_t k_tok, int32_t* tok,
-                           int32_t* tok_counts, hipStream_t stream) {
+                           int32_t* tok_counts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!scores || !chunk_ids || !ctx_len || !tok || !tok_counts)
         return fail(LSA_ERR_INVALID_ARGUMENT, "scores, chunk_ids, ctx_len, tok and tok_counts are required");
     if (B < 1 || k < 1 || k_tok < 1)
@@ -132,7 +137,15 @@ lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const 
     if (!aligned(scores, 4) || !aligned(chunk_ids, 4) || !aligned(ctx_len, 4) || !aligned(tok, 4) ||
         !aligned(tok_counts, 4) || (counts && !aligned(counts, 4)))
         return fail(LSA_ERR_INVALID_ARGUMENT, "all pointers need 4-byte alignment");
-    hipError_t e = lsa::launch_topk_tokens(scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, stream);
+    if (workspace) {
+        const size_t need = lsa::topk_tokens_workspace_bytes(B, k, k_tok);
+        if (workspace_bytes < need)
+            return fail(LSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+        if (!aligned(workspace, 256)) return fail(LSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (need == 0) workspace = nullptr;  // no split for these sizes
+    }
+    hipError_t e = lsa::launch_topk_tokens(scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, workspace,
+                                           stream);
     if (e != hipSuccess) return hip_fail(e, "token top-k launch");
     return ok();
 }

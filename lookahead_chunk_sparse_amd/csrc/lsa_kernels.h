@@ -20,10 +20,18 @@ constexpr int kTopkMaxC = 1 << 30;
 hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
                        hipStream_t stream);
 // token stage: top k_tok of the usable list positions of each row's recalled
-// chunks by float score; ascending, -1 padded, tok_counts[r] = kept
+// chunks by float score; ascending, -1 padded, tok_counts[r] = kept.  With a
+// workspace (topk_tokens_workspace_bytes, when nonzero) long rows run as
+// slices + candidates over many workgroups per row.
+struct TopkSplit {
+    int slices;     // 0: no split
+    int slice_len;  // positions per slice, a multiple of 64
+};
+TopkSplit topk_tokens_split(int n_list, int k_tok);
+size_t topk_tokens_workspace_bytes(int R, int n_list, int k_tok);
 hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, const int32_t* list_counts,
                               const int32_t* ctx, int R, int n_list, int k_tok, int32_t* tok, int32_t* tok_counts,
-                              hipStream_t stream);
+                              void* workspace, hipStream_t stream);
 
 // ---- gathered GQA decode attention ----
 struct AttendArgs {

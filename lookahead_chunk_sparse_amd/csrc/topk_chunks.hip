@@ -104,29 +104,43 @@ __device__ inline uint32_t score_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One row per workgroup.  Three modes:
-//  * budget (counts == nullptr, !TOK): the first k of C int32 logits;
-//  * threshold (counts != nullptr, !TOK): the logits above thr, at most k;
-//    the row is padded with -1 and counts[row] = chunks kept;
-//  * tokens (TOK): float scores of the C = 64 * n_list list positions of a
+// One row (or row slice) per workgroup.  Modes:
+//  * kModeLogits, budget (counts == nullptr): the first k of C int32 logits;
+//  * kModeLogits, threshold (counts != nullptr): the logits above thr, at
+//    most k; the row is padded with -1 and counts[row] = chunks kept;
+//  * kModeTokens: float scores of the C = 64 * n_list list positions of a
 //    row's recalled chunks; only usable positions compete (entry j < the
 //    row's list count, context position ids[j]*64 + t < ctx); at most k are
-//    kept, -1 padding, counts[row] = kept.
+//    kept, -1 padding, counts[row] = kept;
+//  * kModeSlice: the same on slice s of the row (positions [s*L, s*L + L),
+//    L a multiple of 64), workgroup r*n_slices + s; the slice's top k go to
+//    the candidate arrays as (position, key), ascending, padded (-1, 0);
+//  * kModeCand: row r's n_slices*k candidates (key 0: none) in position
+//    order; the top k of them are written as positions, -1 padding,
+//    counts[row] = kept.
+// Slice + candidates give the tokens mode's result with many workgroups per
+// row: every position of the row's top k is in its slice's top k.
+enum : int { kModeLogits = 0, kModeTokens = 1, kModeSlice = 2, kModeCand = 3 };
+
 struct TopkArgs {
-    const int32_t* logits;      // [R][C] (budget / threshold)
-    const float* scores;        // [R][C] (tokens)
-    const int32_t* list_ids;    // [R][n_list] recalled chunk ids (tokens)
-    const int32_t* list_counts; // [R] entries in use, may be null (tokens)
-    const int32_t* ctx;         // [R] context length (tokens)
+    const int32_t* logits;      // [R][C] (logits)
+    const float* scores;        // [R][64 * n_list] (tokens, slice)
+    const int32_t* list_ids;    // [R][n_list] recalled chunk ids (tokens, slice)
+    const int32_t* list_counts; // [R] entries in use, may be null (tokens, slice)
+    const int32_t* ctx;         // [R] context length (tokens, slice)
     int n_list;
-    int C, k;
+    int C, k;                   // positions per workgroup's row (slice mode: the slice length L), kept
     int32_t thr;
-    int32_t* out;     // [R][k]
-    int32_t* counts;  // [R] or null (budget)
+    int32_t* out;               // [R][k] (logits, tokens, candidates)
+    int32_t* counts;            // [R] or null (logits budget)
+    int n_slices;               // slice, candidates
+    int32_t* cand_pos;          // [R][n_slices][k] positions (written by slice, read by candidates)
+    uint32_t* cand_key;         // [R][n_slices][k] keys, 0 = none
 };
 
-template <int KPT, bool TOK>
+template <int KPT, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
+    constexpr bool kScoreKeys = MODE != kModeLogits;  // key 0 marks a position that does not compete
     __shared__ int sm_i[kWaves];
     __shared__ int sm_j[kWaves];
     __shared__ int sm_avail[kWaves];
@@ -135,57 +149,89 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[2];  // digit chosen by the pass, keys still needed
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int C = a.C, k = a.k;
-    int32_t* dst = a.out + (int64_t)blockIdx.x * k;
+    const int k = a.k;
+    // the workgroup's row, slice and positions
+    const int row = MODE == kModeSlice ? (int)blockIdx.x / a.n_slices : (int)blockIdx.x;
+    const int slice = MODE == kModeSlice ? (int)blockIdx.x % a.n_slices : 0;
+    const int row_len = MODE == kModeSlice ? a.n_list * kChunkTokens
+                        : MODE == kModeCand ? a.n_slices * k : a.C;
+    const int off = MODE == kModeSlice ? slice * a.C : 0;  // first position of the slice
+    const int C = MODE == kModeSlice ? min(a.C, row_len - off) : row_len;  // positions here (may be <= 0 for a slice)
+    int32_t* dst = MODE == kModeSlice ? a.cand_pos + (int64_t)blockIdx.x * k : a.out + (int64_t)row * k;
+    uint32_t* dst_key = MODE == kModeSlice ? a.cand_key + (int64_t)blockIdx.x * k : nullptr;
     // wave w owns positions [w*64*KPT, (w+1)*64*KPT); slot e of lane l is
     // position w*64*KPT + 64*e + l, so every load instruction reads 64
     // consecutive positions
     const int wbase = wave * 64 * KPT;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < lane
 
-    // A position competes iff ok(e): in token mode key 0 marks the others (no
-    // float score maps to 0), otherwise the position must lie in the row.
+    // A position competes iff ok(e): with score keys, key 0 marks the others
+    // (no float score maps to 0); with logits the position must lie in the row.
     uint32_t key[KPT];
-    auto ok = [&](int e) { return TOK ? key[e] != 0u : wbase + 64 * e + lane < C; };
+    auto ok = [&](int e) { return kScoreKeys ? key[e] != 0u : wbase + 64 * e + lane < C; };
     // Loads are unconditional, from clamped in-bounds indices, and all issued
     // before any is used: loads under a branch each wait for their data.
-    if constexpr (TOK) {
-        // slot e of wave w is exactly list entry j = w*KPT + e (64 tokens)
-        const float* row = a.scores + (int64_t)blockIdx.x * C;
-        const int32_t* ids = a.list_ids + (int64_t)blockIdx.x * a.n_list;
+    if constexpr (MODE == kModeTokens || MODE == kModeSlice) {
+        // slot e of wave w is exactly list entry j = off/64 + w*KPT + e (64 tokens)
+        const float* srow = a.scores + (int64_t)row * row_len;
+        const int32_t* ids = a.list_ids + (int64_t)row * a.n_list;
         int kb = a.n_list;
         if (a.list_counts) {
-            const int cnt = a.list_counts[blockIdx.x];
+            const int cnt = a.list_counts[row];
             kb = cnt < 0 ? 0 : cnt > a.n_list ? a.n_list : cnt;
         }
-        const int64_t ctx = a.ctx[blockIdx.x];
+        const int64_t ctx = a.ctx[row];
+        const int j0 = off / kChunkTokens;
         // lane e < KPT loads the id of the wave's slot e (KPT <= 64)
-        const int jl = wave * KPT + lane;
+        const int jl = j0 + wave * KPT + lane;
         const int32_t cidv = ids[jl < a.n_list ? jl : a.n_list - 1];
         float sc[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int idx = wbase + 64 * e + lane;
-            sc[e] = row[idx < C ? idx : C - 1];
+            const int idx = wbase + 64 * e + lane;  // position off + idx of the row
+            sc[e] = srow[idx < C ? off + idx : row_len - 1];  // clamped into the row (never used then)
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int j = wave * KPT + e;
+            const int j = j0 + wave * KPT + e;
             const int32_t cid = __builtin_amdgcn_readlane(cidv, e);
-            const bool use = j < kb && (int64_t)cid * kChunkTokens + lane < ctx;
+            const bool use = wbase + 64 * e + lane < C && j < kb && (int64_t)cid * kChunkTokens + lane < ctx;
             key[e] = use ? score_key(sc[e]) : 0u;
         }
+    } else if constexpr (MODE == kModeCand) {
+        const uint32_t* krow = a.cand_key + (int64_t)row * C;
+        uint32_t kv[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int idx = wbase + 64 * e + lane;
+            kv[e] = krow[idx < C ? idx : C - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = wbase + 64 * e + lane < C ? kv[e] : 0u;
     } else {
-        const int32_t* row = a.logits + (int64_t)blockIdx.x * C;
+        const int32_t* lrow = a.logits + (int64_t)row * C;
         int32_t lg[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int idx = wbase + 64 * e + lane;
-            lg[e] = row[idx < C ? idx : C - 1];
+            lg[e] = lrow[idx < C ? idx : C - 1];
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) key[e] = ((uint32_t)lg[e] ^ 0x80000000u);  // positions >= C: never ok
     }
+    // the output of slot e taken at place p
+    auto emit = [&](int p, int e) {
+        const int idx = wbase + 64 * e + lane;
+        if constexpr (MODE == kModeSlice) {
+            dst[p] = off + idx;
+            dst_key[p] = key[e];
+        } else if constexpr (MODE == kModeCand) {
+            dst[p] = a.cand_pos[(int64_t)row * C + idx];
+        } else {
+            dst[p] = idx;
+        }
+    };
+
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
@@ -195,12 +241,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
     // keys that may be kept: all competing ones (budget, tokens) or those
     // above the threshold; counted per wave with the min / max
-    const bool capped = TOK || a.counts != nullptr;
+    const bool capped = kScoreKeys || a.counts != nullptr;
     int avail = 0;
     if (capped) {
-        const uint32_t tkey = TOK ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
+        const uint32_t tkey = kScoreKeys ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) avail += __popcll(__ballot(ok(e) && (TOK || key[e] > tkey)));
+        for (int e = 0; e < KPT; ++e) avail += __popcll(__ballot(ok(e) && (kScoreKeys || key[e] > tkey)));
     }
     lmin = wave_min(lmin);
     lmax = wave_max(lmax);
@@ -223,8 +269,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     int kk = k;
     if (capped) {
         kk = avail < k ? avail : k;
-        if (tid == 0) a.counts[blockIdx.x] = kk;
-        for (int j = kk + tid; j < k; j += kThreads) dst[j] = -1;
+        if (MODE != kModeSlice && tid == 0) a.counts[row] = kk;
+        for (int j = kk + tid; j < k; j += kThreads) {
+            dst[j] = -1;
+            if constexpr (MODE == kModeSlice) dst_key[j] = 0u;
+        }
         if (kk == 0) return;  // uniform: every thread saw the same sum
     }
 
@@ -233,12 +282,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     const int nb = range == 0u ? 0 : 32 - __builtin_clz(range);
     uint64_t prefix = 0;  // digits chosen so far, as the value of key - kmin above bit `hi`
     int need = kk;
+    const int copy = lane % kCopies;
     for (int hi = nb; hi > 0; hi -= kDigitBits) {
         const int w = hi < kDigitBits ? hi : kDigitBits;
         const int sh = hi - w;
         for (int j = tid; j < kBins * kCopies; j += kThreads) sm_hist[j] = 0;
         __syncthreads();
-        const int copy = lane % kCopies;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const uint64_t r = key[e] - kmin;
@@ -287,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         const int p = pos + __popcll(tm & below);
         // p < kk holds by construction (|{> v*}| + need == kk); the test
         // keeps every store inside the row even so.
-        if (take && p < kk) dst[p] = wbase + 64 * e + lane;
+        if (take && p < kk) emit(p, e);
         pos += __popcll(tm);
         eq_seen += __popcll(eqm);
     }
@@ -467,30 +516,61 @@ int stream_min_c() {
     return v > 0 ? v : kTopkRegisterMaxC + 1;
 }
 
-template <bool TOK>
-hipError_t launch(const TopkArgs& a, int R, hipStream_t stream) {
-    if (a.C >= stream_min_c()) {
-        hipLaunchKernelGGL((topk_stream_kernel<TOK>), dim3((unsigned)R), dim3(kThreads), 0, stream, a);
-        return hipGetLastError();
-    }
-    const int kpt = (a.C + kThreads - 1) / kThreads;
-    const dim3 grid((unsigned)R), block(kThreads);
-    if (kpt <= 1) hipLaunchKernelGGL((topk_kernel<1, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 2) hipLaunchKernelGGL((topk_kernel<2, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 4) hipLaunchKernelGGL((topk_kernel<4, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 8) hipLaunchKernelGGL((topk_kernel<8, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 12) hipLaunchKernelGGL((topk_kernel<12, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 16) hipLaunchKernelGGL((topk_kernel<16, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 20) hipLaunchKernelGGL((topk_kernel<20, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 24) hipLaunchKernelGGL((topk_kernel<24, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 32) hipLaunchKernelGGL((topk_kernel<32, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 48) hipLaunchKernelGGL((topk_kernel<48, TOK>), grid, block, 0, stream, a);
-    else if (kpt <= 64) hipLaunchKernelGGL((topk_kernel<64, TOK>), grid, block, 0, stream, a);
+template <int MODE>
+hipError_t launch_mode(const TopkArgs& a, int grid, int positions, hipStream_t stream) {
+    const int kpt = (positions + kThreads - 1) / kThreads;
+    const dim3 g((unsigned)grid), block(kThreads);
+    if (kpt <= 1) hipLaunchKernelGGL((topk_kernel<1, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 2) hipLaunchKernelGGL((topk_kernel<2, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 4) hipLaunchKernelGGL((topk_kernel<4, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 8) hipLaunchKernelGGL((topk_kernel<8, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 12) hipLaunchKernelGGL((topk_kernel<12, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 16) hipLaunchKernelGGL((topk_kernel<16, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 20) hipLaunchKernelGGL((topk_kernel<20, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 24) hipLaunchKernelGGL((topk_kernel<24, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 32) hipLaunchKernelGGL((topk_kernel<32, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 48) hipLaunchKernelGGL((topk_kernel<48, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 64) hipLaunchKernelGGL((topk_kernel<64, MODE>), g, block, 0, stream, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
+
+// Split of a token row of 64*n_list positions into slices for the
+// slice + candidates path, for rows of more than 32768 positions (measured:
+// at 17,664 positions one workgroup per row is faster, 19.5 against 23.8 us
+// for 16 rows; at 50,048 the split takes 36 against 73 us, at 104,832 43
+// against 165 us); LSA_TOPK_SPLIT_MIN_N, read per call, lowers the bound for
+// testing.  About n / (2 k_tok) slices (at most 16), each a multiple of 64
+// positions; none (slices = 0) when that gives fewer than 2 or the slices or
+// candidates would not fit the register-resident kernel.
+TopkSplit topk_tokens_split(int n_list, int k_tok) {
+    TopkSplit sp{0, 0};
+    const int64_t n = (int64_t)n_list * kChunkTokens;
+    const char* env = getenv("LSA_TOPK_SPLIT_MIN_N");
+    const int64_t min_n = env && atoi(env) > 0 ? atoi(env) : 2 * kTopkRegisterMaxC / 4 + 1;  // 32769
+    if (n < min_n) return sp;
+    int64_t P = n / (2 * (int64_t)k_tok);
+    if (P > 16) P = 16;
+    if (P < 2) return sp;
+    int64_t L = (n + P - 1) / P;
+    L = (L + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
+    P = (n + L - 1) / L;
+    if (P < 2 || L > kTopkRegisterMaxC || P * k_tok > kTopkRegisterMaxC) return sp;
+    sp.slices = (int)P;
+    sp.slice_len = (int)L;
+    return sp;
+}
+
+size_t topk_tokens_workspace_bytes(int R, int n_list, int k_tok) {
+    const TopkSplit sp = topk_tokens_split(n_list, k_tok);
+    if (sp.slices == 0) return 0;
+    const size_t n = (size_t)R * sp.slices * k_tok;
+    return round256(n * sizeof(int32_t)) + n * sizeof(uint32_t);
+}
 
 hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chunk_ids, int32_t thr, int32_t* counts,
                        hipStream_t stream) {
@@ -501,12 +581,16 @@ hipError_t launch_topk(const int32_t* logits, int R, int C, int k, int32_t* chun
     a.thr = thr;
     a.out = chunk_ids;
     a.counts = counts;
-    return launch<false>(a, R, stream);
+    if (C >= stream_min_c()) {
+        hipLaunchKernelGGL((topk_stream_kernel<false>), dim3((unsigned)R), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    return launch_mode<kModeLogits>(a, R, C, stream);
 }
 
 hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, const int32_t* list_counts,
                               const int32_t* ctx, int R, int n_list, int k_tok, int32_t* tok, int32_t* tok_counts,
-                              hipStream_t stream) {
+                              void* workspace, hipStream_t stream) {
     TopkArgs a{};
     a.scores = scores;
     a.list_ids = list_ids;
@@ -517,7 +601,24 @@ hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, cons
     a.k = k_tok;
     a.out = tok;
     a.counts = tok_counts;
-    return launch<true>(a, R, stream);
+    const TopkSplit sp = workspace ? topk_tokens_split(n_list, k_tok) : TopkSplit{0, 0};
+    if (sp.slices > 0) {
+        // every slice's top k_tok, then the top k_tok of those candidates
+        char* w = static_cast<char*>(workspace);
+        const size_t n = (size_t)R * sp.slices * k_tok;
+        a.cand_pos = reinterpret_cast<int32_t*>(w);
+        a.cand_key = reinterpret_cast<uint32_t*>(w + round256(n * sizeof(int32_t)));
+        a.n_slices = sp.slices;
+        a.C = sp.slice_len;
+        hipError_t e = launch_mode<kModeSlice>(a, R * sp.slices, sp.slice_len, stream);
+        if (e != hipSuccess) return e;
+        return launch_mode<kModeCand>(a, R, sp.slices * k_tok, stream);
+    }
+    if (a.C >= stream_min_c()) {
+        hipLaunchKernelGGL((topk_stream_kernel<true>), dim3((unsigned)R), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    return launch_mode<kModeTokens>(a, R, a.C, stream);
 }
 
 }  // namespace lsa

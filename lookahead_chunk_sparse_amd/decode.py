@@ -51,8 +51,9 @@ import math
 
 import torch
 
-from ._binding import (CHUNK_TOKENS, alloc_workspace, lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_gather_attend,
-                       lsa_index_score, lsa_pool_assign, lsa_threshold_chunks, lsa_topk_chunks, lsa_topk_tokens)
+from ._binding import (CHUNK_TOKENS, alloc_topk_tokens_workspace, alloc_workspace, lsa_fetch_chunks,
+                       lsa_fetch_chunks_pull, lsa_gather_attend, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
+                       lsa_topk_chunks, lsa_topk_tokens)
 
 TAU = 64
 
@@ -130,6 +131,7 @@ class LsaDecoder:
         if self.k_tok:
             self.tok = torch.empty((B, self.k_tok), dtype=torch.int32, device=dev)
             self.tok_counts = torch.empty(B, dtype=torch.int32, device=dev)
+            self.tok_workspace = alloc_topk_tokens_workspace(B, k, self.k_tok, device=dev)
             entries = (self.k_tok + CHUNK_TOKENS - 1) // CHUNK_TOKENS
             self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, entries, n_split, device=dev)
         else:
@@ -178,7 +180,7 @@ class LsaDecoder:
             if token_scores is None:
                 raise ValueError("the token stage needs this step's token_scores")
             lsa_topk_tokens(token_scores, ids, self.ctx_len, self.k_tok, counts=self.sel_counts[sel % 2],
-                            tok=self.tok, tok_counts=self.tok_counts, stream=stream)
+                            tok=self.tok, tok_counts=self.tok_counts, workspace=self.tok_workspace, stream=stream)
             tok = dict(tok=self.tok, tok_counts=self.tok_counts)
         if self.lag:
             slots = self.sel_slots[sel % 2] if self.delta else self.slots

@@ -40,12 +40,16 @@ int main(void) {
     bad += expect("pool assign P", lsa_pool_assign(bogus, bogus, 4, bogus, 1, 4, 7, bogus, bogus, NULL),
                   LSA_ERR_INVALID_ARGUMENT);
     bad += expect("token top-k k", lsa_topk_tokens(bogus, bogus, NULL, bogus, 2, (1 << 24) + 1, 8, bogus, bogus,
-                                                                   NULL),
+                                                                   NULL, 0, NULL),
                   LSA_ERR_UNSUPPORTED);
     bad += expect("token attend tok", lsa_gather_attend_tokens(bogus, bogus, 4, bogus, NULL, NULL, bogus, NULL, NULL,
                                                                128, NULL, NULL, 0, 2, 64, 8, 128, 4, 0.1f, NULL, 0, 1,
                                                                bogus, NULL),
                   LSA_ERR_INVALID_ARGUMENT);
+    bad += expect("token top-k workspace", lsa_topk_tokens(bogus, bogus, NULL, bogus, 4, 1638, 2048, bogus, bogus,
+                                                             bogus, 64, NULL),
+                  LSA_ERR_WORKSPACE);
+    if (lsa_topk_tokens_workspace_size(4, 12, 500) != 0) { puts("FAIL token workspace size"); ++bad; }
     if (lsa_gather_attend_workspace_size(16, 64, 8, 128, 276, 1) != 0) { puts("FAIL workspace size"); ++bad; }
     if (lsa_gather_attend_default_splits(16, 8, 276) < 1) { puts("FAIL default splits"); ++bad; }
     if (strcmp(lsa_status_string(LSA_OK), "LSA_OK") != 0) { puts("FAIL status string"); ++bad; }

@@ -118,12 +118,17 @@ def test_attend_validation(lsa, lib):
 
 def test_token_stage_validation(lib):
     f = lib.lsa_topk_tokens
-    # scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, stream
-    assert f(0, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1
-    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, 0, 0) == 1 and "tok_counts" in _err(lib)
-    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 0, BOGUS, BOGUS, 0) == 1 and "k_tok=0" in _err(lib)
-    assert f(BOGUS, BOGUS, 0, BOGUS, 2, (1 << 24) + 1, 8, BOGUS, BOGUS, 0) == 2 and "k <= 16777216" in _err(lib)
-    assert f(BOGUS + 2, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0) == 1 and "alignment" in _err(lib)
+    # scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, workspace, workspace_bytes, stream
+    assert f(0, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0, 0, 0) == 1
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, 0, 0, 0, 0) == 1 and "tok_counts" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, 4, 0, BOGUS, BOGUS, 0, 0, 0) == 1 and "k_tok=0" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 2, (1 << 24) + 1, 8, BOGUS, BOGUS, 0, 0, 0) == 2 and "k <= 16777216" in _err(lib)
+    assert f(BOGUS + 2, BOGUS, 0, BOGUS, 2, 4, 8, BOGUS, BOGUS, 0, 0, 0) == 1 and "alignment" in _err(lib)
+    assert lib.lsa_topk_tokens_workspace_size(16, 276, 2048) == 0  # 17,664 positions: no split
+    need = lib.lsa_topk_tokens_workspace_size(4, 1638, 2048)      # the 1M recall: 16 slices
+    assert need > 0
+    assert f(BOGUS, BOGUS, 0, BOGUS, 4, 1638, 2048, BOGUS, BOGUS, BOGUS, need - 1, 0) == 3 and "workspace" in _err(lib)
+    assert f(BOGUS, BOGUS, 0, BOGUS, 4, 1638, 2048, BOGUS, BOGUS, BOGUS + 16, need, 0) == 3 and "256-byte" in _err(lib)
     g = lib.lsa_gather_attend_tokens
     # q, kv, C, ids, slots, counts, ctx, tok, tok_counts, k_tok, seg, seg_len, S_max, B, Hq, Hkv, d, k, scale,
     # ws, ws_bytes, n_split, out, stream

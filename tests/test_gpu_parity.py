@@ -344,8 +344,9 @@ def _token_scores(synth_lib, B, n, seed):
     (4, 2048, 276, 2048),  # the 128K recall, a 2048-token budget
     (2, 4096, 1024, 2048),  # the largest list: 65536 positions
 ])
-def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
+def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_tok):
     say("token top-k", B, C, k, k_tok)
+    monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")  # the slice + candidates path on every size it can split
     scores = _token_scores(synth_lib, B, k * 64, seed=k)
     ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4010 + b)))
                     for b in range(B)]).astype(np.int32)
@@ -356,11 +357,13 @@ def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
     counts = np.full(B, k, dtype=np.int32)
     counts[1] = max(1, k - 3)
     for cn in (None, counts):
-        tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok,
-                                      counts=None if cn is None else to_dev(cn))
         ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=cn)
-        assert np.array_equal(tc.cpu().numpy(), rc), (B, C, k, k_tok)
-        assert np.array_equal(tok.cpu().numpy(), ref), (B, C, k, k_tok)
+        # "auto": the slice + candidates path where the library splits; None: one workgroup per request
+        for ws in ("auto", None):
+            tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok,
+                                          counts=None if cn is None else to_dev(cn), workspace=ws)
+            assert np.array_equal(tc.cpu().numpy(), rc), (B, C, k, k_tok, ws)
+            assert np.array_equal(tok.cpu().numpy(), ref), (B, C, k, k_tok, ws)
 
 
 @pytest.mark.parametrize("B,C,k,k_tok", [(4, 12, 5, 7), (3, 64, 40, 600), (4, 2048, 276, 2048)])
@@ -374,22 +377,25 @@ def test_topk_tokens_streaming_parity(lsa, oracle_lib, synth_lib, monkeypatch, B
     ctx[0] = ids[0, -1] * 64 + 17
     counts = np.full(B, k, dtype=np.int32)
     counts[1] = max(1, k - 3)
-    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, counts=to_dev(counts))
+    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, counts=to_dev(counts),
+                                  workspace=None)  # no workspace: the streaming kernel, not the split
     ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=counts)
     assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref)
 
 
 def test_topk_tokens_1m_recall(lsa, oracle_lib, synth_lib):
     """The 1M workload's recall (1638 chunks = 104,832 token positions):
-    beyond the register-resident kernel, so the streaming kernel runs."""
+    beyond the register-resident kernel.  With a workspace it runs as 16
+    slices + candidates; without, the streaming kernel runs."""
     B, C, k, k_tok = 2, 16384, 1638, 2048
     scores = _token_scores(synth_lib, B, k * 64, seed=11)
     ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4040 + b)))
                     for b in range(B)]).astype(np.int32)
     ctx = np.array([C * 64, ids[1, -1] * 64 + 5], dtype=np.int32)
-    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok)
     ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok)
-    assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref)
+    for ws in ("auto", None):
+        tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, workspace=ws)
+        assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref), ws
 
 
 TOKEN_CASES = [
