@@ -5,14 +5,16 @@
 // practical ceiling beside the published peak.
 //
 // Each workgroup takes tiles t = blockIdx.x, +gridDim.x, ... and reads them
-// whole with 16-byte loads, UNROLL loads in flight per thread; the data is
-// XOR-folded into one word per thread so the loads stay live.
+// whole with 16-byte loads carrying the non-temporal hint (as the attention's
+// tile loads do), UNROLL loads in flight per thread; the data is XOR-folded
+// into one word per thread so the loads stay live.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
 
 constexpr int kThreads = 256;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 template <int UNROLL>
 __global__ __launch_bounds__(kThreads) void tile_read_kernel(const uint4* __restrict__ base,
@@ -26,7 +28,8 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(const uint4* __rest
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int i = o + u * kThreads;
-                v[u] = p[i < tile_u4 ? i : tile_u4 - 1];
+                v[u] = __builtin_bit_cast(
+                    uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + (i < tile_u4 ? i : tile_u4 - 1))));
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
