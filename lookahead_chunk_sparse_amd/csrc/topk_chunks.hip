@@ -9,16 +9,23 @@
 // (coalesced loads), as order-preserving unsigned keys (logit XOR 0x80000000),
 // offset by the row's smallest key so that only the bits spanning the row's
 // range remain (logits of both signs would otherwise differ in every bit).
-//  1. Radix select, 8 bits per pass from the top of the range: the keys of
-//     the current bucket are counted per digit into an LDS histogram
-//     (ds_add, 16 copies against same-word conflicts), then one wave finds,
-//     by a suffix scan over the 256 bins, the digit that holds the k-th
-//     largest key.  The result is that key v* and
-//     `need`, the number of keys equal to v* that belong to the selection.
+//  1. Radix select from the top of the range.  A pass counts the keys of the
+//     current bucket per 8-bit digit into an LDS histogram (ds_add, 16
+//     copies against same-word conflicts); one wave then finds, by a suffix
+//     scan over the 256 bins, the digit that holds the k-th largest key, and
+//     that digit's keys become the bucket.  Every pass over the registers
+//     costs the whole row's keys in VALU work on one CU, so once the bucket
+//     fits (8192 keys) it moves into LDS and later passes read only it; once
+//     it is down to 256 keys one wave decides the remaining bits one at a
+//     time from ballots (a bit of the k-th key is 1 iff at least `need` keys
+//     of the bucket have it set).  The result is that key v*, the number of
+//     keys equal to v*, and `need`, how many of those belong to the selection.
 //  2. Ordered compaction: keys > v* are taken; keys == v* are taken while
-//     their rank among equal keys, in index order, is below `need`.  Ranks
-//     in index order come from ballots within a wave (slot by slot) and from
-//     scans of the per-wave totals across waves, so the output is ascending.
+//     their rank among equal keys, in index order, is below `need` (all of
+//     them when need is their number, the common case: then simply the keys
+//     >= v*).  Ranks in index order come from ballots within a wave (slot by
+//     slot) and from scans of the per-wave totals across waves, so the output
+//     is ascending.
 //
 // The same select serves the token-level stage: after the chunk recall the
 // model's own token scores pick a fine-grained top-k among the recalled
@@ -54,17 +61,25 @@ constexpr int kBins = 1 << kDigitBits;
 // few bins, and same-word LDS atomics serialise).
 constexpr int kCopies = 16;
 
-// After a histogram pass (and its barrier): sums the copies of every bin
-// and picks the digit holding the need-th largest key of the bucket;
-// sm_pick = {digit, keys still needed within it}.  Ends with a barrier.
+// After a histogram pass (and its barrier): sums the COPIES copies of every
+// bin ([bin][copy] layout) and picks the digit holding the need-th largest
+// key of the bucket; sm_pick = {digit, keys still needed within it, keys in
+// it}.  Ends with a barrier.
+template <int COPIES>
 __device__ inline void pick_digit(const int* sm_hist, int* sm_tot, int* sm_pick, int tid, int lane, int wave,
                                   int need) {
     {
-        // every thread sums 4 copies of bin tid/4; 4 neighbouring lanes
-        // complete the bin
-        static_assert(kThreads == 4 * kBins && kCopies == 16, "copy reduction layout");
-        const int4 v = *reinterpret_cast<const int4*>(&sm_hist[4 * tid]);
-        int t = (v.x + v.y) + (v.z + v.w);
+        // every thread sums COPIES/4 copies of bin tid/4; 4 neighbouring
+        // lanes complete the bin
+        static_assert(kThreads == 4 * kBins && COPIES % 16 == 0, "copy reduction layout");
+        constexpr int kPer = COPIES / 4;
+        const int4* p = reinterpret_cast<const int4*>(&sm_hist[kPer * tid]);
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < kPer / 4; ++i) {
+            const int4 v = p[i];
+            t += (v.x + v.y) + (v.z + v.w);
+        }
         t += __shfl_xor(t, 1);
         t += __shfl_xor(t, 2);
         if ((tid & 3) == 0) sm_tot[tid >> 2] = t;
@@ -90,6 +105,7 @@ __device__ inline void pick_digit(const int* sm_hist, int* sm_tot, int* sm_pick,
             if (above < need && need <= above + h[j]) {  // exactly one (lane, j) matches
                 sm_pick[0] = 4 * lane + j;
                 sm_pick[1] = need - above;
+                sm_pick[2] = h[j];
             }
             above += h[j];
         }
@@ -138,6 +154,20 @@ struct TopkArgs {
     uint32_t* cand_key;         // [R][n_slices][k] keys, 0 = none
 };
 
+// A bucket of at most kListCap keys moves from registers into LDS; one of at
+// most kBallotMax keys is finished bit by bit by one wave.
+constexpr int kListCap = 8192;
+constexpr int kBallotMax = 256;
+constexpr int kBallotSlots = kBallotMax / 64;
+// The register kernel's histogram has one copy per lane: keys of one digit in
+// one load instruction then never share an LDS word.
+constexpr int kLaneCopies = 64;
+
+// Rank of this lane among the set bits of m below it.
+__device__ inline int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <int KPT, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     constexpr bool kScoreKeys = MODE != kModeLogits;  // key 0 marks a position that does not compete
@@ -145,10 +175,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int sm_j[kWaves];
     __shared__ int sm_avail[kWaves];
     __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
-    __shared__ __align__(16) int sm_hist[kBins * kCopies];  // [bin][copy]
+    __shared__ __align__(16) int sm_hist[kBins * kLaneCopies];  // [bin][copy]
     __shared__ int sm_tot[kBins];
-    __shared__ int sm_pick[2];  // digit chosen by the pass, keys still needed
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int sm_pick[3];  // digit chosen by a pass, keys still needed, keys in the digit
+    __shared__ uint32_t sm_list[2][kListCap];  // a bucket's keys as r (below), in no particular order
+    __shared__ int sm_cnt[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int k = a.k;
     // the workgroup's row, slice and positions
     const int row = MODE == kModeSlice ? (int)blockIdx.x / a.n_slices : (int)blockIdx.x;
@@ -163,14 +196,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     // position w*64*KPT + 64*e + l, so every load instruction reads 64
     // consecutive positions
     const int wbase = wave * 64 * KPT;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < lane
 
-    // A position competes iff ok(e): with score keys, key 0 marks the others
-    // (no float score maps to 0); with logits the position must lie in the row.
-    uint32_t key[KPT];
-    auto ok = [&](int e) { return kScoreKeys ? key[e] != 0u : wbase + 64 * e + lane < C; };
     // Loads are unconditional, from clamped in-bounds indices, and all issued
-    // before any is used: loads under a branch each wait for their data.
+    // before any is used; keys are formed without branches (a load whose
+    // only use sits under a branch moves into it and waits there).
+    uint32_t key[KPT];
     if constexpr (MODE == kModeTokens || MODE == kModeSlice) {
         // slot e of wave w is exactly list entry j = off/64 + w*KPT + e (64 tokens)
         const float* srow = a.scores + (int64_t)row * row_len;
@@ -182,6 +212,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         const int64_t ctx = a.ctx[row];
         const int j0 = off / kChunkTokens;
+        // entries of this workgroup in use: j0 <= j < jend (C is a multiple of 64)
+        const int jend = C > 0 ? min(kb, j0 + C / kChunkTokens) : 0;
         // lane e < KPT loads the id of the wave's slot e (KPT <= 64)
         const int jl = j0 + wave * KPT + lane;
         const int32_t cidv = ids[jl < a.n_list ? jl : a.n_list - 1];
@@ -193,60 +225,50 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
+            // tokens of entry j below the context length, 0 for an entry not in use
             const int j = j0 + wave * KPT + e;
-            const int32_t cid = __builtin_amdgcn_readlane(cidv, e);
-            const bool use = wbase + 64 * e + lane < C && j < kb && (int64_t)cid * kChunkTokens + lane < ctx;
-            key[e] = use ? score_key(sc[e]) : 0u;
+            const int64_t cid = __builtin_amdgcn_readlane(cidv, e);
+            const int64_t below_ctx = ctx - cid * kChunkTokens;
+            const int lim = j < jend ? (below_ctx < 0 ? 0 : below_ctx > kChunkTokens ? kChunkTokens : (int)below_ctx) : 0;
+            key[e] = score_key(sc[e]) & (0u - (uint32_t)(lane < lim));
         }
     } else if constexpr (MODE == kModeCand) {
         const uint32_t* krow = a.cand_key + (int64_t)row * C;
-        uint32_t kv[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int idx = wbase + 64 * e + lane;
-            kv[e] = krow[idx < C ? idx : C - 1];
+            key[e] = krow[idx < C ? idx : C - 1];
         }
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) key[e] = wbase + 64 * e + lane < C ? kv[e] : 0u;
+        for (int e = 0; e < KPT; ++e) key[e] &= 0u - (uint32_t)(wbase + 64 * e + lane < C);
     } else {
         const int32_t* lrow = a.logits + (int64_t)row * C;
-        int32_t lg[KPT];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int idx = wbase + 64 * e + lane;
-            lg[e] = lrow[idx < C ? idx : C - 1];
+            key[e] = (uint32_t)lrow[idx < C ? idx : C - 1] ^ 0x80000000u;  // positions >= C: made inert below
         }
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) key[e] = ((uint32_t)lg[e] ^ 0x80000000u);  // positions >= C: never ok
     }
-    // the output of slot e taken at place p
-    auto emit = [&](int p, int e) {
-        const int idx = wbase + 64 * e + lane;
-        if constexpr (MODE == kModeSlice) {
-            dst[p] = off + idx;
-            dst_key[p] = key[e];
-        } else if constexpr (MODE == kModeCand) {
-            dst[p] = a.cand_pos[(int64_t)row * C + idx];
-        } else {
-            dst[p] = idx;
-        }
-    };
 
-    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e)
-        if (ok(e)) {
-            lmin = min(lmin, key[e]);
-            lmax = max(lmax, key[e]);
-        }
-    // keys that may be kept: all competing ones (budget, tokens) or those
-    // above the threshold; counted per wave with the min / max
+    // --- range and keep count ---
+    // Score keys: the minimum is taken over key - 1, so that key 0 (not
+    // competing) wraps to the top and drops out; 1 is added back below.
     const bool capped = kScoreKeys || a.counts != nullptr;
+    const uint32_t tkey = kScoreKeys ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
     int avail = 0;
-    if (capped) {
-        const uint32_t tkey = kScoreKeys ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) avail += __popcll(__ballot(ok(e) && (kScoreKeys || key[e] > tkey)));
+    for (int e = 0; e < KPT; ++e) {
+        if constexpr (kScoreKeys) {
+            lmin = min(lmin, key[e] - 1u);
+            lmax = max(lmax, key[e]);
+            avail += __popcll(__ballot(key[e] != 0u));
+        } else {
+            const bool o = wbase + 64 * e + lane < C;
+            lmin = min(lmin, o ? key[e] : 0xFFFFFFFFu);
+            lmax = max(lmax, o ? key[e] : 0u);
+            if (capped) avail += __popcll(__ballot(o && key[e] > tkey));
+        }
     }
     lmin = wave_min(lmin);
     lmax = wave_max(lmax);
@@ -255,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         sm_max[wave] = lmax;
         sm_avail[wave] = avail;
     }
+    if (tid == 0) sm_cnt[0] = 0;
     __syncthreads();
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     avail = 0;
@@ -264,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         kmax = max(kmax, sm_max[w]);
         avail += sm_avail[w];
     }
+    if constexpr (kScoreKeys) kmin += 1u;  // (no competing key: avail == 0, unused)
 
     // --- how many to keep ---
     int kk = k;
@@ -276,69 +300,231 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         if (kk == 0) return;  // uniform: every thread saw the same sum
     }
+    const int n_ok = kScoreKeys ? avail : C;  // competing keys
 
-    // --- radix select on key - kmin, 8 bits per pass ---
+    // --- keys relative to the row minimum: r = key - kmin in [0, range] ---
+    // A score key that does not compete becomes 0xFFFFFFFF, above every r
+    // (range <= 0xFFFFFFFE as kmin >= 1), and every test below bounds r by
+    // range.  A logits position past the row gets r = 0, the smallest value,
+    // behind every real key of its value in position order: it is never
+    // selected (at most the C real keys are) and moves no pick (it only adds
+    // to the lowest bucket).
     const uint32_t range = kmax - kmin;
-    const int nb = range == 0u ? 0 : 32 - __builtin_clz(range);
-    uint64_t prefix = 0;  // digits chosen so far, as the value of key - kmin above bit `hi`
-    int need = kk;
-    const int copy = lane % kCopies;
-    for (int hi = nb; hi > 0; hi -= kDigitBits) {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        if constexpr (kScoreKeys)
+            key[e] = key[e] != 0u ? key[e] - kmin : 0xFFFFFFFFu;
+        else
+            key[e] = wbase + 64 * e + lane < C ? key[e] - kmin : 0u;
+    }
+    uint32_t* rr = key;
+
+    // --- radix select on r ---
+    // The bits of r* (the kk-th largest r) are decided from the top; the
+    // current bucket holds the keys that agree with r* on the decided bits
+    // (cnt keys, of which `need` are kept): r in [rstar, rstar + ub].
+    int hi = range == 0u ? 0 : 32 - __builtin_clz(range);  // bits [0, hi) of r* are undecided
+    if (kk == n_ok) hi = 0;  // every competing key is kept: r* = 0 will do
+    uint32_t rstar = 0;      // decided bits of r*, in place
+    int need = kk, cnt = n_ok;
+    int src = -1;            // the bucket is in registers (-1) or in sm_list[src]
+    auto bucket_ub = [&](int h) {  // r - rstar <= ub <=> r in the bucket (and r <= range)
+        const uint32_t span = h >= 32 ? 0xFFFFFFFFu : (1u << h) - 1u;
+        return min(span, range - rstar);
+    };
+    while (hi > 0) {
+        if (src >= 0 && cnt <= kBallotMax) {
+            // one wave decides the remaining bits, high to low: with c1 keys
+            // of the bucket having the bit set, the bit of r* is 1 iff
+            // need <= c1; the bucket keeps the keys that agree
+            if (wave == 0) {
+                const uint32_t* lst = sm_list[src];
+                const int ns = (cnt + 63) >> 6;  // occupied slots
+                uint32_t v[kBallotSlots];
+                uint64_t cand[kBallotSlots];
+#pragma unroll
+                for (int s = 0; s < kBallotSlots; ++s) {
+                    const int i = 64 * s + lane;
+                    v[s] = lst[i < cnt ? i : 0];
+                    cand[s] = __ballot(i < cnt);
+                }
+                uint32_t low = 0;
+                int nd = need;
+                for (int b = hi - 1; b >= 0; --b) {
+                    uint64_t one[kBallotSlots];
+                    int c1 = 0;
+#pragma unroll
+                    for (int s = 0; s < kBallotSlots; ++s) {
+                        one[s] = s < ns ? cand[s] & __ballot((v[s] >> b) & 1u) : 0ull;
+                        c1 += __popcll(one[s]);
+                    }
+                    if (nd <= c1) {
+                        low |= 1u << b;
+#pragma unroll
+                        for (int s = 0; s < kBallotSlots; ++s) cand[s] = one[s];
+                    } else {
+                        nd -= c1;
+#pragma unroll
+                        for (int s = 0; s < kBallotSlots; ++s) cand[s] &= ~one[s];
+                    }
+                }
+                int ceq = 0;
+#pragma unroll
+                for (int s = 0; s < kBallotSlots; ++s) ceq += __popcll(cand[s]);
+                if (lane == 0) {
+                    sm_pick[0] = (int)low;
+                    sm_pick[1] = nd;
+                    sm_pick[2] = ceq;
+                }
+            }
+            __syncthreads();
+            rstar |= (uint32_t)sm_pick[0];
+            need = sm_pick[1];
+            cnt = sm_pick[2];
+            break;
+        }
+        // one histogram pass over the next (up to) 8 bits
         const int w = hi < kDigitBits ? hi : kDigitBits;
         const int sh = hi - w;
-        for (int j = tid; j < kBins * kCopies; j += kThreads) sm_hist[j] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const uint64_t r = key[e] - kmin;
-            if (ok(e) && (r >> hi) == prefix) {
-                const int bin = (int)((r >> sh) & ((1u << w) - 1u));
-                atomicAdd(&sm_hist[bin * kCopies + copy], 1);
-            }
+        const uint32_t dmask = (1u << w) - 1u;
+        const int nxt = src < 0 ? 0 : 1 - src;  // list the next bucket may move to
+        {
+            int4* h4 = reinterpret_cast<int4*>(sm_hist);
+            for (int j = tid; j < kBins * kLaneCopies / 4; j += kThreads) h4[j] = make_int4(0, 0, 0, 0);
         }
         __syncthreads();
-        pick_digit(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
-        prefix = (prefix << w) | (uint64_t)sm_pick[0];
+        if (tid == 0) sm_cnt[nxt] = 0;  // ordered before its use by the barriers of pick_digit
+        if (src < 0) {
+            const uint32_t ub = bucket_ub(hi);
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const uint32_t d = rr[e] - rstar;
+                if (d <= ub) atomicAdd(&sm_hist[(int)(d >> sh) * kLaneCopies + lane], 1);
+            }
+        } else {
+            const uint32_t* lst = sm_list[src];
+            for (int i = tid; i < cnt; i += kThreads)
+                atomicAdd(&sm_hist[(int)((lst[i] >> sh) & dmask) * kLaneCopies + lane], 1);
+        }
+        __syncthreads();
+        pick_digit<kLaneCopies>(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
+        const uint32_t dg = (uint32_t)sm_pick[0];
+        const int cnt_in = cnt;
         need = sm_pick[1];
+        cnt = sm_pick[2];
+        rstar |= dg << sh;
+        hi = sh;
+        if (hi > 0 && cnt <= kListCap) {
+            // move the new bucket into sm_list[nxt]: per wave, one LDS atomic
+            // reserves the places of its keys (the bucket tests are
+            // recomputed rather than kept, to spare scalar registers)
+            uint32_t* out = sm_list[nxt];
+            if (src < 0) {
+                const uint32_t ub = bucket_ub(hi);
+                int n = 0;
+#pragma unroll
+                for (int e = 0; e < KPT; ++e) n += __popcll(__ballot(rr[e] - rstar <= ub));
+                int base = 0;
+                if (lane == 0 && n > 0) base = atomicAdd(&sm_cnt[nxt], n);
+                base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+                for (int e = 0; e < KPT; ++e) {
+                    const bool in = rr[e] - rstar <= ub;
+                    const uint64_t mk = __ballot(in);
+                    if (in) out[base + lanes_below(mk)] = rr[e];
+                    base += __popcll(mk);
+                }
+            } else {
+                const uint32_t* in = sm_list[src];
+                for (int i0 = 0; i0 < cnt_in; i0 += kThreads) {
+                    const int i = i0 + tid;
+                    const uint32_t r = in[i < cnt_in ? i : 0];
+                    const bool match = i < cnt_in && ((r >> sh) & dmask) == dg;
+                    const uint64_t mk = __ballot(match);
+                    int base = 0;
+                    if (lane == 0 && mk != 0) base = atomicAdd(&sm_cnt[nxt], __popcll(mk));
+                    base = __builtin_amdgcn_readfirstlane(base);
+                    if (match) out[base + lanes_below(mk)] = r;
+                }
+            }
+            src = nxt;
+            __syncthreads();
+        }
     }
-    const uint32_t vstar = kmin + (uint32_t)prefix;
+    // every key equal to r* is kept: the selection is exactly the keys >= r*
+    const bool all_eq = need == cnt;
 
     // --- ordered compaction ---
-    // Per wave: keys > v* and keys == v*; in position order the waves come
-    // one after the other, so exclusive scans over the wave totals give each
-    // wave the equal keys and the outputs before it.
-    int n_gt = 0, n_eq = 0;
+    // On r: ge <=> rstar <= r <= range, gt <=> rstar < r <= range, eq <=> r == rstar.
+    const uint32_t top = range - rstar;
+    auto ge = [&](int e) { return rr[e] - rstar <= top; };
+    auto gt = [&](int e) { return rr[e] - rstar - 1u < top; };
+    auto eq = [&](int e) { return rr[e] == rstar; };
+    // the output of slot e taken at place p
+    auto emit = [&](int p, int e) {
+        const int idx = wbase + 64 * e + lane;
+        if constexpr (MODE == kModeSlice) {
+            dst[p] = off + idx;
+            dst_key[p] = rr[e] + kmin;
+        } else if constexpr (MODE == kModeCand) {
+            dst[p] = a.cand_pos[(int64_t)row * C + idx];
+        } else {
+            dst[p] = idx;
+        }
+    };
+    // Per wave: keys taken (all_eq) or keys > r* and keys == r*; in position
+    // order the waves come one after the other, so exclusive scans over the
+    // wave totals give each wave the equal keys and the outputs before it.
+    int n_a = 0, n_b = 0;
+    if (all_eq) {
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        n_gt += __popcll(__ballot(ok(e) && key[e] > vstar));
-        n_eq += __popcll(__ballot(ok(e) && key[e] == vstar));
+        for (int e = 0; e < KPT; ++e) n_a += __popcll(__ballot(ge(e)));
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            n_a += __popcll(__ballot(gt(e)));
+            n_b += __popcll(__ballot(eq(e)));
+        }
     }
     if (lane == 0) {
-        sm_i[wave] = n_gt;
-        sm_j[wave] = n_eq;
+        sm_i[wave] = n_a;
+        sm_j[wave] = n_b;
     }
     __syncthreads();
-    int gt_before = 0, eq_before = 0;
+    int a_before = 0, b_before = 0;
     for (int w = 0; w < wave; ++w) {
-        gt_before += sm_i[w];
-        eq_before += sm_j[w];
+        a_before += sm_i[w];
+        b_before += sm_j[w];
     }
-    // equal keys are taken in position order: min(eq_before, need) of them precede
-    int pos = gt_before + (eq_before < need ? eq_before : need);
-    int eq_seen = eq_before;
+    // p < kk holds for every real key by construction; the tests keep every
+    // store inside the row even so (and drop a logits position past the row)
+    if (all_eq) {
+        int pos = a_before;
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const bool gt = ok(e) && key[e] > vstar;
-        const bool eq = ok(e) && key[e] == vstar;
-        const uint64_t eqm = __ballot(eq);
-        const bool take = gt || (eq && eq_seen + __popcll(eqm & below) < need);
-        const uint64_t tm = __ballot(take);
-        const int p = pos + __popcll(tm & below);
-        // p < kk holds by construction (|{> v*}| + need == kk); the test
-        // keeps every store inside the row even so.
-        if (take && p < kk) emit(p, e);
-        pos += __popcll(tm);
-        eq_seen += __popcll(eqm);
+        for (int e = 0; e < KPT; ++e) {
+            const bool take = ge(e);
+            const uint64_t tm = __ballot(take);
+            const int p = pos + lanes_below(tm);
+            if (take && p < kk) emit(p, e);
+            pos += __popcll(tm);
+        }
+    } else {
+        // equal keys are taken in position order: min(b_before, need) of them precede
+        int pos = a_before + (b_before < need ? b_before : need);
+        int eq_seen = b_before;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            bool take = gt(e);
+            const uint64_t eqm = __ballot(eq(e));
+            if (eqm != 0) {
+                take = take || (eq(e) && eq_seen + lanes_below(eqm) < need);
+                eq_seen += __popcll(eqm);
+            }
+            const uint64_t tm = __ballot(take);
+            const int p = pos + lanes_below(tm);
+            if (take && p < kk) emit(p, e);
+            pos += __popcll(tm);
+        }
     }
 }
 
@@ -358,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
     __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
     __shared__ __align__(16) int sm_hist[kBins * kCopies];  // [bin][copy]
     __shared__ int sm_tot[kBins];
-    __shared__ int sm_pick[2];
+    __shared__ int sm_pick[3];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = a.C, k = a.k;
     int32_t* dst = a.out + (int64_t)blockIdx.x * k;
@@ -471,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
             if (ok && (r >> hi) == prefix) atomicAdd(&sm_hist[(int)((r >> sh) & ((1u << w) - 1u)) * kCopies + copy], 1);
         });
         __syncthreads();
-        pick_digit(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
+        pick_digit<kCopies>(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
         prefix = (prefix << w) | (uint64_t)sm_pick[0];
         need = sm_pick[1];
     }

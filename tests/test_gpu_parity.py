@@ -121,10 +121,18 @@ def _rows(synth_lib, kind, R, C, seed):
     if kind == "extremes":
         v = synth_lib.uniform_i32((R, C), seed, s, 0, 3)
         return np.choose(v, [-(2 ** 31), 2 ** 31 - 1, 0, -1]).astype(np.int32)
+    if kind == "crowded":
+        # a wide range (outliers at both ends) with nearly every value in a
+        # narrow band: most keys share their top bits, and the band's
+        # buckets stay large for several digits
+        v = synth_lib.uniform_i32((R, C), seed, s, 0, 999)
+        v[:, 0] = 2 ** 30
+        v[:, -1] = -(2 ** 30)
+        return v.astype(np.int32)
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("kind", ["random", "narrow", "few", "equal", "extremes"])
+@pytest.mark.parametrize("kind", ["random", "narrow", "few", "equal", "extremes", "crowded"])
 @pytest.mark.parametrize("C", [1, 2, 63, 64, 65, 1000, 1024, 1025, 2048, 7813, 16384])
 def test_topk_parity(lsa, oracle_lib, synth_lib, kind, C):
     R = 3 if C <= 2048 else 1
@@ -140,6 +148,15 @@ def test_topk_parity(lsa, oracle_lib, synth_lib, kind, C):
 def test_topk_large_rows(lsa, oracle_lib, synth_lib, C):
     rows = _rows(synth_lib, "narrow", 1, C, seed=C)
     for k in (1, C // 10, C):
+        got = lsa.lsa_topk_chunks(to_dev(rows), k).cpu().numpy()
+        assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (C, k)
+
+
+@pytest.mark.parametrize("C", [40000, 65536])
+def test_topk_large_rows_crowded(lsa, oracle_lib, synth_lib, C):
+    """Long rows whose buckets stay larger than LDS holds for a digit or two."""
+    rows = _rows(synth_lib, "crowded", 1, C, seed=C + 9)
+    for k in (C // 10, C // 2 + 3):
         got = lsa.lsa_topk_chunks(to_dev(rows), k).cpu().numpy()
         assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (C, k)
 
@@ -170,7 +187,7 @@ def test_topk_rows_beyond_registers(lsa, oracle_lib, synth_lib):
         assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), k
 
 
-@pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes", "none", "all"])
+@pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes", "crowded", "none", "all"])
 @pytest.mark.parametrize("C", [1, 64, 1000, 2048, 16384])
 def test_threshold_parity(lsa, oracle_lib, synth_lib, kind, C):
     """Sigmoid gating with a cap: ids, padding and counts bit-exact."""
@@ -364,6 +381,28 @@ def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_
                                           counts=None if cn is None else to_dev(cn), workspace=ws)
             assert np.array_equal(tc.cpu().numpy(), rc), (B, C, k, k_tok, ws)
             assert np.array_equal(tok.cpu().numpy(), ref), (B, C, k, k_tok, ws)
+
+
+@pytest.mark.parametrize("B,C,k,k_tok", [(3, 2048, 276, 2048), (2, 4096, 1024, 5000), (2, 64, 3, 17)])
+def test_topk_tokens_crowded_scores(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
+    """Scores spread evenly over [1, 2) with infinities at both ends: the
+    whole list shares its top key bits, so the select keeps working on a
+    crowded bucket for several digits (in registers while it is larger than
+    LDS holds), with runs of equal scores at the end."""
+    say("token top-k crowded", B, C, k, k_tok)
+    s = synth_lib.stream(synth_lib.TAG_MISC, 4050)
+    u = synth_lib.uniform_i32((B, k * 64), k, s, 0, 2 ** 16 - 1)
+    scores = (1.0 + u.astype(np.float64) / 2 ** 16).astype(np.float32)  # 65536 distinct values, many repeats
+    scores[:, 1] = np.inf
+    scores[:, -2] = -np.inf
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4060 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    ctx[-1] = ids[-1, -1] * 64 + 9
+    ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok)
+    for ws in ("auto", None):
+        tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, workspace=ws)
+        assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref), ws
 
 
 @pytest.mark.parametrize("B,C,k,k_tok", [(4, 12, 5, 7), (3, 64, 40, 600), (4, 2048, 276, 2048)])
