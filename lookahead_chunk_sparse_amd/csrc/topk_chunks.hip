@@ -168,6 +168,48 @@ __device__ inline int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// One wave finishes a select on the cnt <= 64*NS keys of lst (all agreeing
+// above bit hi): bit by bit from bit hi-1 down, the bit of the need-th
+// largest key is 1 iff at least `need` of the remaining candidates have it
+// set, and the candidates keep the keys that agree with it.  Writes
+// sm_pick = {the decided low bits, keys still needed, keys equal to the
+// result}.  Branch-free inner loop: the masks live in scalar registers.
+template <int NS>
+__device__ inline void ballot_finish(const uint32_t* lst, int cnt, int hi, int need, int lane, int* sm_pick) {
+    uint32_t v[NS];
+    uint64_t cand[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int i = 64 * s + lane;
+        v[s] = lst[i < cnt ? i : 0];
+        cand[s] = __ballot(i < cnt);
+    }
+    uint32_t low = 0;
+    int nd = need;
+    for (int b = hi - 1; b >= 0; --b) {
+        uint64_t one[NS];
+        int c1 = 0;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            one[s] = cand[s] & __ballot((v[s] >> b) & 1u);
+            c1 += __popcll(one[s]);
+        }
+        const bool set = nd <= c1;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) cand[s] = set ? one[s] : (cand[s] & ~one[s]);
+        nd = set ? nd : nd - c1;
+        low |= set ? (1u << b) : 0u;
+    }
+    int ceq = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) ceq += __popcll(cand[s]);
+    if (lane == 0) {
+        sm_pick[0] = (int)low;
+        sm_pick[1] = nd;
+        sm_pick[2] = ceq;
+    }
+}
+
 template <int KPT, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     constexpr bool kScoreKeys = MODE != kModeLogits;  // key 0 marks a position that does not compete
@@ -287,6 +329,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         kmax = max(kmax, sm_max[w]);
         avail += sm_avail[w];
     }
+    // values read back from LDS are the same in every lane: say so, so that
+    // they live in scalar registers and the control flow on them stays scalar
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    avail = __builtin_amdgcn_readfirstlane(avail);
     if constexpr (kScoreKeys) kmin += 1u;  // (no competing key: avail == 0, unused)
 
     // --- how many to keep ---
@@ -338,49 +385,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             // of the bucket having the bit set, the bit of r* is 1 iff
             // need <= c1; the bucket keeps the keys that agree
             if (wave == 0) {
-                const uint32_t* lst = sm_list[src];
-                const int ns = (cnt + 63) >> 6;  // occupied slots
-                uint32_t v[kBallotSlots];
-                uint64_t cand[kBallotSlots];
-#pragma unroll
-                for (int s = 0; s < kBallotSlots; ++s) {
-                    const int i = 64 * s + lane;
-                    v[s] = lst[i < cnt ? i : 0];
-                    cand[s] = __ballot(i < cnt);
-                }
-                uint32_t low = 0;
-                int nd = need;
-                for (int b = hi - 1; b >= 0; --b) {
-                    uint64_t one[kBallotSlots];
-                    int c1 = 0;
-#pragma unroll
-                    for (int s = 0; s < kBallotSlots; ++s) {
-                        one[s] = s < ns ? cand[s] & __ballot((v[s] >> b) & 1u) : 0ull;
-                        c1 += __popcll(one[s]);
-                    }
-                    if (nd <= c1) {
-                        low |= 1u << b;
-#pragma unroll
-                        for (int s = 0; s < kBallotSlots; ++s) cand[s] = one[s];
-                    } else {
-                        nd -= c1;
-#pragma unroll
-                        for (int s = 0; s < kBallotSlots; ++s) cand[s] &= ~one[s];
-                    }
-                }
-                int ceq = 0;
-#pragma unroll
-                for (int s = 0; s < kBallotSlots; ++s) ceq += __popcll(cand[s]);
-                if (lane == 0) {
-                    sm_pick[0] = (int)low;
-                    sm_pick[1] = nd;
-                    sm_pick[2] = ceq;
-                }
+                if (cnt <= 64)
+                    ballot_finish<1>(sm_list[src], cnt, hi, need, lane, sm_pick);
+                else
+                    ballot_finish<kBallotSlots>(sm_list[src], cnt, hi, need, lane, sm_pick);
             }
             __syncthreads();
-            rstar |= (uint32_t)sm_pick[0];
-            need = sm_pick[1];
-            cnt = sm_pick[2];
+            rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
+            need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
+            cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
             break;
         }
         // one histogram pass over the next (up to) 8 bits
@@ -408,10 +421,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
         __syncthreads();
         pick_digit<kLaneCopies>(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
-        const uint32_t dg = (uint32_t)sm_pick[0];
+        const uint32_t dg = (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
         const int cnt_in = cnt;
-        need = sm_pick[1];
-        cnt = sm_pick[2];
+        need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
+        cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
         rstar |= dg << sh;
         hi = sh;
         if (hi > 0 && cnt <= kListCap) {
@@ -496,6 +509,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         a_before += sm_i[w];
         b_before += sm_j[w];
     }
+    a_before = __builtin_amdgcn_readfirstlane(a_before);
+    b_before = __builtin_amdgcn_readfirstlane(b_before);
     // p < kk holds for every real key by construction; the tests keep every
     // store inside the row even so (and drop a logits position past the row)
     if (all_eq) {
@@ -545,7 +560,8 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
     __shared__ __align__(16) int sm_hist[kBins * kCopies];  // [bin][copy]
     __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[3];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int C = a.C, k = a.k;
     int32_t* dst = a.out + (int64_t)blockIdx.x * k;
     const int S = (C + 64 * kWaves - 1) / (64 * kWaves);
@@ -633,6 +649,9 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
         kmax = max(kmax, sm_max[w]);
         avail += sm_avail[w];
     }
+    kmin = __builtin_amdgcn_readfirstlane(kmin);  // the same in every lane
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    avail = __builtin_amdgcn_readfirstlane(avail);
     int kk = k;
     if (capped) {
         kk = avail < k ? avail : k;
@@ -658,8 +677,8 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
         });
         __syncthreads();
         pick_digit<kCopies>(sm_hist, sm_tot, sm_pick, tid, lane, wave, need);
-        prefix = (prefix << w) | (uint64_t)sm_pick[0];
-        need = sm_pick[1];
+        prefix = (prefix << w) | (uint64_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
+        need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
     }
     const uint32_t vstar = kmin + (uint32_t)prefix;
 
@@ -679,6 +698,8 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
         gt_before += sm_i[w];
         eq_before += sm_j[w];
     }
+    gt_before = __builtin_amdgcn_readfirstlane(gt_before);  // the same in every lane
+    eq_before = __builtin_amdgcn_readfirstlane(eq_before);
     int pos = gt_before + (eq_before < need ? eq_before : need);
     int eq_seen = eq_before;
     for_each_slot([&](int e, uint32_t key, bool ok) {
