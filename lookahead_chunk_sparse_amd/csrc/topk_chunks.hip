@@ -217,10 +217,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int sm_j[kWaves];
     __shared__ int sm_avail[kWaves];
     __shared__ uint32_t sm_min[kWaves], sm_max[kWaves];
-    __shared__ __align__(16) int sm_hist[kBins * kLaneCopies];  // [bin][copy]
+    // While selecting: the histogram ([bin][copy]) and two lists that hold a
+    // bucket's keys as r (below), in no particular order.  Afterwards the
+    // same words hold the per-wave output regions of the compaction.
+    constexpr int kRawWords = kBins * kLaneCopies + 2 * kListCap;
+    __shared__ __align__(16) uint32_t sm_raw[kRawWords];
+    int* const sm_hist = reinterpret_cast<int*>(sm_raw);
+    uint32_t* const sm_lists = sm_raw + kBins * kLaneCopies;  // list s: sm_lists + s * kListCap
     __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[3];  // digit chosen by a pass, keys still needed, keys in the digit
-    __shared__ uint32_t sm_list[2][kListCap];  // a bucket's keys as r (below), in no particular order
     __shared__ int sm_cnt[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     if (kk == n_ok) hi = 0;  // every competing key is kept: r* = 0 will do
     uint32_t rstar = 0;      // decided bits of r*, in place
     int need = kk, cnt = n_ok;
-    int src = -1;            // the bucket is in registers (-1) or in sm_list[src]
+    int src = -1;            // the bucket is in registers (-1) or in list src
     auto bucket_ub = [&](int h) {  // r - rstar <= ub <=> r in the bucket (and r <= range)
         const uint32_t span = h >= 32 ? 0xFFFFFFFFu : (1u << h) - 1u;
         return min(span, range - rstar);
@@ -386,9 +391,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             // need <= c1; the bucket keeps the keys that agree
             if (wave == 0) {
                 if (cnt <= 64)
-                    ballot_finish<1>(sm_list[src], cnt, hi, need, lane, sm_pick);
+                    ballot_finish<1>(sm_lists + src * kListCap, cnt, hi, need, lane, sm_pick);
                 else
-                    ballot_finish<kBallotSlots>(sm_list[src], cnt, hi, need, lane, sm_pick);
+                    ballot_finish<kBallotSlots>(sm_lists + src * kListCap, cnt, hi, need, lane, sm_pick);
             }
             __syncthreads();
             rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
                 if (d <= ub) atomicAdd(&sm_hist[(int)(d >> sh) * kLaneCopies + lane], 1);
             }
         } else {
-            const uint32_t* lst = sm_list[src];
+            const uint32_t* lst = sm_lists + src * kListCap;
             for (int i = tid; i < cnt; i += kThreads)
                 atomicAdd(&sm_hist[(int)((lst[i] >> sh) & dmask) * kLaneCopies + lane], 1);
         }
@@ -428,10 +433,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         rstar |= dg << sh;
         hi = sh;
         if (hi > 0 && cnt <= kListCap) {
-            // move the new bucket into sm_list[nxt]: per wave, one LDS atomic
+            // move the new bucket into list nxt: per wave, one LDS atomic
             // reserves the places of its keys (the bucket tests are
             // recomputed rather than kept, to spare scalar registers)
-            uint32_t* out = sm_list[nxt];
+            uint32_t* out = sm_lists + nxt * kListCap;
             if (src < 0) {
                 const uint32_t ub = bucket_ub(hi);
                 int n = 0;
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
                     base += __popcll(mk);
                 }
             } else {
-                const uint32_t* in = sm_list[src];
+                const uint32_t* in = sm_lists + src * kListCap;
                 for (int i0 = 0; i0 < cnt_in; i0 += kThreads) {
                     const int i = i0 + tid;
                     const uint32_t r = in[i < cnt_in ? i : 0];
@@ -485,60 +490,135 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             dst[p] = idx;
         }
     };
-    // Per wave: keys taken (all_eq) or keys > r* and keys == r*; in position
-    // order the waves come one after the other, so exclusive scans over the
-    // wave totals give each wave the equal keys and the outputs before it.
-    int n_a = 0, n_b = 0;
-    if (all_eq) {
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) n_a += __popcll(__ballot(ge(e)));
-    } else {
+    // The selection in position order: keys > r*, and the first `need` keys
+    // == r* (all of them when all_eq).  Waves come one after the other in
+    // position order, so exclusive scans over per-wave totals place each
+    // wave's outputs.  The select reads the histogram and the lists no more
+    // (its last step ended with a barrier): their words take the regions.
+    constexpr int kEntryWords = MODE == kModeSlice ? 2 : 1;  // position (and key)
+    constexpr int kRegionWords = 64 * KPT * kEntryWords;
+    if constexpr (kWaves * kRegionWords <= kRawWords) {
+        // One sweep: every wave appends its keys >= r* to its own region in
+        // position order (an equal key flagged in bit 31; positions < 2^30),
+        // then, after one barrier, copies the ones taken to the output with
+        // coalesced stores.
+        uint32_t* reg = sm_raw + wave * kRegionWords;
+        int n_ge = 0, n_eq = 0;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            n_a += __popcll(__ballot(gt(e)));
-            n_b += __popcll(__ballot(eq(e)));
+            const bool in = ge(e);
+            const uint64_t m = __ballot(in);
+            if (in) {
+                const int i = n_ge + lanes_below(m);
+                const uint32_t idx = (uint32_t)(wbase + 64 * e + lane);
+                const uint32_t ent = all_eq || !eq(e) ? idx : idx | 0x80000000u;
+                if constexpr (MODE == kModeSlice) {
+                    reg[2 * i] = ent;
+                    reg[2 * i + 1] = rr[e] + kmin;
+                } else {
+                    reg[i] = ent;
+                }
+            }
+            n_ge += __popcll(m);
+            if (!all_eq) n_eq += __popcll(__ballot(eq(e)));
         }
-    }
-    if (lane == 0) {
-        sm_i[wave] = n_a;
-        sm_j[wave] = n_b;
-    }
-    __syncthreads();
-    int a_before = 0, b_before = 0;
-    for (int w = 0; w < wave; ++w) {
-        a_before += sm_i[w];
-        b_before += sm_j[w];
-    }
-    a_before = __builtin_amdgcn_readfirstlane(a_before);
-    b_before = __builtin_amdgcn_readfirstlane(b_before);
-    // p < kk holds for every real key by construction; the tests keep every
-    // store inside the row even so (and drop a logits position past the row)
-    if (all_eq) {
-        int pos = a_before;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const bool take = ge(e);
-            const uint64_t tm = __ballot(take);
-            const int p = pos + lanes_below(tm);
-            if (take && p < kk) emit(p, e);
-            pos += __popcll(tm);
+        if (lane == 0) {
+            sm_i[wave] = n_ge;
+            sm_j[wave] = n_eq;
         }
-    } else {
-        // equal keys are taken in position order: min(b_before, need) of them precede
-        int pos = a_before + (b_before < need ? b_before : need);
-        int eq_seen = b_before;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            bool take = gt(e);
-            const uint64_t eqm = __ballot(eq(e));
-            if (eqm != 0) {
-                take = take || (eq(e) && eq_seen + lanes_below(eqm) < need);
+        __syncthreads();
+        int ge_before = 0, eq_before = 0;
+        for (int w = 0; w < wave; ++w) {
+            ge_before += sm_i[w];
+            eq_before += sm_j[w];
+        }
+        ge_before = __builtin_amdgcn_readfirstlane(ge_before);
+        eq_before = __builtin_amdgcn_readfirstlane(eq_before);
+        // equal keys are taken in position order: min(eq_before, need) of them precede
+        int pos = all_eq ? ge_before : ge_before - eq_before + (eq_before < need ? eq_before : need);
+        int eq_seen = eq_before;
+        for (int i0 = 0; i0 < n_ge; i0 += 64) {
+            const int i = i0 + lane;
+            const bool valid = i < n_ge;
+            const uint32_t v = reg[kEntryWords * (valid ? i : 0)];
+            bool take = valid;
+            if (!all_eq) {
+                const bool is_eq = valid && (v >> 31) != 0u;
+                const uint64_t eqm = __ballot(is_eq);
+                take = valid && (!is_eq || eq_seen + lanes_below(eqm) < need);
                 eq_seen += __popcll(eqm);
             }
             const uint64_t tm = __ballot(take);
             const int p = pos + lanes_below(tm);
-            if (take && p < kk) emit(p, e);
+            // p < kk for every real key; the test also drops a logits position past the row
+            if (take && p < kk) {
+                const int idx = (int)(v & 0x7FFFFFFFu);
+                if constexpr (MODE == kModeSlice) {
+                    dst[p] = off + idx;
+                    dst_key[p] = reg[2 * i + 1];
+                } else if constexpr (MODE == kModeCand) {
+                    dst[p] = a.cand_pos[(int64_t)row * C + idx];
+                } else {
+                    dst[p] = idx;
+                }
+            }
             pos += __popcll(tm);
+        }
+    } else {
+        // Two sweeps over the registers: per-wave totals (keys taken when
+        // all_eq, else keys > r* and keys == r*), then the outputs.
+        int n_a = 0, n_b = 0;
+        if (all_eq) {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) n_a += __popcll(__ballot(ge(e)));
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                n_a += __popcll(__ballot(gt(e)));
+                n_b += __popcll(__ballot(eq(e)));
+            }
+        }
+        if (lane == 0) {
+            sm_i[wave] = n_a;
+            sm_j[wave] = n_b;
+        }
+        __syncthreads();
+        int a_before = 0, b_before = 0;
+        for (int w = 0; w < wave; ++w) {
+            a_before += sm_i[w];
+            b_before += sm_j[w];
+        }
+        a_before = __builtin_amdgcn_readfirstlane(a_before);
+        b_before = __builtin_amdgcn_readfirstlane(b_before);
+        // p < kk holds for every real key by construction; the tests keep every
+        // store inside the row even so (and drop a logits position past the row)
+        if (all_eq) {
+            int pos = a_before;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const bool take = ge(e);
+                const uint64_t tm = __ballot(take);
+                const int p = pos + lanes_below(tm);
+                if (take && p < kk) emit(p, e);
+                pos += __popcll(tm);
+            }
+        } else {
+            // equal keys are taken in position order: min(b_before, need) of them precede
+            int pos = a_before + (b_before < need ? b_before : need);
+            int eq_seen = b_before;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                bool take = gt(e);
+                const uint64_t eqm = __ballot(eq(e));
+                if (eqm != 0) {
+                    take = take || (eq(e) && eq_seen + lanes_below(eqm) < need);
+                    eq_seen += __popcll(eqm);
+                }
+                const uint64_t tm = __ballot(take);
+                const int p = pos + lanes_below(tm);
+                if (take && p < kk) emit(p, e);
+                pos += __popcll(tm);
+            }
         }
     }
 }
