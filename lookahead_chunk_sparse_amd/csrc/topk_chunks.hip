@@ -114,10 +114,11 @@ __device__ inline void pick_digit(const int* sm_hist, int* sm_tot, int* sm_pick,
 }
 
 // Order-preserving unsigned key of a float score: equal values give equal
-// keys (-0 is taken as +0), larger values larger keys.  NaN is not a score.
+// keys (-0 is taken as +0: adding +0 maps -0 to +0 and leaves every other
+// value as it is), larger values larger keys.  NaN is not a score.
 __device__ inline uint32_t score_key(float x) {
-    const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u; else u | 2^31
 }
 
 // One row (or row slice) per workgroup.  Modes:
@@ -257,7 +258,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             const int cnt = a.list_counts[row];
             kb = cnt < 0 ? 0 : cnt > a.n_list ? a.n_list : cnt;
         }
-        const int64_t ctx = a.ctx[row];
+        // usable tokens of chunk c: 64 below chunk ctx/64, ctx%64 in it, none above
+        const int ctx_row = a.ctx[row] > 0 ? a.ctx[row] : 0;
+        const uint32_t ctx_chunk = (uint32_t)ctx_row / kChunkTokens;
+        const int ctx_rem = ctx_row % kChunkTokens;
         const int j0 = off / kChunkTokens;
         // entries of this workgroup in use: j0 <= j < jend (C is a multiple of 64)
         const int jend = C > 0 ? min(kb, j0 + C / kChunkTokens) : 0;
@@ -272,12 +276,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            // tokens of entry j below the context length, 0 for an entry not in use
+            // tokens of entry j below the context length, 0 for an entry not
+            // in use (scalar arithmetic: the entry and its chunk id are uniform)
             const int j = j0 + wave * KPT + e;
-            const int64_t cid = __builtin_amdgcn_readlane(cidv, e);
-            const int64_t below_ctx = ctx - cid * kChunkTokens;
-            const int lim = j < jend ? (below_ctx < 0 ? 0 : below_ctx > kChunkTokens ? kChunkTokens : (int)below_ctx) : 0;
-            key[e] = score_key(sc[e]) & (0u - (uint32_t)(lane < lim));
+            const uint32_t cid = (uint32_t)__builtin_amdgcn_readlane(cidv, e);
+            const int lim = j >= jend ? 0 : cid < ctx_chunk ? kChunkTokens : cid == ctx_chunk ? ctx_rem : 0;
+            const uint32_t kv = score_key(sc[e]);
+            key[e] = lane < lim ? kv : 0u;
         }
     } else if constexpr (MODE == kModeCand) {
         const uint32_t* krow = a.cand_key + (int64_t)row * C;
@@ -293,8 +298,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int idx = wbase + 64 * e + lane;
-            key[e] = (uint32_t)lrow[idx < C ? idx : C - 1] ^ 0x80000000u;  // positions >= C: made inert below
+            key[e] = (uint32_t)lrow[idx < C ? idx : C - 1] ^ 0x80000000u;
         }
+    }
+
+    if constexpr (!kScoreKeys) {
+        // A position past the row takes key 0, the smallest key, behind every
+        // real key of that value in position order: it is never selected (at
+        // most the C real keys are) and moves no pick (it can only add to the
+        // lowest bucket); the range below is taken over real keys only.
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = wbase + 64 * e + lane < C ? key[e] : 0u;
     }
 
     // --- range and keep count ---
@@ -354,24 +368,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
     const int n_ok = kScoreKeys ? avail : C;  // competing keys
 
-    // --- keys relative to the row minimum: r = key - kmin in [0, range] ---
-    // A score key that does not compete becomes 0xFFFFFFFF, above every r
-    // (range <= 0xFFFFFFFE as kmin >= 1), and every test below bounds r by
-    // range.  A logits position past the row gets r = 0, the smallest value,
-    // behind every real key of its value in position order: it is never
-    // selected (at most the C real keys are) and moves no pick (it only adds
-    // to the lowest bucket).
+    // --- radix select ---
+    // On r = key - kmin: a competing key has r in [0, range].  A score key
+    // that does not compete is 0, so r wraps above range (kmin >= 1 and
+    // kmax < 2^32), and every test below bounds r by range; a logits position
+    // past the row has key 0 too: outside every bucket unless kmin is 0, and
+    // then the smallest value, as above.
     const uint32_t range = kmax - kmin;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        if constexpr (kScoreKeys)
-            key[e] = key[e] != 0u ? key[e] - kmin : 0xFFFFFFFFu;
-        else
-            key[e] = wbase + 64 * e + lane < C ? key[e] - kmin : 0u;
-    }
-    uint32_t* rr = key;
-
-    // --- radix select on r ---
     // The bits of r* (the kk-th largest r) are decided from the top; the
     // current bucket holds the keys that agree with r* on the decided bits
     // (cnt keys, of which `need` are kept): r in [rstar, rstar + ub].
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     uint32_t rstar = 0;      // decided bits of r*, in place
     int need = kk, cnt = n_ok;
     int src = -1;            // the bucket is in registers (-1) or in list src
-    auto bucket_ub = [&](int h) {  // r - rstar <= ub <=> r in the bucket (and r <= range)
+    auto bucket_ub = [&](int h) {  // key - (kmin + rstar) <= ub <=> key in the bucket (and r <= range)
         const uint32_t span = h >= 32 ? 0xFFFFFFFFu : (1u << h) - 1u;
         return min(span, range - rstar);
     };
@@ -414,9 +417,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         if (tid == 0) sm_cnt[nxt] = 0;  // ordered before its use by the barriers of pick_digit
         if (src < 0) {
             const uint32_t ub = bucket_ub(hi);
+            const uint32_t base = kmin + rstar;
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
-                const uint32_t d = rr[e] - rstar;
+                const uint32_t d = key[e] - base;
                 if (d <= ub) atomicAdd(&sm_hist[(int)(d >> sh) * kLaneCopies + lane], 1);
             }
         } else {
@@ -439,18 +443,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             uint32_t* out = sm_lists + nxt * kListCap;
             if (src < 0) {
                 const uint32_t ub = bucket_ub(hi);
+                const uint32_t base = kmin + rstar;
                 int n = 0;
 #pragma unroll
-                for (int e = 0; e < KPT; ++e) n += __popcll(__ballot(rr[e] - rstar <= ub));
-                int base = 0;
-                if (lane == 0 && n > 0) base = atomicAdd(&sm_cnt[nxt], n);
-                base = __builtin_amdgcn_readfirstlane(base);
+                for (int e = 0; e < KPT; ++e) n += __popcll(__ballot(key[e] - base <= ub));
+                int at = 0;
+                if (lane == 0 && n > 0) at = atomicAdd(&sm_cnt[nxt], n);
+                at = __builtin_amdgcn_readfirstlane(at);
 #pragma unroll
                 for (int e = 0; e < KPT; ++e) {
-                    const bool in = rr[e] - rstar <= ub;
+                    const bool in = key[e] - base <= ub;
                     const uint64_t mk = __ballot(in);
-                    if (in) out[base + lanes_below(mk)] = rr[e];
-                    base += __popcll(mk);
+                    if (in) out[at + lanes_below(mk)] = key[e] - kmin;
+                    at += __popcll(mk);
                 }
             } else {
                 const uint32_t* in = sm_lists + src * kListCap;
@@ -473,17 +478,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     const bool all_eq = need == cnt;
 
     // --- ordered compaction ---
-    // On r: ge <=> rstar <= r <= range, gt <=> rstar < r <= range, eq <=> r == rstar.
-    const uint32_t top = range - rstar;
-    auto ge = [&](int e) { return rr[e] - rstar <= top; };
-    auto gt = [&](int e) { return rr[e] - rstar - 1u < top; };
-    auto eq = [&](int e) { return rr[e] == rstar; };
+    // ge <=> v* <= key <= kmax, gt <=> v* < key <= kmax, eq <=> key == v*.
+    const uint32_t vstar = kmin + rstar;
+    const uint32_t top = kmax - vstar;
+    auto ge = [&](int e) { return key[e] - vstar <= top; };
+    auto gt = [&](int e) { return key[e] - vstar - 1u < top; };
+    auto eq = [&](int e) { return key[e] == vstar; };
     // the output of slot e taken at place p
     auto emit = [&](int p, int e) {
         const int idx = wbase + 64 * e + lane;
         if constexpr (MODE == kModeSlice) {
             dst[p] = off + idx;
-            dst_key[p] = rr[e] + kmin;
+            dst_key[p] = key[e];
         } else if constexpr (MODE == kModeCand) {
             dst[p] = a.cand_pos[(int64_t)row * C + idx];
         } else {
@@ -514,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
                 const uint32_t ent = all_eq || !eq(e) ? idx : idx | 0x80000000u;
                 if constexpr (MODE == kModeSlice) {
                     reg[2 * i] = ent;
-                    reg[2 * i + 1] = rr[e] + kmin;
+                    reg[2 * i + 1] = key[e];
                 } else {
                     reg[i] = ent;
                 }

@@ -344,13 +344,16 @@ def test_attend_deterministic(lsa, synth_lib):
 
 def _token_scores(synth_lib, B, n, seed):
     """bf16-rounded normals coarsened to quarters (long runs of equal scores),
-    with signed zeros and infinities planted."""
+    with signed zeros, subnormals and infinities planted."""
     s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), seed, synth_lib.stream(synth_lib.TAG_MISC, 4000)))
     s = np.round(s * 4) / 4
     s[:, 3::17] = 0.0
     s[:, 5::19] = -0.0
     s[:, 7::41] = np.inf
     s[:, 11::43] = -np.inf
+    s[:, 13::47] = np.float32(1e-40)    # subnormals of both signs: ordered like any value,
+    s[:, 15::53] = np.float32(-1e-40)   # and apart from zero
+    s[:, 19::59] = np.float32(1.4e-45)
     return np.ascontiguousarray(s, dtype=np.float32)
 
 
