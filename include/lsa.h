@@ -143,7 +143,8 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
  * NULL) and chunk_ids[b][j]*64 + t < ctx_len[b].  Among the competing
  * positions the first min(k_tok, competing) of the order "score descending,
  * then position ascending" are kept (scores compare as values: -0 equals
- * +0), written in ascending position order into tok[b][0..tok_counts[b]),
+ * +0, subnormals are not flushed), written in ascending position order
+ * into tok[b][0..tok_counts[b]),
  * the rest of the row set to -1.  The set is unique: bit-exact.
  *
  *  scores      device fp32 [B][k*64], no NaN among competing positions
@@ -156,12 +157,11 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
  *  workspace   device buffer of lsa_topk_tokens_workspace_size(B, k, k_tok)
  *              bytes, 256-byte aligned, or NULL.  With it, lists of more
  *              than 32768 positions are selected by many workgroups per
- *              request: each slice of the
- *              list keeps its own top k_tok, then the top k_tok of those
- *              candidates are taken (the same set, since every position of
- *              the request's top k_tok is in its slice's).  NULL: one
- *              workgroup per request.  Scratch only; calls sharing a
- *              workspace must not overlap in time.
+ *              request: each slice of the list keeps its own top k_tok,
+ *              then the top k_tok of those candidates are taken (the same
+ *              set, since every position of the request's top k_tok is in
+ *              its slice's).  NULL: one workgroup per request.  Scratch
+ *              only; calls sharing a workspace must not overlap in time.
  * All other pointers need 4-byte alignment.
  */
 lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const int32_t* counts,

@@ -6,12 +6,13 @@
 //
 // One 1024-thread workgroup per row; wave w keeps positions
 // [64*KPT*w, 64*KPT*(w+1)) in registers, lane l every 64th of them from l
-// (coalesced loads), as order-preserving unsigned keys (logit XOR 0x80000000),
-// offset by the row's smallest key so that only the bits spanning the row's
-// range remain (logits of both signs would otherwise differ in every bit).
+// (coalesced loads), as order-preserving unsigned keys (logit XOR 0x80000000);
+// digits are taken of key - (the row's smallest key), so that only the bits
+// spanning the row's range remain (logits of both signs would otherwise
+// differ in every bit).
 //  1. Radix select from the top of the range.  A pass counts the keys of the
-//     current bucket per 8-bit digit into an LDS histogram (ds_add, 16
-//     copies against same-word conflicts); one wave then finds, by a suffix
+//     current bucket per 8-bit digit into an LDS histogram (ds_add, one copy
+//     per lane against same-word conflicts); one wave then finds, by a suffix
 //     scan over the 256 bins, the digit that holds the k-th largest key, and
 //     that digit's keys become the bucket.  Every pass over the registers
 //     costs the whole row's keys in VALU work on one CU, so once the bucket
@@ -22,10 +23,13 @@
 //     keys equal to v*, and `need`, how many of those belong to the selection.
 //  2. Ordered compaction: keys > v* are taken; keys == v* are taken while
 //     their rank among equal keys, in index order, is below `need` (all of
-//     them when need is their number, the common case: then simply the keys
-//     >= v*).  Ranks in index order come from ballots within a wave (slot by
-//     slot) and from scans of the per-wave totals across waves, so the output
-//     is ascending.
+//     them when need is their number: then simply the keys >= v*).  Each
+//     wave appends its keys >= v* to its own LDS region in index order;
+//     scans of the per-wave totals then place every wave's outputs, so the
+//     output is ascending.
+// Rows too long for registers stream from memory instead (the same select
+// with a 16-copy histogram and no LDS bucket), and very long token rows are
+// split into slices whose top k are merged by a candidates pass.
 //
 // The same select serves the token-level stage: after the chunk recall the
 // model's own token scores pick a fine-grained top-k among the recalled
@@ -56,9 +60,9 @@ __device__ inline uint32_t wave_max(uint32_t v) {
 
 constexpr int kDigitBits = 8;
 constexpr int kBins = 1 << kDigitBits;
-// Copies of the histogram: lane l counts into copy l % kCopies, so lanes
-// whose keys share a bin hit kCopies different words (scores crowd into a
-// few bins, and same-word LDS atomics serialise).
+// Copies of the streaming kernel's histogram: lane l counts into copy
+// l % kCopies, so lanes whose keys share a bin hit kCopies different words
+// (scores crowd into a few bins, and same-word LDS atomics serialise).
 constexpr int kCopies = 16;
 
 // After a histogram pass (and its barrier): sums the COPIES copies of every
