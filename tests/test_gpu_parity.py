@@ -363,6 +363,7 @@ def _token_scores(synth_lib, B, n, seed):
     (3, 64, 40, 600),
     (4, 2048, 276, 2048),  # the 128K recall, a 2048-token budget
     (2, 4096, 1024, 2048),  # the largest list: 65536 positions
+    (2, 600, 500, 3000),   # 32000 positions: 32 per thread, the most whose output regions fit LDS
 ])
 def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_tok):
     say("token top-k", B, C, k, k_tok)
@@ -406,6 +407,25 @@ def test_topk_tokens_crowded_scores(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
     for ws in ("auto", None):
         tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, workspace=ws)
         assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref), ws
+
+
+@pytest.mark.parametrize("slices,k_tok", [(2, 2048), (12, 4096)])
+def test_topk_tokens_split_shapes(lsa, oracle_lib, synth_lib, monkeypatch, slices, k_tok):
+    """The 500K recall (782 chunks, 50,048 positions) split into 2 long slices
+    (32 positions per thread in the slice select, which keeps keys too: its
+    output takes two sweeps over the registers) or 12 slices with a 4096-token
+    budget (49,152 candidates, 48 per thread: the same in the candidates
+    select)."""
+    say("token top-k split shapes", slices, k_tok)
+    monkeypatch.setenv("LSA_TOPK_SPLIT_SLICES", str(slices))
+    B, C, k = 2, 7813, 782
+    scores = _token_scores(synth_lib, B, k * 64, seed=slices)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4070 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.array([500000, ids[1, -1] * 64 + 33], dtype=np.int32)
+    ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok)
+    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok, workspace="auto")
+    assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(tok.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("B,C,k,k_tok", [(4, 12, 5, 7), (3, 64, 40, 600), (4, 2048, 276, 2048)])
