@@ -537,8 +537,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(--gpus must be 1).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the decode path here has no multi-GPU "
+              "mode (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
