@@ -99,12 +99,12 @@ class LsaDecoder:
         self.Hq, self.k, self.alpha, self.tau = Hq, k, alpha, tau
         self.d_idx = k_idx.shape[2]
         self.lag = 1 if host_kv is not None else 0
-        if host_kv is not None and n_split == 0:
-            # with the fetch gathering on a few compute units, more and smaller
-            # attention workgroups balance around them (measured on 1M: 4x the
-            # library's split count beats 1x by about 20%)
-            from ._binding import lsa_gather_attend_default_splits
-            n_split = min(k, 4 * lsa_gather_attend_default_splits(self.B, self.Hkv, k))
+        # The host tier keeps the library's split count too (0).  Measured on
+        # the 1M workload with the 16-workgroup pull fetch: with the delta
+        # fetch and a stable selection (the steady state) it runs 3,992
+        # steps/s against 3,633 with 4x the splits; while the host link is
+        # busy all interval (a drifting query, or full re-fetches) 4x the
+        # splits balance around the fetch workgroups only 1-2% better.
         self.n_split = n_split
         if fetch not in ("pull", "memcpy"):
             raise ValueError("fetch must be 'pull' or 'memcpy'")
