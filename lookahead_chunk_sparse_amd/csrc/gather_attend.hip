@@ -506,13 +506,15 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttendArgs a) {
         }
 #pragma unroll
         for (int sp = 0; sp < NS; ++sp) mstar = fmaxf(mstar, pm[sp]);
-        if (mstar != -INFINITY) {
+        // Branch-free, so that every load above is issued before any result is
+        // needed (loads used only under a branch move into it, a second round
+        // trip).  A split with no valid token has m = -inf and weight 0; when
+        // all have, every weight is 0 and so is the output.
 #pragma unroll
-            for (int sp = 0; sp < NS; ++sp) {
-                const float sc = __builtin_amdgcn_exp2f(pm[sp] - mstar);
-                l += sc * pl[sp];
-                o += sc * po[sp];
-            }
+        for (int sp = 0; sp < NS; ++sp) {
+            const float sc = pm[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm[sp] - mstar);
+            l += sc * pl[sp];
+            o += sc * po[sp];
         }
     } else {
         for (int sp = 0; sp < a.n_split; ++sp) mstar = fmaxf(mstar, a.part_ml[((base + sp) * a.G + hh) * 2]);
