@@ -45,22 +45,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attend_bytes_per_launch(w) -> int:
+def attend_bytes_per_launch(w, seg: int = 0) -> int:
     """Algorithmic HBM bytes of one attention launch: the retained K and V
-    tiles of every (request, KV head), the bf16 queries, the fp32 outputs and
-    the chunk ids."""
+    tiles of every (request, KV head), the K and V rows of a resident segment
+    of `seg` tokens per request if any, the bf16 queries, the fp32 outputs
+    and the chunk ids."""
     kv = w.B * w.Hkv * w.k * 2 * w.T * w.d * 2
+    sk = w.B * w.Hkv * seg * 2 * w.d * 2
     q = w.B * w.Hq * w.d * 2
     out = w.B * w.Hq * w.d * 4
     ids = w.B * w.k * 4
-    return kv + q + out + ids
+    return kv + sk + q + out + ids
 
 
-def step_bytes(w, layers: int = 1) -> int:
+def step_bytes(w, layers: int = 1, seg: int = 0) -> int:
     """Algorithmic bytes of one decode step: one attention launch per layer
     plus the indexer scan (every key byte once, one scan shared by all
     layers) amortised over tau steps."""
-    return layers * attend_bytes_per_launch(w) + (w.B * w.C * w.d_idx) // w.tau
+    return layers * attend_bytes_per_launch(w, seg) + (w.B * w.C * w.d_idx) // w.tau
 
 
 def kernel_sha() -> str:
@@ -526,6 +528,9 @@ def main():
     ap.add_argument("--token-topk", type=int, default=0, metavar="K_TOK",
                     help="two-stage selection: attend over the K_TOK best tokens of the recalled chunks")
     ap.add_argument("--layers", type=int, default=1, help="layers sharing one selection (HBM-resident only)")
+    ap.add_argument("--segment", type=int, default=0, metavar="S",
+                    help="resident tokens per request (local window, decoded tokens, compressed entries) "
+                         "attended in the same softmax as the recalled chunks (HBM-resident, one layer)")
     ap.add_argument("--fetch", default="pull", choices=("pull", "memcpy"), help="host-tier fetch method")
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
     ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
@@ -567,6 +572,15 @@ def main():
                         False if args.no_delta else None)
         return
     dec = setup(w, args.n_split, args.layers)
+    if args.segment:
+        if args.layers != 1:
+            print("--segment runs with one layer", file=sys.stderr)
+            sys.exit(2)
+        # synthetic resident tokens: seeded normals, every request's segment full
+        gen = torch.Generator(device="cuda:0").manual_seed(w.seed + 77)
+        dec.seg_kv = torch.randn((w.B, 2, w.Hkv, args.segment, w.d), generator=gen, device="cuda:0",
+                                 dtype=torch.float32).to(torch.bfloat16)
+        dec.seg_len = torch.full((w.B,), args.segment, dtype=torch.int32, device="cuda:0")
     n_q = max(args.steps, args.warmup, w.tau)
     q_all, qidx = make_queries(w, n_q)
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
@@ -576,7 +590,7 @@ def main():
     if args.kernel_only:
         dec.reselect(qidx[0], 0)
         mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
-        gbs = attend_bytes_per_launch(w) / (mean_ms * 1e-3) / 1e9
+        gbs = attend_bytes_per_launch(w, args.segment) / (mean_ms * 1e-3) / 1e9
         print(json.dumps({"kernel": "attend_split_kernel<128>+combine", "workload": w.name, "n_split": splits,
                           "launches": args.kernel_launches, "mean_ms": mean_ms, "median_ms": med_ms,
                           "achieved_GBs": gbs}))
@@ -612,18 +626,20 @@ def main():
 
     # ---- the dominant kernel, event-timed on its own stream ----
     mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
-    a_bytes = attend_bytes_per_launch(w)
+    a_bytes = attend_bytes_per_launch(w, args.segment)
     achieved = a_bytes / (mean_ms * 1e-3) / 1e9
     log(f"[bench] attention launch: mean {mean_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
-    traffic = traffic_for_current_kernel(w)
+    traffic = traffic_for_current_kernel(w) if not args.segment else None  # counters: no segment
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy (torch, 1 GiB, read + write bytes): {copy_gbs:.0f} GB/s")
     ceiling = read_ceiling(dec.kv)
     log(f"[bench] read ceiling, random 16 KB tiles of the K/V store: {ceiling['GBs']:.0f} GB/s")
 
-    sb = step_bytes(w, args.layers)
+    sb = step_bytes(w, args.layers, args.segment)
     layer_txt = "one layer" if args.layers == 1 else f"{args.layers} layers sharing one selection"
+    if args.segment:
+        layer_txt += f", plus {args.segment} resident tokens per request in the same softmax"
     result = {
         "metric": METRIC,
         "value": round(steps_s, 2),
@@ -644,6 +660,7 @@ def main():
             "global_batch": w.B,
             "seq_len": w.N,
             "retained_chunks": w.k,
+            "resident_segment_tokens": args.segment,
             "n_split": splits,
             "timing": "eager launches" if args.eager else "hipGraph replay of all steps",
             "tokens_per_s": round(steps_s * w.B, 1),
@@ -669,7 +686,7 @@ def main():
             "mean_launch_us": round(mean_ms * 1e3, 2),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.segment:  # the oracle sample has no segment
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
