@@ -1,0 +1,122 @@
+"""Randomised parity of the select kernels with the oracle: seeded draws of
+row shapes, budgets and key distributions (ties, both-sign extremes, crowded
+bands, signed zeros, infinities, subnormals, partial contexts, ragged entry
+counts), every output compared bit for bit.  The draws are fixed by their
+case number, so a failure names a reproducible case."""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from helpers import to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    import lookahead_chunk_sparse_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ chunk logits
+
+def _logit_case(i):
+    rng = np.random.default_rng(1000 + i)
+    C = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 4000)), int(rng.integers(4000, 12000))]))
+    R = int(rng.integers(1, 5))
+    k = int(rng.choice([1, C, int(rng.integers(1, C + 1))]))
+    kind = str(rng.choice(["wide", "narrow", "few", "crowded", "equal"]))
+    thr = int(rng.choice([0, -3, 1, 2 ** 31 - 1, -(2 ** 31)]))
+    return R, C, k, kind, thr
+
+
+def _logit_rows(synth_lib, kind, R, C, case):
+    s = synth_lib.stream(synth_lib.TAG_MISC, 5000 + case)
+    if kind == "wide":
+        return synth_lib.uniform_i32((R, C), case, s, -(2 ** 31), 2 ** 31 - 1)
+    if kind == "narrow":
+        return synth_lib.uniform_i32((R, C), case, s, -50, 50)
+    if kind == "few":
+        return synth_lib.uniform_i32((R, C), case, s, 0, 2)
+    if kind == "crowded":  # a narrow band between outliers at both ends of the int32 range
+        v = synth_lib.uniform_i32((R, C), case, s, 0, 4095)
+        v[:, 0] = 2 ** 31 - 1
+        v[:, -1] = -(2 ** 31)
+        return v
+    return np.full((R, C), -5, dtype=np.int32)
+
+
+@pytest.mark.parametrize("case", range(100))
+def test_topk_and_threshold_random(lsa, oracle_lib, synth_lib, case):
+    R, C, k, kind, thr = _logit_case(case)
+    say("random logits case", case, R, C, k, kind, thr)
+    rows = _logit_rows(synth_lib, kind, R, C, case)
+    dl = to_dev(rows)
+    got = lsa.lsa_topk_chunks(dl, k).cpu().numpy()
+    assert np.array_equal(got, oracle_lib.topk_chunks(rows.astype(np.int64), k)), (case, R, C, k, kind)
+    ids, counts = lsa.lsa_threshold_chunks(dl, k, thr)
+    ref_ids, ref_counts = oracle_lib.threshold_chunks(rows.astype(np.int64), k, thr)
+    assert np.array_equal(counts.cpu().numpy(), ref_counts), (case, R, C, k, kind, thr)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids), (case, R, C, k, kind, thr)
+
+
+# ------------------------------------------------------------------ token scores
+
+def _token_case(i):
+    rng = np.random.default_rng(2000 + i)
+    k = int(rng.integers(1, 300))
+    C = int(rng.integers(k, 4096))
+    B = int(rng.integers(1, 5))
+    k_tok = int(rng.choice([1, int(rng.integers(1, k * 64 + 1)), k * 64 + 50]))
+    kind = str(rng.choice(["normal", "quarters", "band", "equal"]))
+    split = bool(rng.integers(0, 2))
+    return B, C, k, k_tok, kind, split, rng
+
+
+def _token_scores(synth_lib, kind, B, n, case):
+    s = synth_lib.stream(synth_lib.TAG_MISC, 6000 + case)
+    if kind in ("normal", "quarters"):
+        x = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), case, s)).astype(np.float64)
+        if kind == "quarters":
+            x = np.round(x * 4) / 4
+    elif kind == "band":  # 2^20 + 1 values spread over [1, 2]: the whole list shares its top key bits
+        x = 1.0 + synth_lib.uniform_i32((B, n), case, s, 0, 2 ** 20).astype(np.float64) / 2 ** 20
+    else:
+        x = np.full((B, n), 0.5)
+    x = x.astype(np.float32)
+    if n > 8:  # special values at fixed places
+        x[:, 1] = -0.0
+        x[:, 2] = 0.0
+        x[:, 3] = np.inf
+        x[:, 4] = -np.inf
+        x[:, 5] = np.float32(1e-40)
+        x[:, 6] = np.float32(-1e-40)
+    return np.ascontiguousarray(x)
+
+
+@pytest.mark.parametrize("case", range(80))
+def test_topk_tokens_random(lsa, oracle_lib, synth_lib, monkeypatch, case):
+    B, C, k, k_tok, kind, split, rng = _token_case(case)
+    say("random token case", case, B, C, k, k_tok, kind, split)
+    if split:  # the slice + candidates path wherever the row can be split
+        monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")
+    scores = _token_scores(synth_lib, kind, B, k * 64, case)
+    ids = np.stack([np.sort(synth_lib.choose(k, C, case, synth_lib.stream(synth_lib.TAG_MISC, 6100 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    for b in range(B):
+        r = int(rng.integers(0, 4))
+        if r == 1:    # the context ends inside a listed chunk
+            ctx[b] = int(ids[b, int(rng.integers(0, k))]) * 64 + int(rng.integers(0, 64))
+        elif r == 2:  # no context at all
+            ctx[b] = 0
+    counts = rng.integers(0, k + 1, B).astype(np.int32) if rng.integers(0, 2) else None
+    ref, rc = oracle_lib.topk_tokens(scores, ids, ctx, k_tok, counts=counts)
+    tok, tc = lsa.lsa_topk_tokens(to_dev(scores), to_dev(ids), to_dev(ctx), k_tok,
+                                  counts=None if counts is None else to_dev(counts), workspace="auto")
+    assert np.array_equal(tc.cpu().numpy(), rc), (case, B, C, k, k_tok, kind, split)
+    assert np.array_equal(tok.cpu().numpy(), ref), (case, B, C, k, k_tok, kind, split)
