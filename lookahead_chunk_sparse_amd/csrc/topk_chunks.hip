@@ -822,7 +822,9 @@ hipError_t launch_mode(const TopkArgs& a, int grid, int positions, hipStream_t s
     else if (kpt <= 4) hipLaunchKernelGGL((topk_kernel<4, MODE>), g, block, 0, stream, a);
     else if (kpt <= 8) hipLaunchKernelGGL((topk_kernel<8, MODE>), g, block, 0, stream, a);
     else if (kpt <= 12) hipLaunchKernelGGL((topk_kernel<12, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 13) hipLaunchKernelGGL((topk_kernel<13, MODE>), g, block, 0, stream, a);
     else if (kpt <= 14) hipLaunchKernelGGL((topk_kernel<14, MODE>), g, block, 0, stream, a);
+    else if (kpt <= 15) hipLaunchKernelGGL((topk_kernel<15, MODE>), g, block, 0, stream, a);
     else if (kpt <= 16) hipLaunchKernelGGL((topk_kernel<16, MODE>), g, block, 0, stream, a);
     else if (kpt <= 18) hipLaunchKernelGGL((topk_kernel<18, MODE>), g, block, 0, stream, a);
     else if (kpt <= 20) hipLaunchKernelGGL((topk_kernel<20, MODE>), g, block, 0, stream, a);
