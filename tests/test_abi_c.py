@@ -18,3 +18,19 @@ def test_c_program_against_header(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check: ok" in r.stdout
+
+
+def test_c_decode_driver_compiles(tmp_path):
+    """tests/c/decode_interval.c, the plain-C client the GPU suite runs,
+    compiles warning-free against the header and links against liblsa.so and
+    the HIP runtime alone."""
+    import lookahead_chunk_sparse_amd as lsa
+    exe = tmp_path / "decode_interval"
+    libdir = os.path.dirname(lsa.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                           os.path.join(ROOT, "tests", "c", "decode_interval.c"), "-o", str(exe),
+                           "-L", libdir, "-llsa", "-L", "/opt/rocm/lib", "-lamdhip64",
+                           f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"])
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage:" in r.stderr  # argument check only: no HIP call is made
