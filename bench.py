@@ -480,7 +480,8 @@ def copy_calibration(n_bytes: int, reps: int):
 def score_sweep(nqs, C: int, d_idx: int, launches: int):
     """Batched indexer scoring: nq query rows sharing one key set of C chunks.
     Times the int8-MFMA kernel and the GEMV kernel on the same shapes
-    (selected through the library's dispatch threshold)."""
+    (selected through the library's dispatch threshold), and torch's fill of
+    the same output bytes as the write rate they are held to."""
     import torch
 
     import lookahead_chunk_sparse_amd as lsa
@@ -508,6 +509,20 @@ def score_sweep(nqs, C: int, d_idx: int, launches: int):
             byts = C * d_idx + nq * d_idx + nq * C * 8
             row[path] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 2), "GBs": round(byts / us / 1e3, 1)}
         os.environ.pop("LSA_SCORE_MFMA_MIN_NQ", None)
+        # the write ceiling for these outputs: a device fill of the same bytes
+        for _ in range(5):
+            logits.fill_(0)
+            scores.fill_(0)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(launches):
+            logits.fill_(0)
+            scores.fill_(0)
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / launches
+        row["fill_outputs"] = {"us": round(us, 2), "GBs": round(nq * C * 8 / us / 1e3, 1)}
         row["int8_peak_TOPS"] = 5000.0
         print(json.dumps(row), flush=True)
 
