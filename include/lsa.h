@@ -30,6 +30,20 @@
  *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
  *  - Calls keep no mutable global state and may be issued from several host
  *    threads on different streams.
+ *  - Tuning overrides, read from the environment, choose among kernels and
+ *    launch shapes; none changes a result.  Unset, the library picks:
+ *      LSA_ATTEND_DEPTH        tile ring depth of the attention, 2-4
+ *                              (read once per process)
+ *      LSA_SCORE_MFMA_MIN_NQ   query rows from which lsa_index_score uses
+ *                              the int8 MFMA kernel (default 16)
+ *      LSA_TOPK_STREAM_MIN_C   row length from which the selects stream the
+ *                              row from memory instead of registers
+ *      LSA_TOPK_SPLIT_MIN_N, LSA_TOPK_SPLIT_SLICES
+ *                              when and how lsa_topk_tokens splits long rows;
+ *                              they change what
+ *                              lsa_topk_tokens_workspace_size returns, so set
+ *                              them before querying it
+ *    All but the first are read on every call.
  */
 #ifndef LSA_H
 #define LSA_H
