@@ -34,3 +34,16 @@ def test_c_decode_driver_compiles(tmp_path):
                            f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"])
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage:" in r.stderr  # argument check only: no HIP call is made
+
+
+def test_c_threaded_client_compiles(tmp_path):
+    """tests/c/threaded_calls.c (run by the GPU suite) compiles warning-free
+    with pthreads against the header; it is not run here, since every path
+    of it calls the GPU."""
+    import lookahead_chunk_sparse_amd as lsa
+    libdir = os.path.dirname(lsa.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pthread", "-D__HIP_PLATFORM_AMD__",
+                           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                           os.path.join(ROOT, "tests", "c", "threaded_calls.c"), "-o", str(tmp_path / "threaded_calls"),
+                           "-L", libdir, "-llsa", "-L", "/opt/rocm/lib", "-lamdhip64",
+                           f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"])

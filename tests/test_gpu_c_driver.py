@@ -1,11 +1,14 @@
-"""The decode path driven from a plain C program, tests/c/decode_interval.c,
-through include/lsa.h with HIP runtime memory: no PyTorch in the process
-that runs the kernels.  Two re-selection intervals (a drifting indexer
-query, so the second selection differs from the first), delta pool slots,
-the pull fetch from pinned host memory, and the DMA fetch; every output the
-program writes is checked against the oracle.  The workload is the 32K
+"""The library driven from plain C programs through include/lsa.h, with
+HIP runtime memory and no PyTorch in the process that runs the kernels.
+
+tests/c/decode_interval.c runs two re-selection intervals (a drifting
+indexer query, so the second selection differs from the first) with delta
+pool slots, the pull fetch from pinned host memory and the DMA fetch; every
+output it writes is checked against the oracle.  Its workload is the 32K
 shape (4 requests, 64/8 heads, d = 128, 32 kept chunks) over a ragged
-8,229-token context, so the last chunk is partial."""
+8,229-token context, so the last chunk is partial.
+
+tests/c/threaded_calls.c checks the threading promise of the header."""
 import os
 import subprocess
 
@@ -25,11 +28,11 @@ def say(*a):
     print(*a, flush=True)
 
 
-def _compile(exe: str) -> None:
+def _compile(exe: str, source: str = "decode_interval.c") -> None:
     assert os.path.exists(os.path.join(LIBDIR, "liblsa.so")), "liblsa.so is not built"
-    subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
-                           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
-                           os.path.join(ROOT, "tests", "c", "decode_interval.c"), "-o", exe,
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pthread",
+                           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                           os.path.join(ROOT, "tests", "c", source), "-o", exe,
                            "-L", LIBDIR, "-llsa", "-L", "/opt/rocm/lib", "-lamdhip64",
                            f"-Wl,-rpath,{LIBDIR}", "-Wl,-rpath,/opt/rocm/lib"])
 
@@ -100,3 +103,16 @@ def test_c_program_two_intervals(tmp_path, oracle_lib):
     for b in range(B):
         used = np.union1d(s0[b], s1[b])
         assert np.array_equal(pool[b, used], pool_ref[b, used]), f"pool of request {b}"
+
+
+def test_c_program_threads(tmp_path):
+    """tests/c/threaded_calls.c: four host threads, each on its own stream
+    and workspace, repeat scan -> select -> attend and match a serial run bit
+    for bit; a rejected call's message belongs to its own thread."""
+    exe = str(tmp_path / "threaded_calls")
+    _compile(exe, "threaded_calls.c")
+    say("C threads: 4 threads x 12 repetitions")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    say(r.stdout.strip(), r.stderr.strip())
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "threaded_calls: ok" in r.stdout
