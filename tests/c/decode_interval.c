@@ -1,6 +1,6 @@
 /* Two re-selection intervals of the decode path, driven from plain C11
  * through include/lsa.h with device memory from the HIP runtime and nothing
- * else: no PyTorch, no Python.  tests/test_gpu_c_driver.py writes the inputs,
+ * else: no PyTorch, no Python.  tests/test_gpu_c_client.py writes the inputs,
  * runs this program and checks every file it writes against the oracle.
  *
  * Per interval i (0, then 1), all on one compute stream unless noted:

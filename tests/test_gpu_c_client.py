@@ -45,7 +45,7 @@ def _load(d, name, dtype, shape):
 
 def test_c_program_two_intervals(tmp_path, oracle_lib):
     from synth import workloads as W
-    w = W.WORKLOADS["32k"].replace(name="c-driver", N=8229, steps=128, drift=True)
+    w = W.WORKLOADS["32k"].replace(name="c-client", N=8229, steps=128, drift=True)
     B, C, k, Hq, Hkv, d = w.B, w.C, w.k, w.Hq, w.Hkv, w.d
     P = 2 * k
     q_idx = np.stack([W.indexer_query(w, i) for i in range(2)])          # [2][B][1][d_idx]
@@ -63,7 +63,7 @@ def test_c_program_two_intervals(tmp_path, oracle_lib):
     _compile(exe)
 
     args = [exe, out_dir, B, C, w.d_idx, k, Hq, Hkv, d, repr(w.alpha), repr(w.sm_scale)]
-    say("C driver:", " ".join(str(a) for a in args[2:]))
+    say("C client:", " ".join(str(a) for a in args[2:]))
     r = subprocess.run([str(a) for a in args], capture_output=True, text=True, timeout=120)
     say(r.stdout.strip(), r.stderr.strip())
     assert r.returncode == 0, r.stdout + r.stderr
@@ -87,7 +87,7 @@ def test_c_program_two_intervals(tmp_path, oracle_lib):
 
         ref = oracle_lib.gather_attend(q[i], kv, ids_ref.reshape(B, k), ctx, Hkv, w.sm_scale)
         out = _load(out_dir, f"out{i}.bin", np.float32, (B, Hq, d))
-        say(f"interval {i}:", check_attention(out, ref, f"C driver interval {i}"))
+        say(f"interval {i}:", check_attention(out, ref, f"C client interval {i}"))
         outs.append(out)
         prev_ids, prev_slots = ids_ref.reshape(B, k), slots_ref
     assert not np.array_equal(_load(out_dir, "ids0.bin", np.int32, (B, k)),
