@@ -32,13 +32,13 @@
  *     (paperlayer.ai summary, 2.1 Architecture: non-recalled entries are
  *     evicted to CPU; 3 Experiments / Experimental Setup: recalled chunks are
  *     retrieved from CPU cold storage every tau = 64 steps).
- *  7. Threshold selection (summary 2.1 Architecture, 2.4 Configuration:
- *     sigmoid gating at 0.5 instead of a fixed top-k): the chunks whose logit
- *     exceeds a threshold, capped at k_max by the same order as item 3.
  *  6. Pool slots of a delta fetch (the same passages: only the chunks not
  *     already recalled need fetching): a chunk kept from the previous
  *     selection keeps its slot; the r-th new chunk in ascending id order takes
  *     the r-th lowest slot the previous selection does not hold.
+ *  7. Threshold selection (summary 2.1 Architecture, 2.4 Configuration:
+ *     sigmoid gating at 0.5 instead of a fixed top-k): the chunks whose logit
+ *     exceeds a threshold, capped at k_max by the same order as item 3.
  *  8. Token selection inside the recalled chunks (summary 2.1 Architecture:
  *     after the chunk recall, the model's own token-level scores pick a
  *     fine-grained top-k among the recalled entries only).  The scores are an
