@@ -1,0 +1,173 @@
+"""The seeded input generator (synth/) against the published definitions it
+states.  A generator mistake is invisible to the parity tests (the oracle
+and the HIP path get the same bytes either way), but it would make the
+inputs differ from the recipe the benchmark claims, so it is pinned here:
+
+- SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+  generators", OOPSLA 2014): the first outputs from state 0 as the public
+  reference implementation prints them, and the counter form
+  draw(key, i) = i-th output of the sequence started at state key;
+- Lemire's multiply-shift reduction of the top 32 bits to [lo, hi];
+- Box-Muller normals from 53-bit uniforms, rounded to float and then to
+  bfloat16 with round-to-nearest-even;
+- a partial Fisher-Yates shuffle for draws without replacement.
+
+CPU only; the statistics use fixed seeds and bounds of five standard errors.
+"""
+import math
+
+import numpy as np
+import pytest
+
+M64 = (1 << 64) - 1
+GAMMA = 0x9E3779B97F4A7C15
+
+
+@pytest.fixture(scope="module")
+def synth_mod(synth_lib):
+    return synth_lib
+
+
+class SplitMix64:
+    """The sequential generator as published: add the golden gamma to the
+    state, then return the 64-bit finaliser of the new state."""
+
+    def __init__(self, state: int):
+        self.state = state & M64
+
+    @staticmethod
+    def _finalise(z: int) -> int:
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
+        return z ^ (z >> 31)
+
+    def next(self) -> int:
+        self.state = (self.state + GAMMA) & M64
+        return self._finalise(self.state)
+
+
+def test_splitmix64_reference_outputs(synth_mod):
+    # the first three outputs of SplitMix64 from state 0
+    assert [synth_mod.draw(0, i) for i in range(3)] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+                                                       0x06C45D188009454F]
+    g = SplitMix64(0)
+    assert [g.next() for _ in range(3)] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+@pytest.mark.parametrize("seed, strm", [(0, 0), (0, 5), (7, 3), (2 ** 40 + 11, 2 ** 20 + 1)])
+def test_counter_form_is_the_sequence(synth_mod, seed, strm):
+    """key(seed, stream) is output `stream` of the sequence from state seed,
+    and element i of a stream is output i of the sequence from state key."""
+    g = SplitMix64(seed)
+    for _ in range(strm):
+        g.next()
+    k = synth_mod.key(seed, strm)
+    assert k == g.next()
+    g = SplitMix64(k)
+    seq = np.array([g.next() for _ in range(1000)], dtype=np.uint64)
+    assert np.array_equal(synth_mod.raw_u64(1000, seed, strm), seq)
+    # any window of the stream on its own (order-free fills)
+    assert np.array_equal(synth_mod.raw_u64(100, seed, strm, first=437), seq[437:537])
+
+
+@pytest.mark.parametrize("lo, hi", [(-16, 15), (0, 2), (-50, 50), (0, 4095), (-(2 ** 31), 2 ** 31 - 1), (5, 5)])
+def test_uniform_is_lemire_reduction(synth_mod, lo, hi):
+    n, seed, strm = 5000, 3, synth_mod.stream(synth_mod.TAG_MISC, 901)
+    raw = synth_mod.raw_u64(n, seed, strm)
+    span = hi - lo + 1
+    want = np.array([lo + (((int(d) >> 32) * span) >> 32) for d in raw], dtype=np.int64)
+    got = synth_mod.uniform_i32((n,), seed, strm, lo, hi).astype(np.int64)
+    assert np.array_equal(got, want)
+    assert got.min() >= lo and got.max() <= hi
+    if -128 <= lo and hi <= 127:
+        assert np.array_equal(synth_mod.uniform_i8((n,), seed, strm, lo, hi).astype(np.int64), want)
+
+
+def test_uniform_counts(synth_mod):
+    n, bins = 200_000, 10
+    v = synth_mod.uniform_i32((n,), 1, synth_mod.stream(synth_mod.TAG_MISC, 902), 0, bins - 1)
+    counts = np.bincount(v, minlength=bins)
+    p = 1.0 / bins
+    assert (np.abs(counts - n * p) <= 5 * math.sqrt(n * p * (1 - p))).all(), counts
+
+
+def _bf16_rne(x: float) -> int:
+    """float32 value -> bfloat16 bits, round to nearest even (no NaNs here)."""
+    u = int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+
+
+@pytest.mark.parametrize("scale", [1.0, 4.0])
+def test_normal_is_box_muller(synth_mod, scale):
+    n, seed, strm = 4096, 5, synth_mod.stream(synth_mod.TAG_MISC, 903)
+    raw = [int(d) for d in synth_mod.raw_u64(n, seed, strm)]
+    want = []
+    for p in range(n // 2):
+        u1 = ((raw[2 * p] >> 11) + 1) * 2.0 ** -53     # (0, 1]
+        u2 = (raw[2 * p + 1] >> 11) * 2.0 ** -53       # [0, 1)
+        r = math.sqrt(-2.0 * math.log(u1))
+        th = 2.0 * math.pi * u2
+        want += [_bf16_rne(r * math.cos(th) * scale), _bf16_rne(r * math.sin(th) * scale)]
+    got = synth_mod.normal_bf16((n,), seed, strm, scale=scale)
+    assert np.array_equal(got, np.array(want, dtype=np.uint16))
+
+
+def test_normal_statistics(synth_mod):
+    n = 1 << 20
+    x = synth_mod.bf16_bits_to_f32(synth_mod.normal_bf16((n,), 9, synth_mod.stream(synth_mod.TAG_MISC, 904)))
+    x = x.astype(np.float64)
+    se = 1.0 / math.sqrt(n)
+    assert abs(x.mean()) <= 5 * se
+    assert abs(x.var() - 1.0) <= 5 * math.sqrt(2.0) * se + 2e-3  # + bf16 rounding of each value
+    tail = float(np.mean(np.abs(x) > 2.0))
+    assert abs(tail - 0.0455003) <= 5 * math.sqrt(0.0455 * 0.9545 / n) + 2e-3
+
+
+def test_normal_windows_and_runs(synth_mod):
+    """Order-free: a window, or a set of runs, equals the same elements of
+    one long fill (how chunks of a large store are regenerated)."""
+    seed, strm = 2, synth_mod.stream(synth_mod.TAG_MISC, 905)
+    full = synth_mod.normal_bf16((10_000,), seed, strm)
+    assert np.array_equal(synth_mod.normal_bf16((333,), seed, strm, first=4567), full[4567:4900])
+    assert np.array_equal(synth_mod.normal_bf16((1,), seed, strm, first=9999), full[9999:])
+    firsts = np.array([0, 1001, 7777, 3], dtype=np.int64)
+    runs = synth_mod.normal_bf16_runs(firsts, 64, seed, strm)
+    assert np.array_equal(runs.reshape(4, 64), np.stack([full[f:f + 64] for f in firsts]))
+
+
+def _fisher_yates(count, n, excluded, draws):
+    pool = [i for i in range(n) if excluded is None or not excluded[i]]
+    m = len(pool)
+    out = []
+    for j in range(min(count, m)):
+        r = j + (((int(draws[j]) >> 32) * (m - j)) >> 32)
+        pool[j], pool[r] = pool[r], pool[j]
+        out.append(pool[j])
+    return out
+
+
+@pytest.mark.parametrize("count, n, with_excluded", [(26, 512, False), (300, 300, False), (5, 40, True), (40, 40, True)])
+def test_choose_is_partial_fisher_yates(synth_mod, count, n, with_excluded):
+    seed, strm = 4, synth_mod.stream(synth_mod.TAG_MISC, 906 + n)
+    excluded = None
+    if with_excluded:
+        excluded = np.zeros(n, dtype=np.uint8)
+        excluded[::3] = 1
+    got = synth_mod.choose(count, n, seed, strm, excluded)
+    allowed = n if excluded is None else int((excluded == 0).sum())
+    draws = synth_mod.raw_u64(max(min(count, allowed), 1), seed, strm)
+    want = _fisher_yates(count, n, excluded, draws)
+    assert got.tolist() == want  # the same draws, in draw order
+    assert len(set(got.tolist())) == len(got) == min(count, allowed)
+    if excluded is not None:
+        assert not excluded[got].any()
+
+
+def test_choose_is_uniform(synth_mod):
+    """Every position is chosen with probability count/n."""
+    n, count, trials = 64, 8, 4000
+    hits = np.zeros(n)
+    for t in range(trials):
+        hits[synth_mod.choose(count, n, 6, synth_mod.stream(synth_mod.TAG_MISC, 10_000 + t))] += 1
+    p = count / n
+    assert (np.abs(hits - trials * p) <= 5 * math.sqrt(trials * p * (1 - p))).all()
