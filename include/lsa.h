@@ -112,7 +112,7 @@ lsa_status lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, int32_t B, 
  * chunk order.  The set is unique, so the output is bit-exact.
  *
  *  logits     device int32 [R][C]   (any int32 values)
- *  R >= 1, 1 <= C <= 2^30, 1 <= k <= C (rows up to 65536 chunks keep their
+ *  1 <= R < 2^22, 1 <= C <= 2^30, 1 <= k <= C (rows up to 65536 chunks keep their
  *  keys in registers; longer ones stream from memory in every pass)
  *  chunk_ids  device int32 [R][k]   output, ascending within each row
  *  stream     HIP stream
@@ -138,7 +138,7 @@ lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t 
  * integer logit whose score does not exceed s.
  *
  *  logits      device int32 [R][C]
- *  R >= 1, 1 <= C <= 2^30, 1 <= k_max <= C
+ *  1 <= R < 2^22, 1 <= C <= 2^30, 1 <= k_max <= C
  *  chunk_ids   device int32 [R][k_max] output
  *  counts      device int32 [R] output, chunks kept per row (0..k_max)
  */
@@ -165,7 +165,8 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
  *  chunk_ids   device int32 [B][k]
  *  counts      device int32 [B] entries in use, or NULL (all k)
  *  ctx_len     device int32 [B]
- *  B >= 1, k >= 1 with k*64 <= 2^30, k_tok >= 1
+ *  B >= 1, k >= 1 with k*64 <= 2^30, k_tok >= 1; B < 2^22, and B times
+ *  the slices < 2^22 when the list is split (LSA_ERR_UNSUPPORTED otherwise)
  *  tok         device int32 [B][k_tok] output: list positions
  *  tok_counts  device int32 [B] output: positions kept per request
  *  workspace   device buffer of lsa_topk_tokens_workspace_size(B, k, k_tok)
@@ -190,7 +191,8 @@ size_t lsa_topk_tokens_workspace_size(int32_t B, int32_t k, int32_t k_tok);
 /*
  * Number of bytes of workspace lsa_gather_attend needs for these sizes and
  * this split count (n_split = 0: the library's own choice).  Returns 0 when
- * no workspace is needed, (size_t)-1 when the arguments are invalid.
+ * no workspace is needed, (size_t)-1 when the arguments are invalid or the
+ * launch would exceed 2^24 split workgroups (B*Hkv*min(n_split, k)).
  */
 size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
                                         int32_t n_split);
@@ -240,7 +242,8 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *             passes the length of the offloadable history there.
  *  seg_len    device int32 [B]: tokens of the segment in use (<= S_max)
  *  S_max      segment capacity, a multiple of 64 (ignored without seg_kv)
- *  B >= 1; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16; d = 64 or 128; 1 <= k
+ *  B >= 1; Hq % Hkv == 0; 1 <= Hq/Hkv <= 16; d = 64 or 128; 1 <= k;
+ *  B*Hq < 2^24
  *  sm_scale   softmax scale, normally 1/sqrt(d)
  *  workspace  device buffer of at least
  *             lsa_gather_attend_workspace_size(B, Hq, Hkv, d, k, n_split)
@@ -248,7 +251,8 @@ int32_t lsa_gather_attend_default_splits(int32_t B, int32_t Hkv, int32_t k);
  *             scratch for the per-split partial results, no state is kept
  *             in it between calls.  Calls sharing a workspace must not
  *             overlap in time (same stream, or otherwise ordered).
- *  n_split    chunk-list splits per (request, KV head); 0 = library choice
+ *  n_split    chunk-list splits per (request, KV head); 0 = library choice;
+ *             B*Hkv*min(n_split, k) <= 2^24 (LSA_ERR_UNSUPPORTED otherwise)
  *  out        device fp32 [B][Hq][d]
  *  stream     HIP stream
  * q, kv and out need 16-byte alignment.
@@ -344,7 +348,7 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
  *  slots      device int32 [B][k] or NULL (k <= P then)
  *  pool_kv    device bf16 [B][P][2][Hkv][64][d]
  *  B, Hkv, k >= 1; d = 64 or 128
- *  grid       workgroups of the gather (0 = 16).  The link is the bound:
+ *  grid       workgroups of the gather, < 2^24 (0 = 16).  The link is the bound:
  *             8-16 workgroups already reach it (about 57 GB/s on MI355X),
  *             and every workgroup parked on long host-link reads slows the
  *             kernels that share its compute unit
@@ -380,6 +384,7 @@ lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32
  *  prev_slots  device int32 [B][n_prev], distinct within a row, in [0, P)
  *  n_prev      0 for the first selection (every chunk is new)
  *  new_ids     device int32 [B][k], ascending within each row
+ *  B           requests, 1 <= B < 2^22
  *  P           pool slots per request, >= n_prev + k;
  *              (n_prev + P) * 4 + P <= 65536 (LSA_ERR_UNSUPPORTED otherwise)
  *  new_slots, fetch_slots  device int32 [B][k] outputs

@@ -178,7 +178,10 @@ int score_mfma_min_nq() {
 template <int DIDX>
 hipError_t launch(const int8_t* q, const int8_t* keys, int B, int nq, int C, float alpha, int32_t* logits,
                   float* scores, hipStream_t stream) {
-    if (DIDX % 64 == 0 && nq >= score_mfma_min_nq())
+    // The MFMA grid has at least one workgroup per (request, 64 query rows):
+    // beyond 2^22 of those its work-item count would pass 32 bits, and the
+    // GEMV kernel (a capped grid that strides over the rows) takes over.
+    if (DIDX % 64 == 0 && nq >= score_mfma_min_nq() && (int64_t)B * ((nq + 63) / 64) < ((int64_t)1 << 22))
         return launch_mfma<(DIDX % 64 == 0 ? DIDX : 64)>(q, keys, B, nq, C, alpha, logits, scores, stream);
     constexpr int RPB = kThreads / (DIDX / 16);
     const int64_t rows = (int64_t)B * C;

@@ -40,6 +40,11 @@ lsa_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// A launch counts its work-items (workgroups x threads) in 32 bits: these
+// bound the workgroups of the launches whose count follows the arguments.
+constexpr int64_t kMaxRowGroups = (int64_t)1 << 22;    // 1024-thread top-k / pool workgroups
+constexpr int64_t kMaxSplitGroups = (int64_t)1 << 24;  // 256-thread attention workgroups
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +85,7 @@ lsa_status lsa_topk_chunks(const int32_t* logits, int32_t R, int32_t C, int32_t 
     if (R < 1 || C < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "R=%d C=%d must be >= 1", R, C);
     if (k < 1 || k > C) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d must be in [1, C=%d]", k, C);
     if (C > lsa::kTopkMaxC) return fail(LSA_ERR_UNSUPPORTED, "C=%d exceeds %d", C, lsa::kTopkMaxC);
+    if (R >= kMaxRowGroups) return fail(LSA_ERR_UNSUPPORTED, "R=%d: must be < 2^22", R);
     if (!aligned(logits, 4) || !aligned(chunk_ids, 4))
         return fail(LSA_ERR_INVALID_ARGUMENT, "logits and chunk_ids need 4-byte alignment");
     hipError_t e = lsa::launch_topk(logits, R, C, k, chunk_ids, 0, nullptr, stream);
@@ -94,6 +100,7 @@ lsa_status lsa_threshold_chunks(const int32_t* logits, int32_t R, int32_t C, int
     if (R < 1 || C < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "R=%d C=%d must be >= 1", R, C);
     if (k_max < 1 || k_max > C) return fail(LSA_ERR_INVALID_ARGUMENT, "k_max=%d must be in [1, C=%d]", k_max, C);
     if (C > lsa::kTopkMaxC) return fail(LSA_ERR_UNSUPPORTED, "C=%d exceeds %d", C, lsa::kTopkMaxC);
+    if (R >= kMaxRowGroups) return fail(LSA_ERR_UNSUPPORTED, "R=%d: must be < 2^22", R);
     if (!aligned(logits, 4) || !aligned(chunk_ids, 4) || !aligned(counts, 4))
         return fail(LSA_ERR_INVALID_ARGUMENT, "logits, chunk_ids and counts need 4-byte alignment");
     hipError_t e = lsa::launch_topk(logits, R, C, k_max, chunk_ids, logit_threshold, counts, stream);
@@ -109,6 +116,8 @@ static lsa_status check_attend_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t
     if (d != 64 && d != 128) return fail(LSA_ERR_UNSUPPORTED, "d=%d: supported head dims are 64 and 128", d);
     if ((int64_t)B * Hq >= ((int64_t)1 << 31) || (int64_t)B * k >= ((int64_t)1 << 31))
         return fail(LSA_ERR_INVALID_ARGUMENT, "B*Hq and B*k must be < 2^31");
+    if ((int64_t)B * Hq >= ((int64_t)1 << 24))
+        return fail(LSA_ERR_UNSUPPORTED, "B*Hq=%lld: must be < 2^24", (long long)B * Hq);
     return LSA_OK;
 }
 
@@ -144,6 +153,9 @@ lsa_status lsa_topk_tokens(const float* scores, const int32_t* chunk_ids, const 
         if (!aligned(workspace, 256)) return fail(LSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
         if (need == 0) workspace = nullptr;  // no split for these sizes
     }
+    const int64_t groups = (int64_t)B * (workspace ? lsa::topk_tokens_split(k, k_tok).slices : 1);
+    if (groups >= kMaxRowGroups)
+        return fail(LSA_ERR_UNSUPPORTED, "%lld select workgroups (B times the slices): must be < 2^22", (long long)groups);
     hipError_t e = lsa::launch_topk_tokens(scores, chunk_ids, counts, ctx_len, B, k, k_tok, tok, tok_counts, workspace,
                                            stream);
     if (e != hipSuccess) return hip_fail(e, "token top-k launch");
@@ -154,6 +166,7 @@ size_t lsa_gather_attend_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int3
     if (check_attend_shape(B, Hq, Hkv, d, k) != LSA_OK || n_split < 0) return (size_t)-1;
     if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, k);
     if (n_split > k) n_split = k;
+    if ((int64_t)B * Hkv * n_split >= kMaxSplitGroups) return (size_t)-1;
     return lsa::attend_workspace_bytes(B, Hkv, Hq / Hkv, d, n_split);
 }
 
@@ -189,6 +202,8 @@ static lsa_status gather_attend_impl(const uint16_t* q, const uint16_t* kv, int6
     }
     if (n_split == 0) n_split = lsa::attend_default_splits(B, Hkv, entries);
     if (n_split > entries) n_split = entries;
+    if ((int64_t)B * Hkv * n_split >= kMaxSplitGroups)
+        return fail(LSA_ERR_UNSUPPORTED, "B*Hkv*n_split=%lld workgroups: must be < 2^24", (long long)B * Hkv * n_split);
     const int G = Hq / Hkv;
     const size_t need = lsa::attend_workspace_bytes(B, Hkv, G, d, n_split);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -303,8 +318,8 @@ lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32
                                  int32_t grid, hipStream_t stream) {
     if (!host_kv || !chunk_ids || !pool_kv)
         return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv, chunk_ids and pool_kv are required");
-    if (C < 1 || P < 1 || B < 1 || Hkv < 1 || k < 1 || grid < 0)
-        return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, k must be >= 1 and grid >= 0");
+    if (C < 1 || P < 1 || B < 1 || Hkv < 1 || k < 1 || grid < 0 || grid >= (1 << 24))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, k must be >= 1 and 0 <= grid < 2^24");
     if (d != 64 && d != 128) return fail(LSA_ERR_UNSUPPORTED, "d=%d: supported head dims are 64 and 128", d);
     if (!slots && k > P) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d > P=%lld with default slots", k, (long long)P);
     if ((int64_t)B * k >= ((int64_t)1 << 31)) return fail(LSA_ERR_INVALID_ARGUMENT, "B*k must be < 2^31");
@@ -336,6 +351,7 @@ lsa_status lsa_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, i
     if (!new_ids || !new_slots || !fetch_slots || (n_prev > 0 && (!prev_ids || !prev_slots)))
         return fail(LSA_ERR_INVALID_ARGUMENT, "new_ids, new_slots, fetch_slots (and prev_* when n_prev > 0) are required");
     if (B < 1 || k < 1 || n_prev < 0) return fail(LSA_ERR_INVALID_ARGUMENT, "B, k must be >= 1 and n_prev >= 0");
+    if (B >= kMaxRowGroups) return fail(LSA_ERR_UNSUPPORTED, "B=%d: must be < 2^22", B);
     if (P < (int64_t)n_prev + k)
         return fail(LSA_ERR_INVALID_ARGUMENT, "P=%lld must be >= n_prev + k = %d", (long long)P, n_prev + k);
     if (P > INT32_MAX || lsa::pool_assign_lds_bytes(n_prev, (int)P) > 65536)
