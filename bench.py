@@ -37,6 +37,14 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 METRIC = "LSA decode steps/s + achieved HBM GB/s (fraction of peak), 128K ctx batch 16"
+
+
+def metric_for(w) -> str:
+    """The headline metric for the 128K workload; the same measure, named
+    for its own context and batch, for the others."""
+    if w.name == "128k":
+        return METRIC
+    return f"LSA decode steps/s + achieved HBM GB/s (fraction of peak), {w.name.upper()} ctx batch {w.B}"
 KERNEL_SRC = os.path.join(ROOT, "lookahead_chunk_sparse_amd", "csrc", "gather_attend.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_128k_traffic.json")
 
@@ -384,7 +392,7 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
     splits = dec.n_split or lsa_gather_attend_default_splits(w.B, w.Hkv, entries)
     step_b = a_bytes + w.B * w.k * 64 * 4 + (w.B * w.C * w.d_idx) // w.tau  # + token scores read by the top-k
     print(json.dumps({
-        "metric": METRIC, "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "metric": metric_for(w), "value": round(steps_s, 2), "unit": "steps/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
@@ -656,7 +664,7 @@ def main():
     if args.segment:
         layer_txt += f", plus {args.segment} resident tokens per request in the same softmax"
     result = {
-        "metric": METRIC,
+        "metric": metric_for(w),
         "value": round(steps_s, 2),
         "unit": "steps/s",
         "n_gpus": 1,
