@@ -107,10 +107,17 @@ def test_host_tier_graph_replays_match_eager():
                 assert np.array_equal(outs[i][t].cpu().numpy(), eager[i][t]), f"replay {rep}, interval {i}, step {t}"
 
 
-def test_token_stage_graph_replays_match_eager():
+@pytest.mark.parametrize("split", [False, True])
+def test_token_stage_graph_replays_match_eager(monkeypatch, split):
     """Chunk selection, then per step the token top-k and the token-list
-    attention, captured in one graph: every replay gives the eager bits."""
+    attention, captured in one graph: every replay gives the eager bits.
+    split=True forces the slices + candidates select (two launches and a
+    workspace per step), as long recalls take it."""
     import torch
+
+    if split:  # read when the workspace is sized and at every call, so set before the decoder exists
+        monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")
+        monkeypatch.setenv("LSA_TOPK_SPLIT_SLICES", "4")
 
     import synth
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
@@ -120,6 +127,7 @@ def test_token_stage_graph_replays_match_eager():
     dev = torch.device("cuda")
     dec = LsaDecoder(k_idx=to_dev(W.indexer_keys(w)), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k,
                      alpha=w.alpha, kv=W.device_kv_store(w, dev), token_topk=300)
+    assert (dec.tok_workspace is not None) == split
     steps = 6
     qs = [to_dev_bf16(W.attn_query(w, t)) for t in range(steps)]
     sc = [to_dev(np.ascontiguousarray(synth.bf16_bits_to_f32(
