@@ -169,37 +169,89 @@ def time_attention_launches(dec, w, q_all, n_launches: int):
     return statistics.mean(ms), statistics.median(ms), ms
 
 
-def cpu_baseline(w, budget_s: float):
+def host_cores() -> int:
+    """The host threads this process may use: OMP_NUM_THREADS where it is set
+    (the machine's CPU share for this GPU), else the affinity mask's size."""
+    return int(os.environ.get("OMP_NUM_THREADS", 0) or 0) or len(os.sched_getaffinity(0))
+
+
+def _omp_threads(n: int | None):
+    """Set the OpenMP thread count of the oracle's runtime (the libgomp the
+    oracle library links); None restores host_cores()."""
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    gomp.omp_set_num_threads(int(n) if n else host_cores())
+
+
+def cpu_baseline(w, budget_s: float, threads: int | None = None):
     """The oracle on a bounded sample of the same workload: one re-selection
-    (scan + top-k over every request) and as many full attention steps (all
-    requests, all heads) as fit in the time budget.  Returns steps/s scaled
-    from the sample, plus the sample's description."""
+    (scan + top-k over every request) and full attention steps (all heads)
+    over the first nb requests, nb chosen so a step fits the budget, repeated
+    while the budget lasts.  steps/s is scaled to the whole batch
+    (attention time x B/nb).  threads: OpenMP threads (None: every core of
+    this process's affinity)."""
     import numpy as np
 
     import oracle
     from synth import workloads as W
 
-    K = W.indexer_keys(w)
-    q_idx = W.indexer_query(w, 0)
-    t0 = time.perf_counter()
-    _, _, ids = oracle.select(q_idx, K, w.k, w.alpha)
-    t_sel = time.perf_counter() - t0
-    kv_sel = np.stack([W.kv_chunks(w, b, ids[b]) for b in range(w.B)])  # not timed: input placement
-    slots = np.tile(np.arange(w.k, dtype=np.int32), (w.B, 1))
-    ctx = W.ctx_lens(w)
-    t_att, n = 0.0, 0
-    while n < 64 and (n == 0 or t_sel + t_att < budget_s):
-        q = W.attn_query(w, n)
+    n_thr = threads or host_cores()
+    oracle.lib()
+    _omp_threads(n_thr)
+    try:
+        K = W.indexer_keys(w)
+        q_idx = W.indexer_query(w, 0)
         t0 = time.perf_counter()
-        oracle.gather_attend(q, kv_sel, ids, ctx, w.Hkv, w.sm_scale, slots=slots)
-        t_att += time.perf_counter() - t0
-        n += 1
-    per_step = t_att / n + t_sel / w.tau
-    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{w.name}: 1 re-selection (B={w.B}, C={w.C}) in {t_sel:.2f}s + {n} full attention "
-                       f"steps (B={w.B}, Hq={w.Hq}, k={w.k} chunks) in {t_att:.2f}s; steps/s = "
-                       f"1/(attention s/step + re-selection s/{w.tau})")}
+        _, _, ids = oracle.select(q_idx, K, w.k, w.alpha)
+        t_sel = time.perf_counter() - t0
+        ctx = W.ctx_lens(w)
+        slots = np.tile(np.arange(w.k, dtype=np.int32), (w.B, 1))
+        # one request first, to size the sample
+        nb = 1
+        kv_sel = np.stack([W.kv_chunks(w, b, ids[b]) for b in range(nb)])  # not timed: input placement
+        q = W.attn_query(w, 0)
+        t0 = time.perf_counter()
+        oracle.gather_attend(q[:nb], kv_sel, ids[:nb], ctx[:nb], w.Hkv, w.sm_scale, slots=slots[:nb])
+        t_one = time.perf_counter() - t0
+        nb = int(max(1, min(w.B, (0.5 * budget_s) // max(t_one, 1e-6))))
+        kv_sel = np.stack([W.kv_chunks(w, b, ids[b]) for b in range(nb)])
+        t_att, n = 0.0, 0
+        while n < 64 and (n == 0 or t_sel + t_att < budget_s):
+            q = W.attn_query(w, n)
+            t0 = time.perf_counter()
+            oracle.gather_attend(q[:nb], kv_sel, ids[:nb], ctx[:nb], w.Hkv, w.sm_scale, slots=slots[:nb])
+            t_att += time.perf_counter() - t0
+            n += 1
+    finally:
+        _omp_threads(None)
+    per_step = (t_att / n) * (w.B / nb) + t_sel / w.tau
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": n_thr, "kind": "oracle",
+            "sample": (f"{w.name}: 1 re-selection (B={w.B}, C={w.C}) in {t_sel:.2f}s + {n} attention steps over "
+                       f"{nb} of {w.B} requests (Hq={w.Hq}, k={w.k} chunks) in {t_att:.2f}s on {n_thr} thread(s); "
+                       f"steps/s = 1/(attention s/step x {w.B}/{nb} + re-selection s/{w.tau})")}
+
+
+def timed_runs(run, reps: int, stream=None):
+    """Milliseconds of each of `reps` runs of run() (each one exactly the
+    timed steps), HIP events on the stream the work goes to, with a full
+    synchronisation before and after every run."""
+    import torch
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def spread(ms: list) -> dict:
+    """Median, min and max of repeated timings, and the spread max/min - 1."""
+    return {"repeats": len(ms), "median_ms": round(statistics.median(ms), 5), "min_ms": round(min(ms), 5),
+            "max_ms": round(max(ms), 5), "spread": round(max(ms) / min(ms) - 1.0, 4)}
 
 
 def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_split: int = 0, delta=None):
@@ -303,7 +355,7 @@ def token_attend_bytes(w, k_tok: int) -> int:
     return kv + w.B * w.Hq * w.d * (2 + 4) + w.B * k_tok * 4 + w.B * w.k * 4
 
 
-def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
+def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int, repeats: int = 5):
     """Two-stage selection: chunks by the memory indexer every tau steps,
     then at every step the k_tok best tokens of the recalled chunks by a
     per-step token score (synthetic, bf16-rounded normals; the model's own
@@ -351,14 +403,8 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
     if warmup:
         graph(warmup).replay()
     g = graph(steps)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / steps
+    ms_runs = timed_runs(g.replay, repeats)
+    ms_per_step = statistics.median(ms_runs) / steps
     steps_s = 1000.0 / ms_per_step
 
     # the two per-step kernels, event-timed on the stream they run on
@@ -400,7 +446,9 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int):
                          f"heads, head dim {w.d}, top-{w.k} of {w.C} chunks every {w.tau} steps, then the top "
                          f"{k_tok} of their {w.k * 64} tokens by a per-step token score"),
             "global_batch": w.B, "seq_len": w.N, "retained_chunks": w.k, "retained_tokens": k_tok,
-            "n_split": splits, "timing": "hipGraph replay of all steps", "tokens_per_s": round(steps_s * w.B, 1),
+            "n_split": splits, "tokens_per_s": round(steps_s * w.B, 1),
+            "timing": f"hipGraph replay of all steps; value from the median of {repeats} timed runs of exactly "
+                      f"{steps} steps", "timed_runs": spread(ms_runs),
             "step_bytes": step_b, "step_GBs": round(step_b * steps_s / 1e9, 1),
             "token_topk_us": round(topk_ms * 1e3, 2), "token_attend_us": round(att_ms * 1e3, 2),
         },
@@ -501,8 +549,8 @@ def score_sweep(nqs, C: int, d_idx: int, launches: int):
         logits = torch.empty((1, nq, C), dtype=torch.int32, device=dev)
         scores = torch.empty((1, nq, C), dtype=torch.float32, device=dev)
         row = {"nq": nq, "C": C, "d_idx": d_idx}
-        for path, thr in (("gemv", "1000000000"), ("mfma", "1")):
-            os.environ["LSA_SCORE_MFMA_MIN_NQ"] = thr
+        for path, thr in (("gemv", 1000000000), ("mfma", 1)):
+            lsa.lsa_set_tuning("score_mfma_min_nq", thr)
             for _ in range(5):
                 lsa.lsa_index_score(q, K, 1.0 / (16 * d_idx), logits=logits, scores=scores)
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -516,7 +564,7 @@ def score_sweep(nqs, C: int, d_idx: int, launches: int):
             ops = 2.0 * nq * C * d_idx
             byts = C * d_idx + nq * d_idx + nq * C * 8
             row[path] = {"us": round(us, 2), "TOPS": round(ops / us / 1e6, 2), "GBs": round(byts / us / 1e3, 1)}
-        os.environ.pop("LSA_SCORE_MFMA_MIN_NQ", None)
+        lsa.lsa_set_tuning("score_mfma_min_nq", 0)
         # the write ceiling for these outputs: a device fill of the same bytes
         for _ in range(5):
             logits.fill_(0)
@@ -543,7 +591,9 @@ def main():
     ap.add_argument("--workload", default="128k")
     ap.add_argument("--n-split", type=int, default=0, help="attention splits per (request, KV head); 0 = library")
     ap.add_argument("--kernel-launches", type=int, default=200, help="event-timed attention launches")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--repeats", type=int, default=5, help="timed runs of exactly --steps steps (median reported)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the all-core cpu_baseline (the 1-thread one gets 0.6x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
@@ -588,7 +638,7 @@ def main():
     if args.drift:
         w = w.replace(drift=True, n_golden=min(w.n_golden, w.C // max(1, (args.steps + args.warmup) // w.tau + 1)))
     if args.token_topk:
-        token_stage_bench(w, args.steps, args.warmup, args.token_topk, args.n_split)
+        token_stage_bench(w, args.steps, args.warmup, args.token_topk, args.n_split, args.repeats)
         return
     if w.host_tier:
         host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
@@ -630,22 +680,18 @@ def main():
         g = capture(dec, w, q_all, qidx, args.steps, out)
     torch.cuda.synchronize()
 
-    # ---- timed: exactly K steps ----
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # ---- timed: exactly K steps, in each of --repeats runs ----
     t_wall = time.perf_counter()
-    start.record()
     if args.eager:
-        enqueue_steps(dec, w, q_all, qidx, args.steps, out)
+        ms_runs = timed_runs(lambda: enqueue_steps(dec, w, q_all, qidx, args.steps, out), args.repeats)
     else:
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
+        ms_runs = timed_runs(g.replay, args.repeats)
     t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(end)
+    ms_total = statistics.median(ms_runs)
     ms_per_step = ms_total / args.steps
     steps_s = 1000.0 / ms_per_step
-    log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {t_wall * 1e3:.2f} ms)")
+    log(f"[bench] {args.repeats} runs of {args.steps} steps: median {ms_total:.3f} ms, min {min(ms_runs):.3f}, "
+        f"max {max(ms_runs):.3f} (wall {t_wall * 1e3:.1f} ms for all runs)")
 
     # ---- the dominant kernel, event-timed on its own stream ----
     mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
@@ -685,7 +731,9 @@ def main():
             "retained_chunks": w.k,
             "resident_segment_tokens": args.segment,
             "n_split": splits,
-            "timing": "eager launches" if args.eager else "hipGraph replay of all steps",
+            "timing": ("eager launches" if args.eager else "hipGraph replay of all steps")
+                      + f"; value from the median of {args.repeats} timed runs of exactly {args.steps} steps",
+            "timed_runs": spread(ms_runs),
             "tokens_per_s": round(steps_s * w.B, 1),
             "step_bytes": sb,
             "step_GBs": round(sb * steps_s / 1e9, 1),
@@ -710,8 +758,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline and not args.segment:  # the oracle sample has no segment
-        log("[bench] timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        log("[bench] timing the CPU oracle on a bounded sample (all cores, then 1 thread) ...")
+        cb = cpu_baseline(w, args.cpu_budget)
+        cb["single_thread"] = cpu_baseline(w, 0.6 * args.cpu_budget, threads=1)
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
 

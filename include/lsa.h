@@ -28,22 +28,11 @@
  *    range and distinct).
  *  - A chunk is LSA_CHUNK_TOKENS = 64 consecutive tokens.
  *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
- *  - Calls keep no mutable global state and may be issued from several host
- *    threads on different streams.
- *  - Tuning overrides, read from the environment, choose among kernels and
- *    launch shapes; none changes a result.  Unset, the library picks:
- *      LSA_ATTEND_DEPTH        tile ring depth of the attention, 2-4
- *                              (read once per process)
- *      LSA_SCORE_MFMA_MIN_NQ   query rows from which lsa_index_score uses
- *                              the int8 MFMA kernel (default 16)
- *      LSA_TOPK_STREAM_MIN_C   row length from which the selects stream the
- *                              row from memory instead of registers
- *      LSA_TOPK_SPLIT_MIN_N, LSA_TOPK_SPLIT_SLICES
- *                              when and how lsa_topk_tokens splits long rows;
- *                              they change what
- *                              lsa_topk_tokens_workspace_size returns, so set
- *                              them before querying it
- *    All but the first are read on every call.
+ *  - Calls keep no mutable global state (the tuning overrides below are per
+ *    thread) and may be issued from several host threads on different
+ *    streams.
+ *  - Tuning knobs (lsa_tuning below) choose among kernels and launch shapes;
+ *    none changes a result.
  */
 #ifndef LSA_H
 #define LSA_H
@@ -66,6 +55,37 @@ typedef enum lsa_status {
     LSA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required */
     LSA_ERR_HIP = 4               /* a HIP launch or copy failed */
 } lsa_status;
+
+/*
+ * Tuning knobs.  The value in effect for a call is the calling thread's
+ * override (lsa_set_tuning), else the environment variable named beside the
+ * knob (read once per process, at the library's first use of any knob), else
+ * the library's own choice.  No knob changes a result; the top-k split knobs
+ * change what lsa_topk_tokens_workspace_size returns, so a thread sets them
+ * before querying it.
+ */
+typedef enum lsa_tuning {
+    LSA_TUNE_ATTEND_DEPTH = 0,      /* LSA_ATTEND_DEPTH: register ring depth of the
+                                       attention's tile loads, 2-4 (default 2) */
+    LSA_TUNE_SCORE_MFMA_MIN_NQ = 1, /* LSA_SCORE_MFMA_MIN_NQ: query rows per request from
+                                       which lsa_index_score uses the int8 MFMA kernel (16) */
+    LSA_TUNE_TOPK_STREAM_MIN_C = 2, /* LSA_TOPK_STREAM_MIN_C: row length from which the
+                                       selects stream the row from memory (65537) */
+    LSA_TUNE_TOPK_SPLIT_MIN_N = 3,  /* LSA_TOPK_SPLIT_MIN_N: token-list length from which
+                                       lsa_topk_tokens splits a row over workgroups */
+    LSA_TUNE_TOPK_SPLIT_SLICES = 4, /* LSA_TOPK_SPLIT_SLICES: slices of such a split
+                                       (default: chosen from the sizes) */
+    LSA_TUNE_COUNT = 5
+} lsa_tuning;
+
+/* Override a knob for the calling thread; value 0 drops the override.
+ * LSA_ERR_INVALID_ARGUMENT for an unknown knob or a value out of range
+ * (negative; ring depth other than 2-4). */
+lsa_status lsa_set_tuning(lsa_tuning knob, int32_t value);
+
+/* The value in effect for the calling thread (0: chosen per call from the
+ * sizes), or -1 for an unknown knob. */
+int32_t lsa_get_tuning(lsa_tuning knob);
 
 /* Static string naming a status code. */
 const char* lsa_status_string(lsa_status s);

@@ -13,7 +13,7 @@ from ._binding import (CHUNK_TOKENS, EXPORTS, LIB_PATH, LsaError, alloc_workspac
                        lsa_gather_attend_tokens,
                        lsa_gather_attend_workspace_size, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
                        lsa_topk_chunks, lsa_topk_tokens, lsa_topk_tokens_workspace_size,
-                       alloc_topk_tokens_workspace)
+                       alloc_topk_tokens_workspace, lsa_set_tuning, lsa_get_tuning, tuning, TUNE_KNOBS)
 
 load_library()
 
@@ -21,4 +21,5 @@ __all__ = ["CHUNK_TOKENS", "EXPORTS", "LIB_PATH", "LsaError", "alloc_workspace",
            "lsa_fetch_chunks", "lsa_fetch_chunks_pull", "lsa_gather_attend", "lsa_gather_attend_default_splits",
            "lsa_gather_attend_tokens",
            "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks",
-           "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "alloc_topk_tokens_workspace"]
+           "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "alloc_topk_tokens_workspace",
+           "lsa_set_tuning", "lsa_get_tuning", "tuning", "TUNE_KNOBS"]

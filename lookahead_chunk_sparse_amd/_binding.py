@@ -26,7 +26,17 @@ CHUNK_TOKENS = 64
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
            "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
-           "lsa_pool_assign")
+           "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning")
+
+# lsa_tuning knobs (include/lsa.h)
+TUNE_ATTEND_DEPTH = 0
+TUNE_SCORE_MFMA_MIN_NQ = 1
+TUNE_TOPK_STREAM_MIN_C = 2
+TUNE_TOPK_SPLIT_MIN_N = 3
+TUNE_TOPK_SPLIT_SLICES = 4
+TUNE_KNOBS = {"attend_depth": TUNE_ATTEND_DEPTH, "score_mfma_min_nq": TUNE_SCORE_MFMA_MIN_NQ,
+              "topk_stream_min_c": TUNE_TOPK_STREAM_MIN_C, "topk_split_min_n": TUNE_TOPK_SPLIT_MIN_N,
+              "topk_split_slices": TUNE_TOPK_SPLIT_SLICES}
 
 
 class LsaError(RuntimeError):
@@ -75,6 +85,10 @@ def load_library(path: str = LIB_PATH):
     L.lsa_fetch_chunks_pull.restype = ctypes.c_int
     L.lsa_pool_assign.argtypes = [vp, vp, i32, vp, i32, i32, i64, vp, vp, vp]
     L.lsa_pool_assign.restype = ctypes.c_int
+    L.lsa_set_tuning.argtypes = [ctypes.c_int, i32]
+    L.lsa_set_tuning.restype = ctypes.c_int
+    L.lsa_get_tuning.argtypes = [ctypes.c_int]
+    L.lsa_get_tuning.restype = i32
     _lib = L
     return L
 
@@ -97,12 +111,79 @@ def _ptr(t) -> int:
 
 
 def _need(t: torch.Tensor, dtype, name: str, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def _on(t: torch.Tensor, device: torch.device, name: str):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
+
+
+def _out(t, dtype, shape, device, name: str) -> torch.Tensor:
+    """An output buffer: a new device tensor when t is None, else t checked
+    for dtype, exact shape, device and contiguity (the kernels write exactly
+    that many elements there)."""
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, dtype, name)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    _on(t, device, name)
+    return t
+
+
+def lsa_set_tuning(knob, value: int):
+    """Override a tuning knob (a name of TUNE_KNOBS or its number) for the
+    calling thread; 0 drops the override."""
+    _check(load_library().lsa_set_tuning(TUNE_KNOBS.get(knob, knob), int(value)))
+
+
+def lsa_get_tuning(knob) -> int:
+    """The value of a tuning knob in effect for the calling thread (0: chosen
+    per call)."""
+    v = int(load_library().lsa_get_tuning(TUNE_KNOBS.get(knob, knob)))
+    if v < 0:
+        raise LsaError(1, f"unknown tuning knob {knob!r}")
+    return v
+
+
+class tuning:
+    """Context manager: tuning overrides for the calling thread, e.g.
+    ``with tuning(attend_depth=3): ...``; the previous overrides (or their
+    absence) come back on exit."""
+
+    def __init__(self, **knobs):
+        unknown = set(knobs) - set(TUNE_KNOBS)
+        if unknown:
+            raise ValueError(f"unknown tuning knobs {sorted(unknown)}")
+        self.knobs = knobs
+        self.saved = {}
+
+    def __enter__(self):
+        L = load_library()
+        for name, v in self.knobs.items():
+            # the thread's own override, if any, is what must come back: read
+            # it by dropping the override and comparing with the value in effect
+            knob = TUNE_KNOBS[name]
+            before = int(L.lsa_get_tuning(knob))
+            _check(L.lsa_set_tuning(knob, 0))
+            base = int(L.lsa_get_tuning(knob))
+            self.saved[name] = before if before != base else 0
+            lsa_set_tuning(knob, v)
+        return self
+
+    def __exit__(self, *exc):
+        for name, v in self.saved.items():
+            lsa_set_tuning(TUNE_KNOBS[name], v)
+        return False
 
 
 def lsa_index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, alpha: float, logits=None, scores=None,
@@ -113,12 +194,13 @@ def lsa_index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, alpha: float, logi
     _need(k_idx, torch.int8, "k_idx", 3)
     B, nq, d_idx = q_idx.shape
     C = k_idx.shape[1]
-    if logits is None:
-        logits = torch.empty((B, nq, C), dtype=torch.int32, device=k_idx.device)
-    if scores is None and want_scores:
-        scores = torch.empty((B, nq, C), dtype=torch.float32, device=k_idx.device)
     if k_idx.shape[0] != B or k_idx.shape[2] != d_idx:
         raise ValueError(f"k_idx shape {tuple(k_idx.shape)} does not match q_idx {tuple(q_idx.shape)}")
+    dev = k_idx.device
+    _on(q_idx, dev, "q_idx")
+    logits = _out(logits, torch.int32, (B, nq, C), dev, "logits")
+    if scores is not None or want_scores:
+        scores = _out(scores, torch.float32, (B, nq, C), dev, "scores")
     _check(load_library().lsa_index_score(_ptr(q_idx), _ptr(k_idx), B, nq, C, d_idx, alpha, _ptr(logits),
                                           _ptr(scores), _stream(stream)))
     return logits, scores
@@ -129,8 +211,7 @@ def lsa_topk_chunks(logits: torch.Tensor, k: int, chunk_ids=None, stream=None) -
     _need(logits, torch.int32, "logits")
     C = logits.shape[-1]
     R = logits.numel() // C
-    if chunk_ids is None:
-        chunk_ids = torch.empty((*logits.shape[:-1], k), dtype=torch.int32, device=logits.device)
+    chunk_ids = _out(chunk_ids, torch.int32, (*logits.shape[:-1], k), logits.device, "chunk_ids")
     _check(load_library().lsa_topk_chunks(_ptr(logits), R, C, k, _ptr(chunk_ids), _stream(stream)))
     return chunk_ids
 
@@ -142,10 +223,8 @@ def lsa_threshold_chunks(logits: torch.Tensor, k_max: int, logit_threshold: int 
     _need(logits, torch.int32, "logits")
     C = logits.shape[-1]
     R = logits.numel() // C
-    if chunk_ids is None:
-        chunk_ids = torch.empty((*logits.shape[:-1], k_max), dtype=torch.int32, device=logits.device)
-    if counts is None:
-        counts = torch.empty(logits.shape[:-1], dtype=torch.int32, device=logits.device)
+    chunk_ids = _out(chunk_ids, torch.int32, (*logits.shape[:-1], k_max), logits.device, "chunk_ids")
+    counts = _out(counts, torch.int32, logits.shape[:-1], logits.device, "counts")
     _check(load_library().lsa_threshold_chunks(_ptr(logits), R, C, int(logit_threshold), k_max, _ptr(chunk_ids),
                                                _ptr(counts), _stream(stream)))
     return chunk_ids, counts
@@ -175,16 +254,25 @@ def lsa_topk_tokens(scores: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torc
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
     _need(ctx_len, torch.int32, "ctx_len", 1)
     B, k = chunk_ids.shape
+    dev = scores.device
     if tuple(scores.shape) != (B, k * CHUNK_TOKENS):
         raise ValueError(f"scores shape {tuple(scores.shape)} is not [B][k*64] = [{B}][{k * CHUNK_TOKENS}]")
+    if tuple(ctx_len.shape) != (B,):
+        raise ValueError("ctx_len must have one entry per request")
+    _on(chunk_ids, dev, "chunk_ids")
+    _on(ctx_len, dev, "ctx_len")
     if counts is not None:
         _need(counts, torch.int32, "counts", 1)
-    if tok is None:
-        tok = torch.empty((B, k_tok), dtype=torch.int32, device=scores.device)
-    if tok_counts is None:
-        tok_counts = torch.empty(B, dtype=torch.int32, device=scores.device)
+        if tuple(counts.shape) != (B,):
+            raise ValueError("counts must have one entry per request")
+        _on(counts, dev, "counts")
+    tok = _out(tok, torch.int32, (B, k_tok), dev, "tok")
+    tok_counts = _out(tok_counts, torch.int32, (B,), dev, "tok_counts")
     if isinstance(workspace, str):
-        workspace = alloc_topk_tokens_workspace(B, k, k_tok, device=scores.device)
+        workspace = alloc_topk_tokens_workspace(B, k, k_tok, device=dev)
+    elif workspace is not None:
+        _need(workspace, torch.uint8, "workspace", 1)
+        _on(workspace, dev, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().lsa_topk_tokens(_ptr(scores), _ptr(chunk_ids), _ptr(counts), _ptr(ctx_len), B, k, k_tok,
                                           _ptr(tok), _ptr(tok_counts), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -229,40 +317,57 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
     B, Hq, d = q.shape
     _, C_store, two, Hkv, T, dk = kv.shape
     k = chunk_ids.shape[1]
+    dev = q.device
     if kv.shape[0] != B or two != 2 or T != CHUNK_TOKENS or dk != d:
         raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
-    if chunk_ids.shape[0] != B or ctx_len.shape[0] != B:
+    if chunk_ids.shape[0] != B or tuple(ctx_len.shape) != (B,):
         raise ValueError("chunk_ids / ctx_len batch size mismatch")
+    for t, name in ((kv, "kv"), (chunk_ids, "chunk_ids"), (ctx_len, "ctx_len")):
+        _on(t, dev, name)
     if slots is not None:
         _need(slots, torch.int32, "slots", 2)
         if tuple(slots.shape) != tuple(chunk_ids.shape):
             raise ValueError("slots must have the shape of chunk_ids")
+        _on(slots, dev, "slots")
     if counts is not None:
         _need(counts, torch.int32, "counts", 1)
-        if counts.shape[0] != B:
+        if tuple(counts.shape) != (B,):
             raise ValueError("counts must have one entry per request")
+        _on(counts, dev, "counts")
     S_max = 0
     if seg_kv is not None:
         _need(seg_kv, torch.bfloat16, "seg_kv", 5)
+        if seg_len is None:
+            raise ValueError("seg_kv needs seg_len")
         _need(seg_len, torch.int32, "seg_len", 1)
         if seg_kv.shape[0] != B or seg_kv.shape[1] != 2 or seg_kv.shape[2] != Hkv or seg_kv.shape[4] != d:
             raise ValueError(f"seg_kv shape {tuple(seg_kv.shape)} does not match [B][2][Hkv][S_max][d]")
+        if tuple(seg_len.shape) != (B,):
+            raise ValueError("seg_len must have one entry per request")
+        _on(seg_kv, dev, "seg_kv")
+        _on(seg_len, dev, "seg_len")
         S_max = seg_kv.shape[3]
     k_tok = 0
     if tok is not None:
         _need(tok, torch.int32, "tok", 2)
         if tok.shape[0] != B:
             raise ValueError("tok batch size mismatch")
+        _on(tok, dev, "tok")
         k_tok = tok.shape[1]
         if tok_counts is not None:
             _need(tok_counts, torch.int32, "tok_counts", 1)
+            if tuple(tok_counts.shape) != (B,):
+                raise ValueError("tok_counts must have one entry per request")
+            _on(tok_counts, dev, "tok_counts")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if workspace is None:
         entries = k if tok is None else (k_tok + CHUNK_TOKENS - 1) // CHUNK_TOKENS
-        workspace = alloc_workspace(B, Hq, Hkv, d, entries, n_split, device=q.device)
-    if out is None:
-        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        workspace = alloc_workspace(B, Hq, Hkv, d, entries, n_split, device=dev)
+    else:
+        _need(workspace, torch.uint8, "workspace", 1)
+        _on(workspace, dev, "workspace")
+    out = _out(out, torch.float32, (B, Hq, d), dev, "out")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if tok is not None:
         _check(load_library().lsa_gather_attend_tokens(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
@@ -287,6 +392,22 @@ def lsa_gather_attend_tokens(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch
     return lsa_gather_attend(q, kv, chunk_ids, ctx_len, tok=tok, tok_counts=tok_counts, **kw)
 
 
+def _check_pool(host_kv: torch.Tensor, pool_kv: torch.Tensor):
+    """The pool must hold chunks of the host store's shape: [B][P][2][Hkv][64][d]
+    with the host's B, Hkv and d, in device memory; the host store on the host."""
+    B, C, two, Hkv, T, d = host_kv.shape
+    if two != 2 or T != CHUNK_TOKENS:
+        raise ValueError(f"host_kv shape {tuple(host_kv.shape)} is not [B][C][2][Hkv][64][d]")
+    if host_kv.is_cuda:
+        raise ValueError("host_kv must be pinned host memory")
+    pb, P, ptwo, pH, pT, pd = pool_kv.shape
+    if (pb, ptwo, pH, pT, pd) != (B, 2, Hkv, T, d):
+        raise ValueError(f"pool_kv shape {tuple(pool_kv.shape)} does not match [B][P][2][Hkv][64][d] = "
+                         f"[{B}][P][2][{Hkv}][64][{d}]")
+    if not pool_kv.is_cuda:
+        raise ValueError("pool_kv must be device memory")
+
+
 def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_kv: torch.Tensor,
                      host_slots: torch.Tensor | None = None, stream=None, done=None):
     """host_kv pinned bf16 [B][C][2][Hkv][64][d]; host ids int32 [B][k] (CPU);
@@ -299,8 +420,13 @@ def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_k
     B, C, _, Hkv, T, d = host_kv.shape
     P = pool_kv.shape[1]
     k = host_chunk_ids.shape[1]
+    _check_pool(host_kv, pool_kv)
+    if host_chunk_ids.shape[0] != B:
+        raise ValueError("host_chunk_ids batch size mismatch")
     if host_slots is not None:
         _need(host_slots, torch.int32, "host_slots", 2)
+        if tuple(host_slots.shape) != tuple(host_chunk_ids.shape):
+            raise ValueError("host_slots must have the shape of host_chunk_ids")
     ev = 0
     if done is not None:
         ev = done.cuda_event if hasattr(done, "cuda_event") else int(done)
@@ -317,11 +443,18 @@ def lsa_fetch_chunks_pull(host_kv: torch.Tensor, chunk_ids: torch.Tensor, pool_k
     _need(chunk_ids, torch.int32, "chunk_ids", 2)
     if not chunk_ids.is_cuda or (slots is not None and not slots.is_cuda):
         raise ValueError("chunk ids and slots for the pull fetch must be device tensors")
-    if slots is not None:
-        _need(slots, torch.int32, "slots", 2)
     B, C, _, Hkv, T, d = host_kv.shape
     P = pool_kv.shape[1]
     k = chunk_ids.shape[1]
+    _check_pool(host_kv, pool_kv)
+    if chunk_ids.shape[0] != B:
+        raise ValueError("chunk_ids batch size mismatch")
+    _on(chunk_ids, pool_kv.device, "chunk_ids")
+    if slots is not None:
+        _need(slots, torch.int32, "slots", 2)
+        if tuple(slots.shape) != tuple(chunk_ids.shape):
+            raise ValueError("slots must have the shape of chunk_ids")
+        _on(slots, pool_kv.device, "slots")
     _check(load_library().lsa_fetch_chunks_pull(_ptr(host_kv), C, _ptr(chunk_ids), _ptr(slots), _ptr(pool_kv), P,
                                                 B, Hkv, d, k, grid, _stream(stream)))
 
@@ -332,6 +465,7 @@ def lsa_pool_assign(prev_ids, prev_slots, new_ids: torch.Tensor, P: int, new_slo
     None for the first selection).  Returns (new_slots, fetch_slots), int32 [B][k]."""
     _need(new_ids, torch.int32, "new_ids", 2)
     B, k = new_ids.shape
+    dev = new_ids.device
     n_prev = 0
     if prev_ids is not None:
         _need(prev_ids, torch.int32, "prev_ids", 2)
@@ -339,10 +473,10 @@ def lsa_pool_assign(prev_ids, prev_slots, new_ids: torch.Tensor, P: int, new_slo
         n_prev = prev_ids.shape[1]
         if prev_ids.shape[0] != B or tuple(prev_slots.shape) != tuple(prev_ids.shape):
             raise ValueError("prev_ids / prev_slots shapes do not match")
-    if new_slots is None:
-        new_slots = torch.empty((B, k), dtype=torch.int32, device=new_ids.device)
-    if fetch_slots is None:
-        fetch_slots = torch.empty((B, k), dtype=torch.int32, device=new_ids.device)
+        _on(prev_ids, dev, "prev_ids")
+        _on(prev_slots, dev, "prev_slots")
+    new_slots = _out(new_slots, torch.int32, (B, k), dev, "new_slots")
+    fetch_slots = _out(fetch_slots, torch.int32, (B, k), dev, "fetch_slots")
     _check(load_library().lsa_pool_assign(_ptr(prev_ids), _ptr(prev_slots), n_prev, _ptr(new_ids), B, k, P,
                                           _ptr(new_slots), _ptr(fetch_slots), _stream(stream)))
     return new_slots, fetch_slots

@@ -3,9 +3,11 @@ the measurement-only libtileread.so that bench.py uses to state the HBM read
 ceiling of the attention's access pattern."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -24,10 +26,7 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
-def _compile(sources, out_path: str, verbose: bool) -> str:
-    srcs = [os.path.join(CSRC, s) for s in sources]
-    tmp = out_path + ".tmp"
-    cmd = [HIPCC, *DEVICE_FLAGS, "-shared", "-o", tmp, *srcs]
+def _run(cmd, verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,6 +37,22 @@ def _compile(sources, out_path: str, verbose: bool) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
+    return msg
+
+
+def _compile(sources, out_path: str, verbose: bool) -> str:
+    """Compile every source to an object in parallel, then link the shared
+    library; the objects live in a temporary directory."""
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    with tempfile.TemporaryDirectory(prefix="lsa_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, f"{i}_{os.path.basename(s)}.o") for i, s in enumerate(srcs)]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as pool:
+            futs = [pool.submit(_run, [HIPCC, *DEVICE_FLAGS, "-c", "-o", o, src], verbose)
+                    for src, o in zip(srcs, objs)]
+            for f in futs:
+                f.result()
+        tmp = out_path + ".tmp"
+        _run([HIPCC, *DEVICE_FLAGS, "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, out_path)
     return out_path
 

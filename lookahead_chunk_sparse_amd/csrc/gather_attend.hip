@@ -532,18 +532,11 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttendArgs a) {
 
 }  // namespace
 
-// Register-ring size of the split kernel: 2 unless LSA_ATTEND_DEPTH (2, 3
-// or 4) overrides it for tuning.  Read once per process.  With the
-// non-temporal tile loads one slice in flight per wave beside the one being
-// processed measured fastest (128K: 172.9 us at 2, 175.2 at 3, 177.2 at 4).
-int attend_pipeline_depth() {
-    static const int depth = [] {
-        const char* e = getenv("LSA_ATTEND_DEPTH");
-        const int v = e ? atoi(e) : 2;
-        return (v >= 2 && v <= 4) ? v : 2;
-    }();
-    return depth;
-}
+// Register-ring size of the split kernel: 2 unless the LSA_TUNE_ATTEND_DEPTH
+// knob (2, 3 or 4) says otherwise.  With the non-temporal tile loads one
+// slice in flight per wave beside the one being processed measured fastest
+// (128K: 172.9 us at 2, 175.2 at 3, 177.2 at 4).
+int attend_pipeline_depth() { return tuning(LSA_TUNE_ATTEND_DEPTH); }
 
 int attend_default_splits(int B, int Hkv, int k) {
     // About one workgroup per CU (256): with every K/V byte read exactly once,

@@ -167,13 +167,10 @@ hipError_t launch_mfma(const int8_t* q, const int8_t* keys, int B, int nq, int C
     return hipGetLastError();
 }
 
-// Query rows per request from which the MFMA kernel is used: 16 unless
-// LSA_SCORE_MFMA_MIN_NQ overrides it (read on every call; for tuning and
-// for measuring both kernels on the same shapes).
-int score_mfma_min_nq() {
-    const char* e = getenv("LSA_SCORE_MFMA_MIN_NQ");
-    return e ? atoi(e) : 16;
-}
+// Query rows per request from which the MFMA kernel is used: the
+// LSA_TUNE_SCORE_MFMA_MIN_NQ knob, 16 by default (the crossover measured at
+// C = 16,384).
+int score_mfma_min_nq() { return tuning(LSA_TUNE_SCORE_MFMA_MIN_NQ); }
 
 template <int DIDX>
 hipError_t launch(const int8_t* q, const int8_t* keys, int B, int nq, int C, float alpha, int32_t* logits,

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <limits.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <cmath>
@@ -45,9 +46,60 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 constexpr int64_t kMaxRowGroups = (int64_t)1 << 22;    // 1024-thread top-k / pool workgroups
 constexpr int64_t kMaxSplitGroups = (int64_t)1 << 24;  // 256-thread attention workgroups
 
+// ---- tuning knobs (include/lsa.h, lsa_tuning) ----
+constexpr const char* kTuneEnv[LSA_TUNE_COUNT] = {"LSA_ATTEND_DEPTH", "LSA_SCORE_MFMA_MIN_NQ", "LSA_TOPK_STREAM_MIN_C",
+                                                  "LSA_TOPK_SPLIT_MIN_N", "LSA_TOPK_SPLIT_SLICES"};
+// the library's own choice where it is a constant (0: chosen per call)
+constexpr int32_t kTuneDefault[LSA_TUNE_COUNT] = {2, 16, lsa::kTopkRegisterMaxC + 1, 32769, 0};
+
+bool tune_value_ok(int knob, int32_t v) {
+    if (v < 0) return false;
+    if (knob == LSA_TUNE_ATTEND_DEPTH) return v == 0 || (v >= 2 && v <= 4);
+    return true;
+}
+
+// The environment's values, read once per process (thread-safe static
+// initialisation); values out of range are ignored.
+const int32_t* env_tuning() {
+    static const struct Env {
+        int32_t v[LSA_TUNE_COUNT];
+        Env() {
+            for (int i = 0; i < LSA_TUNE_COUNT; ++i) {
+                const char* e = getenv(kTuneEnv[i]);
+                const long x = e ? strtol(e, nullptr, 10) : 0;
+                v[i] = (x > 0 && x <= INT32_MAX && tune_value_ok(i, (int32_t)x)) ? (int32_t)x : 0;
+            }
+        }
+    } env;
+    return env.v;
+}
+
+thread_local int32_t t_tune[LSA_TUNE_COUNT] = {};
+
 }  // namespace
 
+namespace lsa {
+int32_t tuning(int knob) {
+    if (t_tune[knob] > 0) return t_tune[knob];
+    const int32_t e = env_tuning()[knob];
+    return e > 0 ? e : kTuneDefault[knob];
+}
+}  // namespace lsa
+
 extern "C" {
+
+lsa_status lsa_set_tuning(lsa_tuning knob, int32_t value) {
+    if ((int)knob < 0 || (int)knob >= LSA_TUNE_COUNT) return fail(LSA_ERR_INVALID_ARGUMENT, "unknown knob %d", (int)knob);
+    if (!tune_value_ok(knob, value))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "value %d out of range for %s", value, kTuneEnv[knob]);
+    t_tune[knob] = value;
+    return ok();
+}
+
+int32_t lsa_get_tuning(lsa_tuning knob) {
+    if ((int)knob < 0 || (int)knob >= LSA_TUNE_COUNT) return -1;
+    return lsa::tuning(knob);
+}
 
 const char* lsa_status_string(lsa_status s) {
     switch (s) {

@@ -4,7 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/lsa.h"
+
 namespace lsa {
+
+// Value of a tuning knob (lsa_tuning) for the calling thread: its override,
+// else the environment's value read once per process, else the library's
+// constant default (0 where the choice is made per call).
+int32_t tuning(int knob);
 
 constexpr int kChunkTokens = 64;
 

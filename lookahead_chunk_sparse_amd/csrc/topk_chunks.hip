@@ -805,13 +805,10 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(TopkArgs a) {
     });
 }
 
-// Rows longer than this many positions stream from memory (LSA_TOPK_STREAM_MIN_C,
-// read per call, lowers the bound for testing and tuning).
-int stream_min_c() {
-    const char* e = getenv("LSA_TOPK_STREAM_MIN_C");
-    const int v = e ? atoi(e) : 0;
-    return v > 0 ? v : kTopkRegisterMaxC + 1;
-}
+// Rows of at least this many positions stream from memory (the
+// LSA_TUNE_TOPK_STREAM_MIN_C knob; by default rows beyond the register
+// kernel's 65536 positions).
+int stream_min_c() { return tuning(LSA_TUNE_TOPK_STREAM_MIN_C); }
 
 template <int MODE>
 hipError_t launch_mode(const TopkArgs& a, int grid, int positions, hipStream_t stream) {
@@ -844,23 +841,22 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // slice + candidates path, for rows of more than 32768 positions (measured:
 // at 17,664 positions one workgroup per row is faster, 19.5 against 23.8 us
 // for 16 rows; at 50,048 the split takes 36 against 73 us, at 104,832 43
-// against 165 us); LSA_TOPK_SPLIT_MIN_N, read per call, lowers the bound for
+// against 165 us); the LSA_TUNE_TOPK_SPLIT_MIN_N knob moves the bound for
 // testing.  About n / (8 k_tok) slices (at most 16), each a multiple of 64
 // positions; none (slices = 0) when that gives fewer than 2 or the slices or
 // candidates would not fit the register-resident kernel.
 TopkSplit topk_tokens_split(int n_list, int k_tok) {
     TopkSplit sp{0, 0};
     const int64_t n = (int64_t)n_list * kChunkTokens;
-    const char* env = getenv("LSA_TOPK_SPLIT_MIN_N");
-    const int64_t min_n = env && atoi(env) > 0 ? atoi(env) : 2 * kTopkRegisterMaxC / 4 + 1;  // 32769
+    const int64_t min_n = tuning(LSA_TUNE_TOPK_SPLIT_MIN_N);  // 32769 unless overridden
     if (n < min_n) return sp;
     // ceil(n / (8 k_tok)) slices: a sweep at 8 x 50,048 and 4 x 104,832
     // positions (k_tok = 2048) was fastest at 4-6 slices (more slices grow
-    // the candidates' select, fewer the slices'); LSA_TOPK_SPLIT_SLICES
-    // (read per call) overrides the count for tuning
+    // the candidates' select, fewer the slices'); the
+    // LSA_TUNE_TOPK_SPLIT_SLICES knob overrides the count for tuning
     int64_t P = (n + 8 * (int64_t)k_tok - 1) / (8 * (int64_t)k_tok);
     if (P > 16) P = 16;
-    if (const char* e = getenv("LSA_TOPK_SPLIT_SLICES")) P = atoi(e) > 0 ? atoi(e) : P;
+    if (const int32_t ov = tuning(LSA_TUNE_TOPK_SPLIT_SLICES)) P = ov;
     if (P < 2) return sp;
     int64_t L = (n + P - 1) / P;
     L = (L + kChunkTokens - 1) / kChunkTokens * kChunkTokens;

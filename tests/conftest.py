@@ -33,3 +33,20 @@ def synth_lib():
     import synth
     synth.build(force=not os.path.exists(synth._LIB_PATH))
     return synth
+
+
+@pytest.fixture
+def tune():
+    """tune(**knobs): tuning overrides of the library (lsa_set_tuning) for the
+    calling thread, undone when the test ends."""
+    import lookahead_chunk_sparse_amd as lsa
+    held = []
+
+    def set_knobs(**knobs):
+        cm = lsa.tuning(**knobs)
+        cm.__enter__()
+        held.append(cm)
+
+    yield set_knobs
+    for cm in reversed(held):
+        cm.__exit__(None, None, None)

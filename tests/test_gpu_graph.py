@@ -108,16 +108,15 @@ def test_host_tier_graph_replays_match_eager():
 
 
 @pytest.mark.parametrize("split", [False, True])
-def test_token_stage_graph_replays_match_eager(monkeypatch, split):
+def test_token_stage_graph_replays_match_eager(tune, split):
     """Chunk selection, then per step the token top-k and the token-list
     attention, captured in one graph: every replay gives the eager bits.
     split=True forces the slices + candidates select (two launches and a
     workspace per step), as long recalls take it."""
     import torch
 
-    if split:  # read when the workspace is sized and at every call, so set before the decoder exists
-        monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")
-        monkeypatch.setenv("LSA_TOPK_SPLIT_SLICES", "4")
+    if split:  # consulted when the workspace is sized and at every call, so set before the decoder exists
+        tune(topk_split_min_n=1, topk_split_slices=4)
 
     import synth
     from lookahead_chunk_sparse_amd.decode import LsaDecoder

@@ -85,10 +85,10 @@ def test_index_score_and_selection_workloads(lsa, oracle_lib, W, name):
     (1, 16, 1, 128), (2, 17, 15, 128), (1, 64, 1000, 128), (3, 65, 17, 64), (1, 256, 16384, 128),
     (2, 33, 513, 256), (1, 128, 2048, 64),
 ])
-def test_batched_scoring(lsa, oracle_lib, synth_lib, monkeypatch, path, B, nq, C, d_idx):
+def test_batched_scoring(lsa, oracle_lib, synth_lib, tune, path, B, nq, C, d_idx):
     """Many query rows sharing a request's keys: the int8-MFMA kernel and the
     GEMV kernel (forced through the dispatch threshold) both match."""
-    monkeypatch.setenv("LSA_SCORE_MFMA_MIN_NQ", "1" if path == "mfma" else "1000000")
+    tune(score_mfma_min_nq=1 if path == "mfma" else 1000000)
     s = synth_lib.stream
     q = synth_lib.uniform_i8((B, nq, d_idx), 23, s(synth_lib.TAG_MISC, 1500 + nq), -128, 127)
     K = synth_lib.uniform_i8((B, C, d_idx), 23, s(synth_lib.TAG_MISC, 1600 + C), -128, 127)
@@ -163,10 +163,10 @@ def test_topk_large_rows_crowded(lsa, oracle_lib, synth_lib, C):
 
 @pytest.mark.parametrize("kind", ["random", "few", "equal", "extremes"])
 @pytest.mark.parametrize("C", [1, 65, 1025, 7813])
-def test_topk_streaming_parity(lsa, oracle_lib, synth_lib, monkeypatch, kind, C):
+def test_topk_streaming_parity(lsa, oracle_lib, synth_lib, tune, kind, C):
     """The streaming kernel (rows read from memory in every pass), forced on
     rows that would otherwise keep their keys in registers."""
-    monkeypatch.setenv("LSA_TOPK_STREAM_MIN_C", "1")
+    tune(topk_stream_min_c=1)
     rows = _rows(synth_lib, kind, 2, C, seed=C + 50)
     dl = to_dev(rows)
     for k in sorted({1, C, max(1, C // 7), max(1, C - 1)}):
@@ -365,9 +365,9 @@ def _token_scores(synth_lib, B, n, seed):
     (2, 4096, 1024, 2048),  # the largest list: 65536 positions
     (2, 600, 500, 3000),   # 32000 positions: 32 per thread, the most whose output regions fit LDS
 ])
-def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_tok):
+def test_topk_tokens_parity(lsa, oracle_lib, synth_lib, tune, B, C, k, k_tok):
     say("token top-k", B, C, k, k_tok)
-    monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")  # the slice + candidates path on every size it can split
+    tune(topk_split_min_n=1)  # the slice + candidates path on every size it can split
     scores = _token_scores(synth_lib, B, k * 64, seed=k)
     ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4010 + b)))
                     for b in range(B)]).astype(np.int32)
@@ -410,14 +410,14 @@ def test_topk_tokens_crowded_scores(lsa, oracle_lib, synth_lib, B, C, k, k_tok):
 
 
 @pytest.mark.parametrize("slices,k_tok", [(2, 2048), (12, 4096)])
-def test_topk_tokens_split_shapes(lsa, oracle_lib, synth_lib, monkeypatch, slices, k_tok):
+def test_topk_tokens_split_shapes(lsa, oracle_lib, synth_lib, tune, slices, k_tok):
     """The 500K recall (782 chunks, 50,048 positions) split into 2 long slices
     (32 positions per thread in the slice select, which keeps keys too: its
     output takes two sweeps over the registers) or 12 slices with a 4096-token
     budget (49,152 candidates, 48 per thread: the same in the candidates
     select)."""
     say("token top-k split shapes", slices, k_tok)
-    monkeypatch.setenv("LSA_TOPK_SPLIT_SLICES", str(slices))
+    tune(topk_split_slices=slices)
     B, C, k = 2, 7813, 782
     scores = _token_scores(synth_lib, B, k * 64, seed=slices)
     ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4070 + b)))
@@ -429,9 +429,9 @@ def test_topk_tokens_split_shapes(lsa, oracle_lib, synth_lib, monkeypatch, slice
 
 
 @pytest.mark.parametrize("B,C,k,k_tok", [(4, 12, 5, 7), (3, 64, 40, 600), (4, 2048, 276, 2048)])
-def test_topk_tokens_streaming_parity(lsa, oracle_lib, synth_lib, monkeypatch, B, C, k, k_tok):
+def test_topk_tokens_streaming_parity(lsa, oracle_lib, synth_lib, tune, B, C, k, k_tok):
     """Token selection through the streaming kernel, forced on short lists."""
-    monkeypatch.setenv("LSA_TOPK_STREAM_MIN_C", "1")
+    tune(topk_stream_min_c=1)
     scores = _token_scores(synth_lib, B, k * 64, seed=k + 1)
     ids = np.stack([np.sort(synth_lib.choose(k, C, 9, synth_lib.stream(synth_lib.TAG_MISC, 4030 + b)))
                     for b in range(B)]).astype(np.int32)

@@ -99,11 +99,11 @@ def _token_scores(synth_lib, kind, B, n, case):
 
 
 @pytest.mark.parametrize("case", range(80))
-def test_topk_tokens_random(lsa, oracle_lib, synth_lib, monkeypatch, case):
+def test_topk_tokens_random(lsa, oracle_lib, synth_lib, tune, case):
     B, C, k, k_tok, kind, split, rng = _token_case(case)
     say("random token case", case, B, C, k, k_tok, kind, split)
     if split:  # the slice + candidates path wherever the row can be split
-        monkeypatch.setenv("LSA_TOPK_SPLIT_MIN_N", "1")
+        tune(topk_split_min_n=1)
     scores = _token_scores(synth_lib, kind, B, k * 64, case)
     ids = np.stack([np.sort(synth_lib.choose(k, C, case, synth_lib.stream(synth_lib.TAG_MISC, 6100 + b)))
                     for b in range(B)]).astype(np.int32)
