@@ -285,6 +285,30 @@ lsa_status lsa_gather_attend(const uint16_t* q, const uint16_t* kv, int64_t C_st
                              int32_t n_split, float* out, hipStream_t stream);
 
 /*
+ * lsa_gather_attend_noalloc -- lsa_gather_attend without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, result and validation as lsa_gather_attend, minus the
+ * workspace.  The split partials live in a static device buffer of
+ * LSA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its device address is looked up on the first call
+ * made with that GPU current.  The call allocates nothing.  Sizes whose
+ * partials exceed the buffer (lsa_gather_attend_workspace_size(...) >
+ * LSA_NOALLOC_SCRATCH_BYTES) are rejected with LSA_ERR_WORKSPACE before any
+ * HIP call.  All calls on one GPU share that GPU's buffer: calls whose
+ * executions overlap in time on one GPU (different streams, different host
+ * threads without ordering) race and give wrong results; calls ordered on
+ * one stream are safe.
+ */
+#define LSA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+lsa_status lsa_gather_attend_noalloc(const uint16_t* q, const uint16_t* kv, int64_t C_store,
+                                     const int32_t* chunk_ids, const int32_t* slots, const int32_t* counts,
+                                     const int32_t* ctx_len, const uint16_t* seg_kv, const int32_t* seg_len,
+                                     int32_t S_max, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int32_t k,
+                                     float sm_scale, int32_t n_split, float* out, hipStream_t stream);
+
+/*
  * lsa_gather_attend_tokens -- lsa_gather_attend over a listed subset of the
  * chunk tokens (the output of lsa_topk_tokens).
  *

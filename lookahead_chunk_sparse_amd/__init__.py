@@ -13,7 +13,8 @@ from ._binding import (CHUNK_TOKENS, EXPORTS, LIB_PATH, LsaError, alloc_workspac
                        lsa_gather_attend_tokens,
                        lsa_gather_attend_workspace_size, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
                        lsa_topk_chunks, lsa_topk_tokens, lsa_topk_tokens_workspace_size,
-                       alloc_topk_tokens_workspace, lsa_set_tuning, lsa_get_tuning, tuning, TUNE_KNOBS)
+                       alloc_topk_tokens_workspace, lsa_set_tuning, lsa_get_tuning, tuning, TUNE_KNOBS,
+                       lsa_gather_attend_noalloc, NOALLOC_SCRATCH_BYTES)
 
 load_library()
 
@@ -22,4 +23,5 @@ __all__ = ["CHUNK_TOKENS", "EXPORTS", "LIB_PATH", "LsaError", "alloc_workspace",
            "lsa_gather_attend_tokens",
            "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "alloc_topk_tokens_workspace",
-           "lsa_set_tuning", "lsa_get_tuning", "tuning", "TUNE_KNOBS"]
+           "lsa_set_tuning", "lsa_get_tuning", "tuning", "TUNE_KNOBS", "lsa_gather_attend_noalloc",
+           "NOALLOC_SCRATCH_BYTES"]

@@ -26,7 +26,10 @@ CHUNK_TOKENS = 64
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
            "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
-           "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning")
+           "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning", "lsa_gather_attend_noalloc")
+
+# bytes of the static split-partials buffer of lsa_gather_attend_noalloc (LSA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 # lsa_tuning knobs (include/lsa.h)
 TUNE_ATTEND_DEPTH = 0
@@ -72,6 +75,9 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz,
                                     i32, vp, vp]
     L.lsa_gather_attend.restype = ctypes.c_int
+    L.lsa_gather_attend_noalloc.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                            i32, vp, vp]
+    L.lsa_gather_attend_noalloc.restype = ctypes.c_int
     L.lsa_topk_tokens.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     L.lsa_topk_tokens.restype = ctypes.c_int
     L.lsa_topk_tokens_workspace_size.argtypes = [i32, i32, i32]
@@ -381,6 +387,63 @@ def lsa_gather_attend(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor
                                             Hkv, d, k, sm_scale,
                                             _ptr(workspace), ws_bytes,
                                             n_split, _ptr(out), _stream(stream)))
+    return out
+
+
+def lsa_gather_attend_noalloc(q: torch.Tensor, kv: torch.Tensor, chunk_ids: torch.Tensor, ctx_len: torch.Tensor,
+                              out: torch.Tensor, sm_scale: float | None = None, slots: torch.Tensor | None = None,
+                              n_split: int = 0, counts: torch.Tensor | None = None,
+                              seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """lsa_gather_attend with the split partials in the library's static
+    device buffer: no workspace, and the caller passes `out` (fp32
+    [B][Hq][d]), so nothing is allocated on the call's path."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(kv, torch.bfloat16, "kv", 6)
+    _need(chunk_ids, torch.int32, "chunk_ids", 2)
+    _need(ctx_len, torch.int32, "ctx_len", 1)
+    B, Hq, d = q.shape
+    _, C_store, two, Hkv, T, dk = kv.shape
+    k = chunk_ids.shape[1]
+    dev = q.device
+    if kv.shape[0] != B or two != 2 or T != CHUNK_TOKENS or dk != d:
+        raise ValueError(f"kv shape {tuple(kv.shape)} does not match q {tuple(q.shape)}")
+    if chunk_ids.shape[0] != B or tuple(ctx_len.shape) != (B,):
+        raise ValueError("chunk_ids / ctx_len batch size mismatch")
+    for t, name in ((kv, "kv"), (chunk_ids, "chunk_ids"), (ctx_len, "ctx_len")):
+        _on(t, dev, name)
+    if slots is not None:
+        _need(slots, torch.int32, "slots", 2)
+        if tuple(slots.shape) != tuple(chunk_ids.shape):
+            raise ValueError("slots must have the shape of chunk_ids")
+        _on(slots, dev, "slots")
+    if counts is not None:
+        _need(counts, torch.int32, "counts", 1)
+        if tuple(counts.shape) != (B,):
+            raise ValueError("counts must have one entry per request")
+        _on(counts, dev, "counts")
+    S_max = 0
+    if seg_kv is not None:
+        _need(seg_kv, torch.bfloat16, "seg_kv", 5)
+        if seg_len is None:
+            raise ValueError("seg_kv needs seg_len")
+        _need(seg_len, torch.int32, "seg_len", 1)
+        if seg_kv.shape[0] != B or seg_kv.shape[1] != 2 or seg_kv.shape[2] != Hkv or seg_kv.shape[4] != d:
+            raise ValueError(f"seg_kv shape {tuple(seg_kv.shape)} does not match [B][2][Hkv][S_max][d]")
+        if tuple(seg_len.shape) != (B,):
+            raise ValueError("seg_len must have one entry per request")
+        _on(seg_kv, dev, "seg_kv")
+        _on(seg_len, dev, "seg_len")
+        S_max = seg_kv.shape[3]
+    if out is None:
+        raise ValueError("lsa_gather_attend_noalloc needs the caller's out buffer")
+    out = _out(out, torch.float32, (B, Hq, d), dev, "out")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    _check(load_library().lsa_gather_attend_noalloc(_ptr(q), _ptr(kv), C_store, _ptr(chunk_ids), _ptr(slots),
+                                                    _ptr(counts), _ptr(ctx_len), _ptr(seg_kv), _ptr(seg_len), S_max,
+                                                    B, Hq, Hkv, d, k, sm_scale, n_split, _ptr(out),
+                                                    _stream(stream)))
     return out
 
 

@@ -30,6 +30,22 @@ lsa_status fail(lsa_status s, const char* fmt, ...) {
     return s;
 }
 
+}  // namespace
+
+namespace lsa {
+lsa_status reject(lsa_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+}  // namespace lsa
+
+namespace {
+
 lsa_status ok() {
     g_last_error.clear();
     return LSA_OK;

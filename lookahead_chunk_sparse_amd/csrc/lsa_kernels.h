@@ -13,6 +13,10 @@ namespace lsa {
 // constant default (0 where the choice is made per call).
 int32_t tuning(int knob);
 
+// Records `fmt` as the calling thread's lsa_last_error() message and
+// returns s (for entry points defined outside lsa_abi.hip).
+lsa_status reject(lsa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 constexpr int kChunkTokens = 64;
 
 // ---- index score (indexer dot product + sigmoid) ----
