@@ -25,7 +25,7 @@
  *    surface at the caller's next synchronisation, as with any HIP kernel.
  *  - Chunk ids that are out of range, or duplicated, are caller errors the
  *    kernels do not check (the ids produced by lsa_topk_chunks are always in
- *    range and distinct).
+ *    range and distinct); lsa_check_ids checks a list on request.
  *  - A chunk is LSA_CHUNK_TOKENS = 64 consecutive tokens.
  *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
  *  - Calls keep no mutable global state (the tuning overrides below are per
@@ -78,17 +78,19 @@ typedef enum lsa_tuning {
     LSA_TUNE_COUNT = 5
 } lsa_tuning;
 
-/* Override a knob for the calling thread; value 0 drops the override.
- * LSA_ERR_INVALID_ARGUMENT for an unknown knob or a value out of range
- * (negative; ring depth other than 2-4). */
-lsa_status lsa_set_tuning(lsa_tuning knob, int32_t value);
+/* Override a knob (an lsa_tuning value) for the calling thread; value 0
+ * drops the override.  LSA_ERR_INVALID_ARGUMENT for an unknown knob or a
+ * value out of range (negative; ring depth other than 2-4).  The knob is
+ * passed as int32_t so that any integer a caller passes is well defined. */
+lsa_status lsa_set_tuning(int32_t knob, int32_t value);
 
 /* The value in effect for the calling thread (0: chosen per call from the
  * sizes), or -1 for an unknown knob. */
-int32_t lsa_get_tuning(lsa_tuning knob);
+int32_t lsa_get_tuning(int32_t knob);
 
-/* Static string naming a status code. */
-const char* lsa_status_string(lsa_status s);
+/* Static string naming a status code (an lsa_status value; any other
+ * integer gives "LSA_ERR_UNKNOWN"). */
+const char* lsa_status_string(int32_t s);
 
 /* Message describing the last rejected call made by this host thread
  * ("" if none).  Valid until the thread's next call into the library. */
@@ -340,6 +342,33 @@ lsa_status lsa_gather_attend_tokens(const uint16_t* q, const uint16_t* kv, int64
                                     const uint16_t* seg_kv, const int32_t* seg_len, int32_t S_max, int32_t B,
                                     int32_t Hq, int32_t Hkv, int32_t d, int32_t k, float sm_scale, void* workspace,
                                     size_t workspace_bytes, int32_t n_split, float* out, hipStream_t stream);
+
+/*
+ * lsa_check_ids -- opt-in check of a chunk list before it is attended over or
+ * fetched (the kernels trust their ids; no page passage defines this call).
+ *
+ * Reads only chunk_ids, slots and counts.  For every request b, over its used
+ * entries j < counts[b] (all k when counts is NULL; entries past the count,
+ * such as the -1 padding of lsa_threshold_chunks, are not looked at):
+ *   - 0 <= chunk_ids[b][j] < C_ctx (the request's context chunks);
+ *   - its store position, slots[b][j] (or chunk_ids[b][j] when slots is
+ *     NULL), in [0, C_store);
+ *   - no chunk id and no store position listed twice;
+ *   - counts[b] in [0, k].
+ * Synchronous: enqueues the check on `stream`, waits for the stream, and
+ * returns LSA_OK, or LSA_ERR_INVALID_ARGUMENT with lsa_last_error() naming
+ * the first offending request and entry and the rule it breaks.
+ *
+ *  chunk_ids  device int32 [B][k]
+ *  slots      device int32 [B][k] or NULL
+ *  counts     device int32 [B] or NULL
+ *  1 <= B < 2^22, 1 <= k <= 16384, B*k < 2^31; C_ctx, C_store >= 1
+ *  result     device int32 [4], scratch the check writes (owned by the
+ *             caller, so that the call allocates nothing)
+ *  stream     HIP stream (not under graph capture: the call waits for it)
+ */
+lsa_status lsa_check_ids(const int32_t* chunk_ids, const int32_t* slots, const int32_t* counts, int32_t B, int32_t k,
+                         int64_t C_ctx, int64_t C_store, int32_t* result, hipStream_t stream);
 
 /*
  * lsa_fetch_chunks -- host-tier fetch of the selected chunks into HBM.

@@ -14,7 +14,7 @@ from ._binding import (CHUNK_TOKENS, EXPORTS, LIB_PATH, LsaError, alloc_workspac
                        lsa_gather_attend_workspace_size, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
                        lsa_topk_chunks, lsa_topk_tokens, lsa_topk_tokens_workspace_size,
                        alloc_topk_tokens_workspace, lsa_set_tuning, lsa_get_tuning, tuning, TUNE_KNOBS,
-                       lsa_gather_attend_noalloc, NOALLOC_SCRATCH_BYTES)
+                       lsa_gather_attend_noalloc, NOALLOC_SCRATCH_BYTES, lsa_check_ids)
 
 load_library()
 
@@ -24,4 +24,4 @@ __all__ = ["CHUNK_TOKENS", "EXPORTS", "LIB_PATH", "LsaError", "alloc_workspace",
            "lsa_gather_attend_workspace_size", "lsa_index_score", "lsa_pool_assign", "lsa_threshold_chunks", "lsa_topk_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "alloc_topk_tokens_workspace",
            "lsa_set_tuning", "lsa_get_tuning", "tuning", "TUNE_KNOBS", "lsa_gather_attend_noalloc",
-           "NOALLOC_SCRATCH_BYTES"]
+           "NOALLOC_SCRATCH_BYTES", "lsa_check_ids"]

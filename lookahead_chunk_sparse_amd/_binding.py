@@ -26,7 +26,7 @@ CHUNK_TOKENS = 64
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
            "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
-           "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning", "lsa_gather_attend_noalloc")
+           "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning", "lsa_gather_attend_noalloc", "lsa_check_ids")
 
 # bytes of the static split-partials buffer of lsa_gather_attend_noalloc (LSA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 8 << 20
@@ -91,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     L.lsa_fetch_chunks_pull.restype = ctypes.c_int
     L.lsa_pool_assign.argtypes = [vp, vp, i32, vp, i32, i32, i64, vp, vp, vp]
     L.lsa_pool_assign.restype = ctypes.c_int
+    L.lsa_check_ids.argtypes = [vp, vp, vp, i32, i32, i64, i64, vp, vp]
+    L.lsa_check_ids.restype = ctypes.c_int
     L.lsa_set_tuning.argtypes = [ctypes.c_int, i32]
     L.lsa_set_tuning.restype = ctypes.c_int
     L.lsa_get_tuning.argtypes = [ctypes.c_int]
@@ -520,6 +522,31 @@ def lsa_fetch_chunks_pull(host_kv: torch.Tensor, chunk_ids: torch.Tensor, pool_k
         _on(slots, pool_kv.device, "slots")
     _check(load_library().lsa_fetch_chunks_pull(_ptr(host_kv), C, _ptr(chunk_ids), _ptr(slots), _ptr(pool_kv), P,
                                                 B, Hkv, d, k, grid, _stream(stream)))
+
+
+def lsa_check_ids(chunk_ids: torch.Tensor, C_ctx: int, C_store: int | None = None, slots=None, counts=None,
+                  result=None, stream=None):
+    """Check a chunk list (int32 [B][k], with slots [B][k] and counts [B] if
+    given) before it is attended over: ids in [0, C_ctx), store positions in
+    [0, C_store) (C_store defaults to C_ctx), nothing listed twice, counts in
+    [0, k].  Waits for the stream; raises LsaError naming the first offending
+    entry."""
+    _need(chunk_ids, torch.int32, "chunk_ids", 2)
+    B, k = chunk_ids.shape
+    dev = chunk_ids.device
+    if slots is not None:
+        _need(slots, torch.int32, "slots", 2)
+        if tuple(slots.shape) != (B, k):
+            raise ValueError("slots must have the shape of chunk_ids")
+        _on(slots, dev, "slots")
+    if counts is not None:
+        _need(counts, torch.int32, "counts", 1)
+        if tuple(counts.shape) != (B,):
+            raise ValueError("counts must have one entry per request")
+        _on(counts, dev, "counts")
+    result = _out(result, torch.int32, (4,), dev, "result")
+    _check(load_library().lsa_check_ids(_ptr(chunk_ids), _ptr(slots), _ptr(counts), B, k, int(C_ctx),
+                                        int(C_ctx if C_store is None else C_store), _ptr(result), _stream(stream)))
 
 
 def lsa_pool_assign(prev_ids, prev_slots, new_ids: torch.Tensor, P: int, new_slots=None, fetch_slots=None,

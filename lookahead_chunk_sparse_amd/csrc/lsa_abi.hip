@@ -13,6 +13,7 @@
 #include <string>
 
 #include "../../include/lsa.h"
+#include "fetch_runs.h"
 #include "lsa_kernels.h"
 
 namespace {
@@ -104,20 +105,20 @@ int32_t tuning(int knob) {
 
 extern "C" {
 
-lsa_status lsa_set_tuning(lsa_tuning knob, int32_t value) {
-    if ((int)knob < 0 || (int)knob >= LSA_TUNE_COUNT) return fail(LSA_ERR_INVALID_ARGUMENT, "unknown knob %d", (int)knob);
+lsa_status lsa_set_tuning(int32_t knob, int32_t value) {
+    if (knob < 0 || knob >= LSA_TUNE_COUNT) return fail(LSA_ERR_INVALID_ARGUMENT, "unknown knob %d", knob);
     if (!tune_value_ok(knob, value))
         return fail(LSA_ERR_INVALID_ARGUMENT, "value %d out of range for %s", value, kTuneEnv[knob]);
     t_tune[knob] = value;
     return ok();
 }
 
-int32_t lsa_get_tuning(lsa_tuning knob) {
-    if ((int)knob < 0 || (int)knob >= LSA_TUNE_COUNT) return -1;
+int32_t lsa_get_tuning(int32_t knob) {
+    if (knob < 0 || knob >= LSA_TUNE_COUNT) return -1;
     return lsa::tuning(knob);
 }
 
-const char* lsa_status_string(lsa_status s) {
+const char* lsa_status_string(int32_t s) {
     switch (s) {
         case LSA_OK: return "LSA_OK";
         case LSA_ERR_INVALID_ARGUMENT: return "LSA_ERR_INVALID_ARGUMENT";
@@ -261,7 +262,9 @@ static lsa_status gather_attend_impl(const uint16_t* q, const uint16_t* kv, int6
     if (tok) {
         if (k_tok < 1) return fail(LSA_ERR_INVALID_ARGUMENT, "k_tok=%d must be >= 1", k_tok);
         if ((int64_t)B * k_tok >= ((int64_t)1 << 31)) return fail(LSA_ERR_INVALID_ARGUMENT, "B*k_tok must be < 2^31");
-        if (C_store * 2 * Hkv * lsa::kChunkTokens >= ((int64_t)1 << 31))
+        // C_store * rows < 2^31 (row indices are int32), tested without forming the product
+        const int64_t rows = 2 * (int64_t)Hkv * lsa::kChunkTokens;
+        if (C_store >= ((((int64_t)1 << 31) + rows - 1) / rows))
             return fail(LSA_ERR_UNSUPPORTED, "token lists need C_store*2*Hkv*64 < 2^31 (C_store=%lld)",
                         (long long)C_store);
         if (!aligned(tok, 4) || (tok_counts && !aligned(tok_counts, 4)))
@@ -358,22 +361,14 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
         return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv is not pinned host memory (allocate it with hipHostMalloc)");
     }
     const size_t chunk_bytes = (size_t)2 * Hkv * lsa::kChunkTokens * d * sizeof(uint16_t);
-    for (int32_t b = 0; b < B; ++b) {
-        const int32_t* ids = host_chunk_ids + (int64_t)b * k;
-        const int32_t* sl = host_slots ? host_slots + (int64_t)b * k : nullptr;
-        int32_t j = 0;
-        while (j < k) {
-            const int64_t c0 = ids[j];
-            const int64_t p0 = sl ? sl[j] : j;
-            int32_t run = 1;
-            while (j + run < k && ids[j + run] == c0 + run && (sl ? sl[j + run] : j + run) == p0 + run) ++run;
-            const char* src = reinterpret_cast<const char*>(host_kv) + ((int64_t)b * C + c0) * chunk_bytes;
-            char* dst = reinterpret_cast<char*>(pool_kv) + ((int64_t)b * P + p0) * chunk_bytes;
-            hipError_t e = hipMemcpyAsync(dst, src, run * chunk_bytes, hipMemcpyHostToDevice, side_stream);
-            if (e != hipSuccess) return hip_fail(e, "fetch copy");
-            j += run;
-        }
-    }
+    hipError_t copy_err = hipSuccess;
+    lsa::coalesce_fetch_runs(host_chunk_ids, host_slots, B, k, [&](int32_t b, int64_t c0, int64_t p0, int32_t run) {
+        const char* src = reinterpret_cast<const char*>(host_kv) + ((int64_t)b * C + c0) * chunk_bytes;
+        char* dst = reinterpret_cast<char*>(pool_kv) + ((int64_t)b * P + p0) * chunk_bytes;
+        copy_err = hipMemcpyAsync(dst, src, run * chunk_bytes, hipMemcpyHostToDevice, side_stream);
+        return copy_err == hipSuccess;
+    });
+    if (copy_err != hipSuccess) return hip_fail(copy_err, "fetch copy");
     if (done) {
         hipError_t e = hipEventRecord(done, side_stream);
         if (e != hipSuccess) return hip_fail(e, "fetch event record");
@@ -410,6 +405,50 @@ lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32
     hipError_t e = lsa::launch_fetch_pull(static_cast<const uint16_t*>(dev_view), C, chunk_ids, slots, pool_kv, P, B,
                                           Hkv, d, k, grid ? grid : 16, stream);
     if (e != hipSuccess) return hip_fail(e, "fetch-pull launch");
+    return ok();
+}
+
+lsa_status lsa_check_ids(const int32_t* chunk_ids, const int32_t* slots, const int32_t* counts, int32_t B, int32_t k,
+                         int64_t C_ctx, int64_t C_store, int32_t* result, hipStream_t stream) {
+    if (!chunk_ids || !result) return fail(LSA_ERR_INVALID_ARGUMENT, "chunk_ids and result are required");
+    if (B < 1 || k < 1 || C_ctx < 1 || C_store < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "B=%d, k=%d, C_ctx=%lld, C_store=%lld must all be >= 1", B, k,
+                    (long long)C_ctx, (long long)C_store);
+    if (k > lsa::kCheckMaxEntries)
+        return fail(LSA_ERR_UNSUPPORTED, "k=%d: the check handles at most %d entries per request", k,
+                    lsa::kCheckMaxEntries);
+    if (B >= kMaxRowGroups || (int64_t)B * k >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_UNSUPPORTED, "B=%d, k=%d: B must be < 2^22 and B*k < 2^31", B, k);
+    if (!aligned(chunk_ids, 4) || !aligned(result, 4) || (slots && !aligned(slots, 4)) || (counts && !aligned(counts, 4)))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "all pointers need 4-byte alignment");
+    hipError_t e = lsa::launch_check_ids(chunk_ids, slots, counts, B, k, C_ctx, C_store, result, stream);
+    if (e != hipSuccess) return hip_fail(e, "id-check launch");
+    int32_t r[lsa::kCheckResultWords];
+    e = hipMemcpyAsync(r, result, sizeof r, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "id-check result copy");
+    auto value_at = [](const int32_t* p, int32_t at) {
+        int32_t v = 0;
+        (void)hipMemcpy(&v, p + at, sizeof v, hipMemcpyDeviceToHost);
+        return v;
+    };
+    if (r[3] != INT32_MAX) {
+        const int32_t c = value_at(counts, r[3]);
+        return fail(LSA_ERR_INVALID_ARGUMENT, "request %d: count %d outside [0, k=%d]", r[3], c, k);
+    }
+    if (r[0] != INT32_MAX) {
+        const int32_t c = value_at(chunk_ids, r[0]);
+        const int32_t p = slots ? value_at(slots, r[0]) : c;
+        return fail(LSA_ERR_INVALID_ARGUMENT,
+                    "request %d entry %d: chunk id %d (must be in [0, %lld)) at store position %d (must be in [0, %lld))",
+                    r[0] / k, r[0] % k, c, (long long)C_ctx, p, (long long)C_store);
+    }
+    if (r[1] != INT32_MAX)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "request %d entry %d: chunk id %d listed twice", r[1] / k, r[1] % k,
+                    value_at(chunk_ids, r[1]));
+    if (r[2] != INT32_MAX)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "request %d entry %d: store position %d listed twice", r[2] / k, r[2] % k,
+                    value_at(slots, r[2]));
     return ok();
 }
 

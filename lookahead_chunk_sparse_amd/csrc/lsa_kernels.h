@@ -77,6 +77,12 @@ hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_fetch_pull(const uint16_t* host_kv_dev, int64_t C, const int32_t* ids, const int32_t* slots,
                              uint16_t* pool, int64_t P, int B, int Hkv, int d, int k, int grid, hipStream_t stream);
 
+// ---- opt-in validation of chunk lists ----
+constexpr int kCheckMaxEntries = 16384;  // entries per request the check sorts in LDS
+constexpr int kCheckResultWords = 4;     // first bad entry: range, repeated id, repeated slot; first bad count
+hipError_t launch_check_ids(const int32_t* ids, const int32_t* slots, const int32_t* counts, int B, int k,
+                            int64_t C_ctx, int64_t C_store, int32_t* result, hipStream_t stream);
+
 // ---- pool-slot assignment for a delta fetch ----
 size_t pool_assign_lds_bytes(int n_prev, int P);
 hipError_t launch_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int n_prev, const int32_t* new_ids,

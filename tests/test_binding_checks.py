@@ -199,3 +199,16 @@ def test_tuning_environment_is_read_once():
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split()[0] == "2"
+
+
+def test_check_ids_argument_validation(lsa):
+    """lsa_check_ids rejects bad sizes before any HIP call (no GPU here)."""
+    L = lsa.load_library()
+    P = 1 << 20  # never dereferenced
+    assert L.lsa_check_ids(None, None, None, 1, 1, 10, 10, P, None) == 1
+    assert L.lsa_check_ids(P, None, None, 1, 16385, 20000, 20000, P, None) == 2  # beyond the LDS sort
+    assert L.lsa_check_ids(P, None, None, 1 << 22, 1, 10, 10, P, None) == 2
+    assert L.lsa_check_ids(P, None, None, 2, 3, 0, 10, P, None) == 1
+    assert L.lsa_check_ids(P + 2, None, None, 2, 3, 10, 10, P, None) == 1  # misaligned
+    with pytest.raises(ValueError):
+        lsa.lsa_check_ids(torch.zeros((2, 3), dtype=torch.int32), 10, counts=torch.zeros(3, dtype=torch.int32))
