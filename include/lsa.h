@@ -451,15 +451,23 @@ lsa_status lsa_fetch_chunks_pull(const uint16_t* host_kv, int64_t C, const int32
  * exactly the new chunks (entries with slot -1 are skipped), and new_slots
  * are the slots lsa_gather_attend reads S_new from.  S_prev's slots stay
  * untouched, so attention over S_prev may run while S_new is fetched.
+ * An entry with a negative chunk id is not in use: the -1 padding that
+ * lsa_threshold_chunks writes past each request's count.  In S_prev it holds
+ * no slot (its slot is not read); in S_new it gets new_slots = fetch_slots
+ * = -1, so the pull fetch skips it (and attention, given the counts, never
+ * reads it).  Variable-size selections thus go through unchanged.
  *
- *  prev_ids    device int32 [B][n_prev], ascending within each row (as
- *              lsa_topk_chunks writes them); may be NULL when n_prev = 0
- *  prev_slots  device int32 [B][n_prev], distinct within a row, in [0, P)
+ *  prev_ids    device int32 [B][n_prev], ascending within each row among the
+ *              entries in use (as lsa_topk_chunks and lsa_threshold_chunks
+ *              write them); may be NULL when n_prev = 0
+ *  prev_slots  device int32 [B][n_prev], distinct within a row and in
+ *              [0, P) for the entries in use
  *  n_prev      0 for the first selection (every chunk is new)
- *  new_ids     device int32 [B][k], ascending within each row
+ *  new_ids     device int32 [B][k], ascending within each row among the
+ *              entries in use
  *  B           requests, 1 <= B < 2^22
  *  P           pool slots per request, >= n_prev + k;
- *              (n_prev + P) * 4 + P <= 65536 (LSA_ERR_UNSUPPORTED otherwise)
+ *              (2 n_prev + P) * 4 + P <= 65536 (LSA_ERR_UNSUPPORTED otherwise)
  *  new_slots, fetch_slots  device int32 [B][k] outputs
  */
 lsa_status lsa_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int32_t n_prev, const int32_t* new_ids,

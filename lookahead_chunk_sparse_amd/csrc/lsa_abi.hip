@@ -462,7 +462,7 @@ lsa_status lsa_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, i
     if (P < (int64_t)n_prev + k)
         return fail(LSA_ERR_INVALID_ARGUMENT, "P=%lld must be >= n_prev + k = %d", (long long)P, n_prev + k);
     if (P > INT32_MAX || lsa::pool_assign_lds_bytes(n_prev, (int)P) > 65536)
-        return fail(LSA_ERR_UNSUPPORTED, "n_prev=%d, P=%lld: the assignment needs (n_prev + P) * 4 + P <= 65536 bytes",
+        return fail(LSA_ERR_UNSUPPORTED, "n_prev=%d, P=%lld: the assignment needs (2 n_prev + P) * 4 + P <= 65536 bytes",
                     n_prev, (long long)P);
     hipError_t e = lsa::launch_pool_assign(prev_ids, prev_slots, n_prev, new_ids, B, k, (int)P, new_slots, fetch_slots,
                                            stream);

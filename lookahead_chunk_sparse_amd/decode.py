@@ -34,9 +34,10 @@ passed to attend() (summary 2.1 Architecture: the native token-level top-k
 runs over the recalled subset only; the pages give no scoring formula, so
 the scores are an input), and attends over those tokens.
 
-Several layers can share one selection (kv given as a list of per-layer
-stores): each interval runs one indexer scan and selection, then every step
-attends over the same chunks in every layer.  Reusing one layer's selection
+Several layers can share one selection (kv, or host_kv, given as a list of
+per-layer stores): each interval runs one indexer scan and selection, then
+every step attends over the same chunks in every layer.  On the host tier
+every layer has its own HBM pool, filled at the same slots.  Reusing one layer's selection
 in the following layers is how the indexer cost is amortised across depth
 (the "Daily Papers" listing for the query "lightning indexer": the LongCat
 LSA abstract's cross-layer indexing, and the Multi-layer Indexer and
@@ -70,7 +71,8 @@ class LsaDecoder:
     ctx_len  device int32 [B]
     kv       device bf16 [B][C][2][Hkv][64][d]        (HBM-resident store; a list
                                                         of such: one per layer), or
-    host_kv  pinned bf16 [B][C][2][Hkv][64][d]        (host tier; pool of k slots x 2)
+    host_kv  pinned bf16 [B][C][2][Hkv][64][d]        (host tier; a list of such:
+                                                        one per layer, one pool each)
     """
 
     def __init__(self, *, k_idx: torch.Tensor, ctx_len: torch.Tensor, Hq: int, k: int, alpha: float,
@@ -84,10 +86,12 @@ class LsaDecoder:
         self.k_idx = k_idx
         self.ctx_len = ctx_len
         self.layers = list(kv) if isinstance(kv, (list, tuple)) else None
+        self.host_layers = list(host_kv) if isinstance(host_kv, (list, tuple)) else None
         if self.layers is not None:
-            if host_kv is not None:
-                raise NotImplementedError("several layers are implemented for the HBM-resident store")
             kv = self.layers[0]
+        if self.host_layers is not None:
+            host_kv = self.host_layers[0]
+            self.layers = self.host_layers  # one attention per layer, each on its own pool
         # resident segment: the local window and the decoded tokens, always in
         # HBM and attended with the recalled chunks (ctx_len then bounds only
         # the offloadable history); the caller appends to it and bumps seg_len
@@ -111,8 +115,8 @@ class LsaDecoder:
         self.fetch, self.fetch_grid = fetch, fetch_grid
         if selection not in ("topk", "threshold"):
             raise ValueError("selection must be 'topk' or 'threshold'")
-        if selection == "threshold" and host_kv is not None:
-            raise NotImplementedError("threshold selection is implemented for the HBM-resident store")
+        if selection == "threshold" and host_kv is not None and fetch == "memcpy":
+            raise NotImplementedError("threshold selection on the host tier uses the pull fetch (ids stay on the GPU)")
         self.selection, self.logit_threshold = selection, int(logit_threshold)
         self.delta = (fetch == "pull") if delta is None else bool(delta)
         if self.delta and fetch != "pull":
@@ -137,14 +141,19 @@ class LsaDecoder:
         else:
             self.workspace = alloc_workspace(B, Hq, self.Hkv, self.d, k, n_split, device=dev)
         if self.lag:
+            n_pools = len(self.host_layers) if self.host_layers is not None else 1
+            self.pools = []  # per layer: the pool buffers of selections 0 and 1
+            for _ in range(n_pools):
+                if self.delta:
+                    one = torch.empty((B, 2 * k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
+                    self.pools.append([one, one])  # one pool, indexed through per-selection slots
+                else:
+                    self.pools.append([torch.empty((B, k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16,
+                                                   device=dev) for _ in range(2)])
+            self.pool = self.pools[0]
             if self.delta:
-                one = torch.empty((B, 2 * k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
-                self.pool = [one, one]  # one pool, indexed through per-selection slots
                 self.sel_slots = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
                 self.fetch_slots = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
-            else:
-                self.pool = [torch.empty((B, k, 2, self.Hkv, self.T, self.d), dtype=torch.bfloat16, device=dev)
-                             for _ in range(2)]
             self.slots = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
             self.host_ids = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)]
             self.side = torch.cuda.Stream(device=dev)
@@ -184,9 +193,10 @@ class LsaDecoder:
             tok = dict(tok=self.tok, tok_counts=self.tok_counts)
         if self.lag:
             slots = self.sel_slots[sel % 2] if self.delta else self.slots
-            return lsa_gather_attend(q, self.pool[sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
+            return lsa_gather_attend(q, self.pools[layer][sel % 2], ids, self.ctx_len, self.sm_scale, slots=slots,
                                      workspace=self.workspace, n_split=self.n_split, out=out,
-                                     seg_kv=self.seg_kv, seg_len=self.seg_len, stream=stream, **tok)
+                                     counts=self.sel_counts[sel % 2], seg_kv=self.seg_kv, seg_len=self.seg_len,
+                                     stream=stream, **tok)
         kv = self.layers[layer] if self.layers is not None else self.kv
         return lsa_gather_attend(q, kv, ids, self.ctx_len, self.sm_scale, workspace=self.workspace,
                                  n_split=self.n_split, out=out, counts=self.sel_counts[sel % 2],
@@ -224,7 +234,11 @@ class LsaDecoder:
         src = max(i - 1, 0)
         main.wait_event(self.fetch_done[src % 2])
         for q, o, sc in zip(qs, outs, ts):
-            self.attend(q, src, o, token_scores=sc)
+            if self.layers is None:
+                self.attend(q, src, o, token_scores=sc)
+            else:  # q[l] and o[l] per layer; one selection, one pool per layer
+                for layer in range(len(self.layers)):
+                    self.attend(q[layer], src, o[layer], layer=layer)
         if i >= 1:
             self._fetch(i)  # overlaps the steps just enqueued
         self.attn_done.record(main)
@@ -237,13 +251,15 @@ class LsaDecoder:
             self.side.wait_event(self.attn_done)
         if self.fetch == "memcpy":
             self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
-            lsa_fetch_chunks(self.host_kv, self.host_ids[i % 2], self.pool[i % 2], host_slots=None,
-                             stream=self.side, done=None)
+            for host, pool in zip(self.host_layers or [self.host_kv], self.pools):
+                lsa_fetch_chunks(host, self.host_ids[i % 2], pool[i % 2], host_slots=None, stream=self.side,
+                                 done=None)
         else:
             self.side.wait_event(self.ev_sel)  # selection i (and its slots) are on the device
-            lsa_fetch_chunks_pull(self.host_kv, self.sel_ids[i % 2], self.pool[i % 2],
-                                  slots=self.fetch_slots[i % 2] if self.delta else None, grid=self.fetch_grid,
-                                  stream=self.side)
+            for host, pool in zip(self.host_layers or [self.host_kv], self.pools):
+                lsa_fetch_chunks_pull(host, self.sel_ids[i % 2], pool[i % 2],
+                                      slots=self.fetch_slots[i % 2] if self.delta else None, grid=self.fetch_grid,
+                                      stream=self.side)
         self.fetch_done[i % 2].record(self.side)
 
     def join(self) -> None:

@@ -35,7 +35,9 @@
  *  6. Pool slots of a delta fetch (the same passages: only the chunks not
  *     already recalled need fetching): a chunk kept from the previous
  *     selection keeps its slot; the r-th new chunk in ascending id order takes
- *     the r-th lowest slot the previous selection does not hold.
+ *     the r-th lowest slot the previous selection does not hold.  Entries
+ *     with a negative id (the padding of a variable-size selection) are not
+ *     in use.
  *  7. Threshold selection (summary 2.1 Architecture, 2.4 Configuration:
  *     sigmoid gating at 0.5 instead of a fixed top-k): the chunks whose logit
  *     exceeds a threshold, capped at k_max by the same order as item 3.
@@ -266,7 +268,10 @@ int oracle_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* chunk
  *    prev_ids keeps that entry's slot (fetch_slots[j] = -1); otherwise it
  *    takes the next slot, in ascending order, held by no entry of the
  *    previous selection (fetch_slots[j] = that slot).  new_ids is walked in
- *    the order given (ascending for selections).
+ *    the order given (ascending for selections).  An entry with a negative
+ *    chunk id is not in use (the -1 padding of a threshold selection past its
+ *    count): in prev_ids it holds no slot, and in new_ids it gets
+ *    new_slots[j] = fetch_slots[j] = -1.
  *    Returns 0; -1 for a previous slot outside [0, P); -2 if the free slots
  *    run out. */
 int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64_t n_prev, const int32_t* new_ids,
@@ -276,6 +281,7 @@ int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64
     for (int64_t b = 0; b < B && rc == 0; ++b) {
         memset(held, 0, (size_t)P);
         for (int64_t j = 0; j < n_prev; ++j) {
+            if (prev_ids[b * n_prev + j] < 0) continue; /* not in use */
             const int64_t sl = prev_slots[b * n_prev + j];
             if (sl < 0 || sl >= P) { rc = -1; break; }
             held[sl] = 1;
@@ -283,6 +289,11 @@ int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64
         int64_t next = 0;
         for (int64_t j = 0; j < k && rc == 0; ++j) {
             const int32_t c = new_ids[b * k + j];
+            if (c < 0) { /* not in use */
+                new_slots[b * k + j] = -1;
+                fetch_slots[b * k + j] = -1;
+                continue;
+            }
             int64_t found = -1;
             for (int64_t q = 0; q < n_prev; ++q)
                 if (prev_ids[b * n_prev + q] == c) { found = q; break; }

@@ -406,6 +406,50 @@ def test_pool_assign_chain_keeps_pool_consistent(oracle_lib, synth_lib):
         prev_ids, prev_slots = ids, ns
 
 
+def test_pool_assign_variable_counts(oracle_lib, synth_lib):
+    """Selections of varying size, padded with -1 past each count (as the
+    threshold select writes them): padding in the previous list holds no
+    slot, padding in the new list gets slot -1 and is not fetched, and the
+    pool stays consistent across a chain of such selections."""
+    B, C, k = 3, 40, 9
+    P = 2 * k
+    host = synth_lib.normal_bf16((B, C, 2, 1, 64, 8), 5, synth_lib.stream(synth_lib.TAG_MISC, 1750))
+    pool = np.zeros((B, P, 2, 1, 64, 8), dtype=np.uint16)
+    rng = np.random.default_rng(5)
+    prev_ids = prev_slots = None
+    for step in range(15):
+        counts = rng.integers(0, k + 1, B)
+        ids = np.full((B, k), -1, dtype=np.int32)
+        for b in range(B):
+            ids[b, :counts[b]] = np.sort(rng.choice(C if step % 3 else 14, counts[b], replace=False))
+        ns, fs = oracle_lib.pool_assign(prev_ids, prev_slots, ids, P)
+        for b in range(B):
+            n = int(counts[b])
+            assert (ns[b, n:] == -1).all() and (fs[b, n:] == -1).all()
+            used = ns[b, :n]
+            assert len(set(used.tolist())) == n and (used >= 0).all() and (used < P).all()
+            prev_map = {}
+            if prev_ids is not None:
+                prev_map = {c: s for c, s in zip(prev_ids[b].tolist(), prev_slots[b].tolist()) if c >= 0}
+            held = set(prev_map.values())
+            fetched = []
+            for j in range(n):
+                c = int(ids[b, j])
+                if c in prev_map:
+                    assert ns[b, j] == prev_map[c] and fs[b, j] == -1
+                else:
+                    assert fs[b, j] == ns[b, j] and ns[b, j] not in held
+                    fetched.append(int(ns[b, j]))
+            free = [x for x in range(P) if x not in held]
+            assert fetched == free[:len(fetched)]
+        oracle_lib.fetch_chunks(host, np.maximum(ids, 0), P, slots=fs, pool=pool, skip_negative_slots=True)
+        for b in range(B):
+            for j in range(int(counts[b])):
+                assert np.array_equal(pool[b, ns[b, j]], host[b, ids[b, j]]), (step, b, j)
+        # the slots of entries not in use are not looked at: make them garbage
+        prev_ids, prev_slots = ids, np.where(ids >= 0, ns, 10 ** 6).astype(np.int32)
+
+
 # ---------------------------------------------------------------- threshold selection
 
 def brute_threshold(row, thr, k_max):
