@@ -53,12 +53,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attend_bytes_per_launch(w, seg: int = 0) -> int:
+def attend_bytes_per_launch(w, seg: int = 0, k_eff: float | None = None) -> int:
     """Algorithmic HBM bytes of one attention launch: the retained K and V
-    tiles of every (request, KV head), the K and V rows of a resident segment
-    of `seg` tokens per request if any, the bf16 queries, the fp32 outputs
-    and the chunk ids."""
-    kv = w.B * w.Hkv * w.k * 2 * w.T * w.d * 2
+    tiles of every (request, KV head) (k_eff chunks per request on average
+    when selections vary in size, else k), the K and V rows of a resident
+    segment of `seg` tokens per request if any, the bf16 queries, the fp32
+    outputs and the chunk ids."""
+    kv = int(w.B * w.Hkv * (w.k if k_eff is None else k_eff) * 2 * w.T * w.d * 2)
     sk = w.B * w.Hkv * seg * 2 * w.d * 2
     q = w.B * w.Hq * w.d * 2
     out = w.B * w.Hq * w.d * 4
@@ -66,11 +67,11 @@ def attend_bytes_per_launch(w, seg: int = 0) -> int:
     return kv + sk + q + out + ids
 
 
-def step_bytes(w, layers: int = 1, seg: int = 0) -> int:
+def step_bytes(w, layers: int = 1, seg: int = 0, k_eff: float | None = None) -> int:
     """Algorithmic bytes of one decode step: one attention launch per layer
     plus the indexer scan (every key byte once, one scan shared by all
     layers) amortised over tau steps."""
-    return layers * attend_bytes_per_launch(w, seg) + (w.B * w.C * w.d_idx) // w.tau
+    return layers * attend_bytes_per_launch(w, seg, k_eff) + (w.B * w.C * w.d_idx) // w.tau
 
 
 def kernel_sha() -> str:
@@ -91,7 +92,7 @@ def traffic_for_current_kernel(w):
     return t.get("hbm_bytes_per_launch")
 
 
-def setup(w, n_split: int, layers: int = 1):
+def setup(w, n_split: int, layers: int = 1, selection: str = "topk"):
     import torch
 
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
@@ -105,9 +106,10 @@ def setup(w, n_split: int, layers: int = 1):
     if layers > 1:  # further layers: the same synthetic recipe, each its own store
         stores = [kv] + [W.device_kv_store(w.replace(seed=w.seed + 1000 * l), dev) for l in range(1, layers)]
         dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=stores, n_split=n_split,
-                         device=dev)
+                         selection=selection, device=dev)
     else:
-        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split, device=dev)
+        dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, kv=kv, n_split=n_split,
+                         selection=selection, device=dev)
     log(f"[bench] inputs placed in HBM in {time.time() - t0:.1f}s (K/V {layers * kv.numel() * 2 / 1e9:.2f} GB, "
         f"{layers} layer(s))")
     return dec
@@ -345,6 +347,31 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
                    "interval_ms": round(ms_total / n_time_int, 2)},
     }
     print(json.dumps(res), flush=True)
+
+
+def gating_stats(dec, w, qidx) -> dict:
+    """Sigmoid gating (sigma > 0.5, i.e. logit > 0) on this workload's
+    indexer, outside any timed region: per interval and request, how many
+    chunks pass before the cap, how many are kept (at most k), and how often
+    the cap binds."""
+    import torch
+
+    from lookahead_chunk_sparse_amd import lsa_index_score, lsa_threshold_chunks
+    passing, kept = [], []
+    for i, q in enumerate(qidx):
+        logits, _ = lsa_index_score(q, dec.k_idx, w.alpha, want_scores=False)
+        _, n_all = lsa_threshold_chunks(logits.view(w.B, w.C), w.C, dec.logit_threshold)
+        _, n_cap = lsa_threshold_chunks(logits.view(w.B, w.C), w.k, dec.logit_threshold)
+        passing.append(n_all.cpu())
+        kept.append(n_cap.cpu())
+    passing, kept = torch.stack(passing).double(), torch.stack(kept).double()
+    q = torch.tensor([0.0, 0.5, 1.0], dtype=torch.float64)
+    return {"intervals": len(qidx), "requests": w.B, "cap": w.k, "chunks": w.C,
+            "passing_min_median_max": [round(float(x), 1) for x in torch.quantile(passing.flatten(), q)],
+            "passing_frac_of_chunks_mean": round(float(passing.mean()) / w.C, 4),
+            "kept_min_median_max": [round(float(x), 1) for x in torch.quantile(kept.flatten(), q)],
+            "kept_mean": round(float(kept.mean()), 2), "kept_mean_first_interval": round(float(kept[0].mean()), 2),
+            "cap_binds_frac": round(float((passing > w.k).double().mean()), 4)}
 
 
 def token_attend_bytes(w, k_tok: int) -> int:
@@ -601,6 +628,8 @@ def main():
     ap.add_argument("--token-topk", type=int, default=0, metavar="K_TOK",
                     help="two-stage selection: attend over the K_TOK best tokens of the recalled chunks")
     ap.add_argument("--layers", type=int, default=1, help="layers sharing one selection (HBM-resident only)")
+    ap.add_argument("--selection", default="topk", choices=("topk", "threshold"),
+                    help="chunk selection: top-k, or sigmoid gating (sigma > 0.5) capped at k")
     ap.add_argument("--segment", type=int, default=0, metavar="S",
                     help="resident tokens per request (local window, decoded tokens, compressed entries) "
                          "attended in the same softmax as the recalled chunks (HBM-resident, one layer)")
@@ -644,7 +673,7 @@ def main():
         host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
                         False if args.no_delta else None)
         return
-    dec = setup(w, args.n_split, args.layers)
+    dec = setup(w, args.n_split, args.layers, args.selection)
     if args.segment:
         if args.layers != 1:
             print("--segment runs with one layer", file=sys.stderr)
@@ -693,9 +722,13 @@ def main():
     log(f"[bench] {args.repeats} runs of {args.steps} steps: median {ms_total:.3f} ms, min {min(ms_runs):.3f}, "
         f"max {max(ms_runs):.3f} (wall {t_wall * 1e3:.1f} ms for all runs)")
 
-    # ---- the dominant kernel, event-timed on its own stream ----
+    gating = gating_stats(dec, w, qidx[:(args.steps + w.tau - 1) // w.tau]) if args.selection == "threshold" else None
+    k_step = gating["kept_mean"] if gating else None  # chunks attended per request and step, on average
+
+    # ---- the dominant kernel, event-timed on its own stream (interval 0's selection) ----
+    dec.reselect(qidx[0], 0)
     mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
-    a_bytes = attend_bytes_per_launch(w, args.segment)
+    a_bytes = attend_bytes_per_launch(w, args.segment, gating["kept_mean_first_interval"] if gating else None)
     achieved = a_bytes / (mean_ms * 1e-3) / 1e9
     log(f"[bench] attention launch: mean {mean_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
         f"{achieved:.0f} GB/s algorithmic")
@@ -705,7 +738,7 @@ def main():
     ceiling = read_ceiling(dec.kv)
     log(f"[bench] read ceiling, random 16 KB tiles of the K/V store: {ceiling['GBs']:.0f} GB/s")
 
-    sb = step_bytes(w, args.layers, args.segment)
+    sb = step_bytes(w, args.layers, args.segment, k_step)
     layer_txt = "one layer" if args.layers == 1 else f"{args.layers} layers sharing one selection"
     if args.segment:
         layer_txt += f", plus {args.segment} resident tokens per request in the same softmax"
@@ -757,7 +790,12 @@ def main():
             "mean_launch_us": round(mean_ms * 1e3, 2),
         },
     }
-    if not args.no_cpu_baseline and not args.segment:  # the oracle sample has no segment
+    if args.selection == "threshold":
+        result["metric"] = metric_for(w) + ", sigmoid gating capped at k"
+        result["config"]["selection"] = "sigmoid gating: logit > 0 (sigma > 0.5), at most k chunks"
+        result["config"]["gating"] = gating
+        log(f"[bench] gating: {gating}")
+    if not args.no_cpu_baseline and not args.segment and args.selection == "topk":  # the oracle sample has no segment
         log("[bench] timing the CPU oracle on a bounded sample (all cores, then 1 thread) ...")
         cb = cpu_baseline(w, args.cpu_budget)
         cb["single_thread"] = cpu_baseline(w, 0.6 * args.cpu_budget, threads=1)

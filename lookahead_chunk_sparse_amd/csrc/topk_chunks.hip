@@ -36,6 +36,7 @@
 // tokens only (same summary, 2.1 Architecture); there the keys are float
 // scores over the list positions of the recalled chunks.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -157,6 +158,7 @@ struct TopkArgs {
     int n_slices;               // slice, candidates
     int32_t* cand_pos;          // [R][n_slices][k] positions (written by slice, read by candidates)
     uint32_t* cand_key;         // [R][n_slices][k] keys, 0 = none
+    int sample_rank;            // tokens mode: rank of the sample key that bounds the candidates (0: off)
 };
 
 // A bucket of at most kListCap keys moves from registers into LDS; one of at
@@ -215,6 +217,180 @@ __device__ inline void ballot_finish(const uint32_t* lst, int cnt, int hi, int n
     }
 }
 
+// Token mode's candidate path: 16 keys per wave (256 in all) are a sample of
+// the row; the 12-bit key prefix of the sample key of rank sample_rank bounds
+// a candidate set (every key at or above that prefix) that holds the kept
+// keys whenever it has at least k members; it is then selected from in LDS.
+constexpr int kSamplePerWave = 16;
+constexpr int kSampleBits = 12;        // key prefix the sample decides
+constexpr int kCandCap = 8192;         // candidates held in LDS (keys and positions)
+constexpr int kCandCopies = 16;        // histogram copies of the candidate passes
+
+// Exclusive block-wide sums of two per-thread counts (2 barriers).
+__device__ inline void block_excl_scan2(int& a, int& b, int* sm_a, int* sm_b, int lane, int wave) {
+    int ia = a, ib = b;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int ua = __shfl_up(ia, off), ub = __shfl_up(ib, off);
+        if (lane >= off) {
+            ia += ua;
+            ib += ub;
+        }
+    }
+    if (lane == 63) {
+        sm_a[wave] = ia;
+        sm_b[wave] = ib;
+    }
+    __syncthreads();
+    int pa = 0, pb = 0;
+    for (int w = 0; w < wave; ++w) {
+        pa += sm_a[w];
+        pb += sm_b[w];
+    }
+    __syncthreads();
+    a = pa + ia - a;
+    b = pb + ib - b;
+}
+
+// Token mode, register-resident row of KPT keys per thread, kk < competing
+// keys.  The sample's prefix of rank `rank` (one wave, bit by bit) gives the
+// bound pv; if between kk and kCandCap keys reach it, they are copied to LDS
+// in position order with their positions, the kk-th largest is found among
+// them alone (8-bit digit passes, then one wave bit by bit), and the kept
+// positions are written in ascending order.  Returns false, having written
+// nothing, when the count misses (then the full select runs); the decision
+// is uniform over the workgroup.  The row's counts and -1 padding are the
+// caller's.  Uses sm_raw: [0, 4096) histogram, [4096, 4352) small bucket,
+// [16384, 16384 + kCandCap) keys, then positions.
+template <int KPT>
+__device__ __forceinline__ bool tokens_candidate_select(const uint32_t (&key)[KPT], int kk, uint32_t kmax, int rank, int wbase,
+                                        int tid, int lane, int wave, const uint32_t* sm_sample, uint32_t* sm_raw,
+                                        int* sm_i, int* sm_j, int* sm_tot, int* sm_pick, int32_t* dst) {
+    int* const hist = reinterpret_cast<int*>(sm_raw);           // [256][kCandCopies]
+    uint32_t* const small = sm_raw + kBins * kCandCopies;       // <= kBallotMax keys
+    uint32_t* const ckey = sm_raw + kBins * kLaneCopies;        // [kCandCap]
+    uint32_t* const cpos = ckey + kCandCap;                     // [kCandCap]
+    static_assert(kBins * kCandCopies + kBallotMax <= kBins * kLaneCopies, "histogram and bucket fit below the lists");
+    static_assert(kBins * kLaneCopies + 2 * kCandCap <= kBins * kLaneCopies + 2 * kListCap, "candidates fit the lists");
+
+    // --- the bound: the 12-bit prefix of the sample key of rank `rank` ---
+    if (wave == 0) ballot_finish<kBallotSlots>(sm_sample, kWaves * kSamplePerWave, kSampleBits, rank, lane, sm_pick);
+    __syncthreads();
+    uint32_t pv = (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]) << (32 - kSampleBits);
+    pv = pv ? pv : 1u;  // key 0 does not compete
+    int n_w = 0;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) n_w += __popcll(__ballot(key[e] >= pv));
+    if (lane == 0) sm_i[wave] = n_w;
+    __syncthreads();
+    int c = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int x = sm_i[w];
+        c += x;
+        before += w < wave ? x : 0;
+    }
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c < kk || c > kCandCap) return false;  // uniform
+
+    // --- the candidates, in position order ---
+    before = __builtin_amdgcn_readfirstlane(before);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const bool in = key[e] >= pv;
+        const uint64_t m = __ballot(in);
+        if (in) {
+            const int at = before + lanes_below(m);
+            ckey[at] = key[e];
+            cpos[at] = (uint32_t)(wbase + 64 * e + lane);
+        }
+        before += __popcll(m);
+    }
+    __syncthreads();
+
+    // --- the kk-th largest candidate: digits of key - pv from the top ---
+    const uint32_t range = kmax - pv;
+    int hi = range == 0u ? 0 : 32 - __builtin_clz(range);
+    uint32_t rstar = 0;
+    int need = kk, cnt = c;
+    auto ub_of = [&](int h) {
+        const uint32_t span = h >= 32 ? 0xFFFFFFFFu : (1u << h) - 1u;
+        return min(span, range - rstar);
+    };
+    while (hi > 0) {
+        const uint32_t base = pv + rstar;
+        if (cnt <= kBallotMax) {
+            // the bucket's keys (relative to base) into a small list; one
+            // wave then decides the remaining bits
+            const uint32_t ub = ub_of(hi);
+            if (tid == 0) sm_tot[0] = 0;
+            __syncthreads();
+            for (int i0 = 0; i0 < c; i0 += kThreads) {
+                const int i = i0 + tid;
+                const uint32_t d = i < c ? ckey[i] - base : 0xFFFFFFFFu;
+                const bool in = i < c && d <= ub;
+                const uint64_t m = __ballot(in);
+                int at = 0;
+                if (lane == 0 && m) at = atomicAdd(&sm_tot[0], __popcll(m));
+                at = __builtin_amdgcn_readfirstlane(at);
+                if (in) small[at + lanes_below(m)] = d;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                if (cnt <= 64)
+                    ballot_finish<1>(small, cnt, hi, need, lane, sm_pick);
+                else
+                    ballot_finish<kBallotSlots>(small, cnt, hi, need, lane, sm_pick);
+            }
+            __syncthreads();
+            rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
+            need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
+            cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
+            break;
+        }
+        const int w = hi < kDigitBits ? hi : kDigitBits;
+        const int sh = hi - w;
+        const uint32_t ub = ub_of(hi);
+        for (int j = tid; j < kBins * kCandCopies / 4; j += kThreads)
+            reinterpret_cast<int4*>(hist)[j] = make_int4(0, 0, 0, 0);
+        __syncthreads();
+        for (int i = tid; i < c; i += kThreads) {
+            const uint32_t d = ckey[i] - base;
+            if (d <= ub) atomicAdd(&hist[(int)(d >> sh) * kCandCopies + (lane & (kCandCopies - 1))], 1);
+        }
+        __syncthreads();
+        pick_digit<kCandCopies>(hist, sm_tot, sm_pick, tid, lane, wave, need);
+        rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]) << sh;
+        need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
+        cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
+        hi = sh;
+    }
+    const uint32_t vstar = pv + rstar;
+    const bool all_eq = need == cnt;  // every key equal to v* is kept
+
+    // --- the kept positions, ascending: candidates > v*, and the first `need`
+    // equal to v* in position order; each thread a contiguous run ---
+    const int per = (c + kThreads - 1) / kThreads;
+    const int i0 = min(tid * per, c), i1 = min(i0 + per, c);
+    int n_gt = 0, n_eq = 0;
+    for (int i = i0; i < i1; ++i) {
+        n_gt += ckey[i] > vstar;
+        n_eq += ckey[i] == vstar;
+    }
+    int gt_before = n_gt, eq_before = n_eq;
+    block_excl_scan2(gt_before, eq_before, sm_i, sm_j, lane, wave);
+    int out = gt_before + (all_eq ? eq_before : min(eq_before, need));
+    int eq_seen = eq_before;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t v = ckey[i];
+        const bool eq = v == vstar;
+        const bool take = v > vstar || (eq && (all_eq || eq_seen < need));
+        eq_seen += eq;
+        if (take && out < kk) dst[out++] = (int32_t)cpos[i];
+    }
+    return true;
+}
+
 template <int KPT, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     constexpr bool kScoreKeys = MODE != kModeLogits;  // key 0 marks a position that does not compete
@@ -232,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[3];  // digit chosen by a pass, keys still needed, keys in the digit
     __shared__ int sm_cnt[2];
+    __shared__ uint32_t sm_sample[MODE == kModeTokens ? kWaves * kSamplePerWave : 1];  // key prefixes
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int k = a.k;
@@ -343,6 +520,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         sm_avail[wave] = avail;
     }
     if (tid == 0) sm_cnt[0] = 0;
+    if constexpr (MODE == kModeTokens) {
+        // the sample: lane l < 16 of each wave gives its slot l % KPT, a
+        // position in list entry l % KPT of the wave's range (key 0: not
+        // competing, the smallest)
+        if (lane < kSamplePerWave) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) v = (e == lane % KPT) ? key[e] : v;
+            sm_sample[wave * kSamplePerWave + lane] = v >> (32 - kSampleBits);
+        }
+    }
     __syncthreads();
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     avail = 0;
@@ -371,6 +559,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         if (kk == 0) return;  // uniform: every thread saw the same sum
     }
     const int n_ok = kScoreKeys ? avail : C;  // competing keys
+
+    if constexpr (MODE == kModeTokens) {
+        if (a.sample_rank > 0 && kk < n_ok &&
+            tokens_candidate_select<KPT>(key, kk, kmax, a.sample_rank, wbase, tid, lane, wave, sm_sample, sm_raw,
+                                         sm_i, sm_j, sm_tot, sm_pick, dst))
+            return;
+    }
 
     // --- radix select ---
     // On r = key - kmin: a competing key has r in [0, range].  A score key
@@ -835,6 +1030,18 @@ hipError_t launch_mode(const TopkArgs& a, int grid, int positions, hipStream_t s
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Rank, among the 256 sample keys, whose 12-bit prefix bounds the token
+// candidates: the expected rank of the k_tok-th largest key (256 k/n), plus
+// three binomial standard deviations and 4, so that fewer than k_tok keys
+// reach the bound only rarely (the full select then runs).  0 (no candidate
+// path) when the bound would keep most of the row anyway.
+int token_sample_rank(int n, int k_tok) {
+    if (n <= 0 || k_tok >= n) return 0;
+    const double S = kWaves * kSamplePerWave, p = (double)k_tok / n;
+    const double r = S * p + 3.0 * sqrt(S * p * (1.0 - p)) + 4.0;
+    return r > 0.75 * S ? 0 : (int)ceil(r);
+}
+
 }  // namespace
 
 // Split of a token row of 64*n_list positions into slices for the
@@ -920,6 +1127,7 @@ hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, cons
         hipLaunchKernelGGL((topk_stream_kernel<true>), dim3((unsigned)R), dim3(kThreads), 0, stream, a);
         return hipGetLastError();
     }
+    a.sample_rank = token_sample_rank(a.C, k_tok);
     return launch_mode<kModeTokens>(a, R, a.C, stream);
 }
 

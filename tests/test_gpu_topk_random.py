@@ -120,3 +120,54 @@ def test_topk_tokens_random(lsa, oracle_lib, synth_lib, tune, case):
                                   counts=None if counts is None else to_dev(counts), workspace="auto")
     assert np.array_equal(tc.cpu().numpy(), rc), (case, B, C, k, k_tok, kind, split)
     assert np.array_equal(tok.cpu().numpy(), ref), (case, B, C, k, k_tok, kind, split)
+
+
+# ---- the token select's candidate path and its fallbacks -----------------
+
+def _sample_positions(n_pos: int):
+    """Positions whose keys form the token select's sample: lanes 0-15 of
+    each of the 16 waves, slot (lane mod KPT) of the wave's KPT list entries."""
+    kpt = -(-n_pos // 1024)
+    pos = np.array([w * 64 * kpt + 64 * (l % kpt) + l for w in range(16) for l in range(16)])
+    return pos[pos < n_pos]  # the last wave's range runs past the row: those slots do not compete
+
+
+@pytest.mark.parametrize("kind", ["normal", "quarters", "all_equal", "sample_high", "few_competing", "tiny_k",
+                                  "k_near_n", "negative"])
+def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
+    """Rows that take the candidate path (a sample bound, then a select
+    among the keys at or above it) and rows that miss it on purpose and run
+    the full select: all keys equal (more candidates than LDS holds), the
+    largest scores placed exactly on the sample (too few candidates), fewer
+    competing positions than k_tok, and extreme k_tok.  Bit-exact with the
+    oracle either way."""
+    B, C, k = 3, 2048, 276
+    n = k * 64
+    s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), 31, synth_lib.stream(synth_lib.TAG_MISC, 6500)))
+    k_tok = 2048
+    ids = np.stack([np.sort(synth_lib.choose(k, C, 5, synth_lib.stream(synth_lib.TAG_MISC, 6600 + b)))
+                    for b in range(B)]).astype(np.int32)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    counts = None
+    if kind == "quarters":
+        s = np.round(s * 4) / 4
+    elif kind == "all_equal":
+        s[:] = 0.75
+    elif kind == "sample_high":
+        s = s - 10.0
+        s[:, _sample_positions(n)] = 5.0 + s[:, _sample_positions(n)] / 100
+    elif kind == "few_competing":
+        counts = np.array([20, 40, k], dtype=np.int32)  # 1,280 and 2,560 positions compete
+        ctx[2] = int(ids[2, 30]) * 64 + 7
+    elif kind == "tiny_k":
+        k_tok = 1
+    elif kind == "k_near_n":
+        k_tok = n - 5
+    elif kind == "negative":
+        s = -np.abs(s) - 1.0
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    ref, rc = oracle_lib.topk_tokens(s, ids, ctx, k_tok, counts=counts)
+    tok, tc = lsa.lsa_topk_tokens(to_dev(s), to_dev(ids), to_dev(ctx), k_tok,
+                                  counts=None if counts is None else to_dev(counts), workspace=None)
+    assert np.array_equal(tc.cpu().numpy(), rc), kind
+    assert np.array_equal(tok.cpu().numpy(), ref), kind
