@@ -319,6 +319,7 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
 
     run(0, n_warm_int)
     torch.cuda.synchronize()
+    dec.fetch_events = []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     run(n_warm_int, n_time_int)
@@ -327,20 +328,34 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     n_steps = n_time_int * w.tau
-    fetched = None
-    if dec.delta:
-        last = n_warm_int + n_time_int - 1
-        fetched = round(float((dec.fetch_slots[last % 2] >= 0).float().mean()), 4)
+    # each timed interval's fetch, timed on the side stream while attention runs
+    fetch_ms = [a.elapsed_time(b) for i, a, b in dec.fetch_events]
+    dec.fetch_events = None
+    # the chunks each interval's selection adds to the previous one (outside
+    # the timed region): what a delta fetch moves over the host link
+    sels = []
+    for i in range(n_warm_int + n_time_int):
+        dec.reselect(qidx[i], i)
+        sels.append(dec.sel_ids[i % 2].cpu().numpy().copy())
+    new_frac = [sum(len(set(sels[i][b].tolist()) - set(sels[i - 1][b].tolist())) for b in range(w.B)) / (w.B * w.k)
+                for i in range(n_warm_int, n_warm_int + n_time_int)]
+    moved = [(f if dec.delta else 1.0) * fetch_bytes for f in new_frac]
+    link = [m / (t * 1e-3) / 1e9 for m, t in zip(moved, fetch_ms)] if len(fetch_ms) == len(moved) else []
+    fetched = round(statistics.mean(new_frac), 4) if dec.delta else 1.0
     res = {
-        "metric": "LSA host-tier decode steps/s, 1M ctx batch 4 (selected chunks fetched from pinned host memory)",
+        "metric": "LSA host-tier decode steps/s, 1M ctx batch 4 (selected chunks fetched from pinned host memory)"
+                  + (f", {round(100 * w.churn)}% new chunks per interval" if w.churn else ""),
         "value": round(1000.0 * n_steps / ms_total, 2), "unit": "steps/s", "n_gpus": 1, "steps": n_steps,
         "warmup": n_warm_int * w.tau, "ms_per_step": round(ms_total / n_steps, 5), "higher_is_better": True,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {w.B}, {w.C} chunks of {w.T}, top-{w.k} fetched every {w.tau} "
                                f"steps into a two-buffer HBM pool (lag 1), steady state after the warm-up",
                    "fetch": fetch, "fetch_grid": fetch_grid or 16, "n_split": dec.n_split or "library default",
-                   "delta_fetch": dec.delta, "fetched_fraction_last_interval": fetched,
-                   "fetch_bytes_per_reselect": fetch_bytes,
+                   "delta_fetch": dec.delta, "churn_target": w.churn or None,
+                   "fetched_fraction_per_interval": fetched,
+                   "fetch_bytes_per_reselect_full": fetch_bytes,
+                   "fetch_ms_under_overlap": round(statistics.mean(fetch_ms), 3) if fetch_ms else None,
+                   "link_GBs_under_overlap": round(statistics.mean(link), 1) if link else None,
                    "fetch_alone": fetch_alone,
                    "attention_us_per_step_alone": round(mean_att * 1e3, 2),
                    "attention_GBs_alone": round(attend_bytes_per_launch(w) / (mean_att * 1e-3) / 1e9, 1),
@@ -637,6 +652,8 @@ def main():
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
     ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
     ap.add_argument("--drift", action="store_true", help="host tier: a fresh indexer query every interval")
+    ap.add_argument("--churn", type=float, default=0.0,
+                    help="host tier: the ring indexer, whose selection moves by about this fraction per interval")
     ap.add_argument("--score-sweep", action="store_true",
                     help="batched indexer scoring: MFMA vs GEMV kernel over nq (one key set)")
     ap.add_argument("--score-nq", default="1,2,4,8,16,32,64,128,256,512",
@@ -666,6 +683,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.drift:
         w = w.replace(drift=True, n_golden=min(w.n_golden, w.C // max(1, (args.steps + args.warmup) // w.tau + 1)))
+    if args.churn:
+        if not w.host_tier:
+            print("--churn applies to the host tier (--workload 1m_host)", file=sys.stderr)
+            sys.exit(2)
+        w = w.replace(churn=args.churn)
     if args.token_topk:
         token_stage_bench(w, args.steps, args.warmup, args.token_topk, args.n_split, args.repeats)
         return
@@ -757,8 +779,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{w.name} context decode, {layer_txt}: batch {w.B}, {w.Hq} query / {w.Hkv} KV heads, "
-                         f"head dim {w.d}, {w.N} tokens = {w.C} chunks of {w.T}, top-{w.k} chunks "
-                         f"re-selected every {w.tau} steps, int8 indexer dim {w.d_idx}"),
+                         f"head dim {w.d}, {w.N} tokens = {w.C} chunks of {w.T}, "
+                         + (f"top-{w.k} chunks" if args.selection == "topk"
+                            else f"the chunks with sigmoid score > 0.5, at most {w.k},")
+                         + f" re-selected every {w.tau} steps, int8 indexer dim {w.d_idx}"),
             "global_batch": w.B,
             "seq_len": w.N,
             "retained_chunks": w.k,

@@ -162,6 +162,10 @@ class LsaDecoder:
             self.fetch_done = [torch.cuda.Event() for _ in range(2)]
             self.attn_done = torch.cuda.Event()
             self._attn_done_valid = False
+            # set to a list to record (interval, start, end) timing events
+            # around every fetch on the side stream (eager use only, not
+            # under graph capture)
+            self.fetch_events = None
 
     # ---- single operations -------------------------------------------------
     def reselect(self, q_idx: torch.Tensor, sel: int, stream=None) -> torch.Tensor:
@@ -249,6 +253,12 @@ class LsaDecoder:
         if self._attn_done_valid:
             # pool buffer i % 2 was last read by the previous interval
             self.side.wait_event(self.attn_done)
+        timing = self.fetch_events is not None
+        if timing and self.fetch == "pull":
+            self.side.wait_event(self.ev_sel)  # start the clock once the copy may begin
+        if timing:
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev0.record(self.side)
         if self.fetch == "memcpy":
             self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
             for host, pool in zip(self.host_layers or [self.host_kv], self.pools):
@@ -260,6 +270,10 @@ class LsaDecoder:
                 lsa_fetch_chunks_pull(host, self.sel_ids[i % 2], pool[i % 2],
                                       slots=self.fetch_slots[i % 2] if self.delta else None, grid=self.fetch_grid,
                                       stream=self.side)
+        if timing:
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev1.record(self.side)
+            self.fetch_events.append((i, ev0, ev1))
         self.fetch_done[i % 2].record(self.side)
 
     def join(self) -> None:

@@ -27,6 +27,8 @@ TAG_GOLD_NOISE = 4  # noise added to golden keys
 TAG_KV = 5          # K/V store
 TAG_Q = 6           # attention query, per step
 TAG_MISC = 7        # test-only streams
+TAG_RING = 8        # ring positions of the chunks (churn-controlled indexer), per request
+TAG_RING_PHASE = 9  # starting angle of the ring query, per request
 
 
 def stream(tag: int, sub: int = 0) -> int:

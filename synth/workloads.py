@@ -18,6 +18,16 @@ Recipe (seed 0 unless a test says otherwise):
     (sign(0) = 0), so they score high against that interval's query;
   * K/V store      kv[b][c][K|V][g][t][i] bf16 N(0,1), chunk-major;
   * query          q[t][b][h][i] bf16 N(0,1), fresh each step.
+Churn-controlled indexer (a workload with churn > 0, for the host tier):
+every chunk sits at an angle on a ring (theta_c = 2 pi perm(c) / C, perm a
+seeded permutation per request, so neighbouring angles are scattered chunk
+ids), its key is K[c][i] = round(15 cos(theta_c - pi i / d_idx)), and the
+interval-i query is q[i'] = round(15 cos(phi_i - pi i' / d_idx)) with
+phi_i = phi_0 + i * churn * 2 pi k / C.  A query then favours the chunks
+nearest its angle, an arc of about k chunks, and the arc moves by about
+`churn` of its length per interval (the exact fraction is whatever the
+selections give; the benchmark measures it).
+
 No value here is computed by the method; the generator is SplitMix64
 (see synth.c).
 """
@@ -28,8 +38,8 @@ import math
 
 import numpy as np
 
-from . import (TAG_GOLD_NOISE, TAG_GOLD_POS, TAG_KIDX, TAG_KV, TAG_Q, TAG_QIDX, choose,
-               normal_bf16, normal_bf16_into, normal_bf16_runs, stream, uniform_i8)
+from . import (TAG_GOLD_NOISE, TAG_GOLD_POS, TAG_KIDX, TAG_KV, TAG_Q, TAG_QIDX, TAG_RING, TAG_RING_PHASE, choose,
+               normal_bf16, normal_bf16_into, normal_bf16_runs, raw_u64, stream, uniform_i8)
 
 CHUNK_TOKENS = 64  # tokens per KV chunk (T)
 TAU = 64           # decode steps between re-selections
@@ -53,6 +63,7 @@ class Workload:
     nq: int = 1
     T: int = CHUNK_TOKENS
     tau: int = TAU
+    churn: float = 0.0   # > 0: the ring indexer, moving by about this fraction of k per interval
 
     @property
     def C(self) -> int:
@@ -111,11 +122,41 @@ WORKLOAD_ORDER = ["tiny", "32k", "128k", "500k", "1m_host"]
 
 def query_interval(w: Workload, interval: int) -> int:
     """Which generated indexer query serves re-selection `interval`."""
-    return interval if w.drift else 0
+    return interval if (w.drift or w.churn) else 0
+
+
+def _ring_offsets(w: Workload) -> np.ndarray:
+    """Angular offsets pi i / d_idx of the indexer dimensions."""
+    return np.pi * np.arange(w.d_idx) / w.d_idx
+
+
+def _ring_int8(angles: np.ndarray, w: Workload) -> np.ndarray:
+    """round(15 cos(angle - offset_i)) for every angle and dimension i."""
+    v = np.rint(15.0 * np.cos(angles[..., None] - _ring_offsets(w)))
+    return v.astype(np.int8)
+
+
+def ring_angles(w: Workload) -> np.ndarray:
+    """float64 [B][C]: the ring angle of every chunk (a seeded permutation of
+    C equally spaced angles per request)."""
+    out = np.empty((w.B, w.C), dtype=np.float64)
+    for b in range(w.B):
+        perm = choose(w.C, w.C, w.seed, stream(TAG_RING, b))
+        out[b] = 2.0 * np.pi * perm / w.C
+    return out
+
+
+def ring_query_angle(w: Workload, interval: int) -> np.ndarray:
+    """float64 [B]: the interval's query angle on the ring."""
+    phase = raw_u64(w.B, w.seed, stream(TAG_RING_PHASE)).astype(np.float64) / 2.0 ** 64 * 2.0 * np.pi
+    return phase + interval * w.churn * 2.0 * np.pi * w.k / w.C
 
 
 def indexer_query(w: Workload, interval: int) -> np.ndarray:
     """int8 [B][nq][d_idx]."""
+    if w.churn:
+        assert w.nq == 1
+        return _ring_int8(ring_query_angle(w, interval), w)[:, None, :]
     return uniform_i8((w.B, w.nq, w.d_idx), w.seed, stream(TAG_QIDX, query_interval(w, interval)), -16, 15)
 
 
@@ -139,7 +180,10 @@ def golden_sets(w: Workload) -> list[np.ndarray]:
 
 def indexer_keys(w: Workload) -> np.ndarray:
     """int8 [B][C][d_idx]: background uniform keys with golden chunks planted
-    against every generated query (frozen for the whole run)."""
+    against every generated query (frozen for the whole run); for a workload
+    with churn, the ring keys."""
+    if w.churn:
+        return _ring_int8(ring_angles(w), w)
     K = uniform_i8((w.B, w.C, w.d_idx), w.seed, stream(TAG_KIDX), -16, 15)
     noise = uniform_i8((w.B, w.C, w.d_idx), w.seed, stream(TAG_GOLD_NOISE), -4, 4)
     sets = golden_sets(w)

@@ -50,7 +50,7 @@ def oracle_output(oracle, W, w, t, b, ids_b):
 @pytest.mark.parametrize("name,fetch,delta", [("tiny", None, None), ("32k", None, None), ("128k", None, None),
                                               ("500k", None, None), ("1m_host", "pull", True),
                                               ("1m_host", "pull", False), ("1m_host", "memcpy", False),
-                                              ("128k_host", "pull", True)])
+                                              ("128k_host", "pull", True), ("32k_churn", "pull", True)])
 def test_decode_workload(oracle_lib, name, fetch, delta):
     import torch
 
@@ -60,6 +60,9 @@ def test_decode_workload(oracle_lib, name, fetch, delta):
     if name == "128k_host":  # the drifting 128K workload on the host tier: selections change every interval
         w = W.WORKLOADS["128k"].replace(host_tier=True)
         steps, reqs = [0, 63, 64, 128, 191, 192, 255], [0, 9]
+    elif name == "32k_churn":  # the ring indexer: a quarter of the chunks are new every interval
+        w = W.WORKLOADS["32k"].replace(host_tier=True, churn=0.25)
+        steps, reqs = [0, 64, 128, 192, 255], [0, 1, 2, 3]
     else:
         w = W.WORKLOADS[name]
         steps, reqs = SAMPLED[name]

@@ -171,3 +171,23 @@ def test_choose_is_uniform(synth_mod):
         hits[synth_mod.choose(count, n, 6, synth_mod.stream(synth_mod.TAG_MISC, 10_000 + t))] += 1
     p = count / n
     assert (np.abs(hits - trials * p) <= 5 * math.sqrt(trials * p * (1 - p))).all()
+
+
+@pytest.mark.parametrize("churn", [0.1, 0.25, 0.5])
+def test_ring_indexer_moves_the_selection_by_the_churn(churn):
+    """The churn-controlled indexer: keys and queries are int8 in [-15, 15],
+    every chunk has its own ring angle, and the oracle's top-k selection of
+    consecutive intervals differs by about `churn` of k (the arc the query
+    favours moves by that fraction of its length per interval)."""
+    import oracle
+    from synth import workloads as W
+    w = W.WORKLOADS["32k"].replace(churn=churn, host_tier=True, k=51)
+    ang = W.ring_angles(w)
+    for b in range(w.B):
+        assert len(np.unique(np.round(ang[b] * w.C / (2 * np.pi)).astype(int))) == w.C
+    K = W.indexer_keys(w)
+    assert K.dtype == np.int8 and K.min() >= -15 and K.max() <= 15
+    sels = [oracle.select(W.indexer_query(w, i), K, w.k, w.alpha)[2] for i in range(5)]
+    for i in range(1, 5):
+        new = np.mean([len(set(sels[i][b].tolist()) - set(sels[i - 1][b].tolist())) / w.k for b in range(w.B)])
+        assert abs(new - churn) <= 0.03, (i, new)
