@@ -175,6 +175,72 @@ __device__ inline int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8 lanes, then across rows by
+// adding lane 15 of row 0 to row 1 and lane 47 to row 3, then lane 31 to
+// rows 2 and 3 (DPP row_shr and row_bcast; a lane with no source adds 0).
+__device__ inline int wave_incl_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// OR over the 64 lanes of a wave, the same in every lane (DPP, as above).
+__device__ inline uint32_t wave_or(uint32_t v) {
+    int x = (int)v;
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
+// Sum of per-wave totals tot[0..wave), the same in every lane.
+__device__ inline int sum_below(const int* tot, int wave, int lane) {
+    const int x = lane < wave ? tot[lane & (kThreads / 64 - 1)] : 0;
+    return __builtin_amdgcn_readlane(wave_incl_sum(x), 63);
+}
+
+// The rank-th largest (1-based) of the values v0 and v1 held by the lanes of
+// one wave (128 values), as wave_rank_value below.
+__device__ inline uint32_t wave_rank_value2(uint32_t v0, uint32_t v1, int bits, int rank) {
+    uint64_t c0 = ~0ull, c1 = ~0ull;
+    uint32_t r = 0;
+    for (int b = bits - 1; b >= 0; --b) {
+        const uint64_t o0 = c0 & __ballot((v0 >> b) & 1u), o1 = c1 & __ballot((v1 >> b) & 1u);
+        const int n1 = __popcll(o0) + __popcll(o1);
+        const bool set = rank <= n1;
+        c0 = set ? o0 : c0 & ~o0;
+        c1 = set ? o1 : c1 & ~o1;
+        rank = set ? rank : rank - n1;
+        r |= set ? 1u << b : 0u;
+    }
+    return r;
+}
+
+// The rank-th largest (1-based) of the values v held by the lanes of one
+// wave, all below 2^bits, decided bit by bit from the top: the bit is 1 iff
+// at least `rank` of the values still agreeing with the decided bits have it.
+__device__ inline uint32_t wave_rank_value(uint32_t v, int bits, int rank) {
+    uint64_t cand = ~0ull;
+    uint32_t r = 0;
+    for (int b = bits - 1; b >= 0; --b) {
+        const uint64_t one = cand & __ballot((v >> b) & 1u);
+        const int c1 = __popcll(one);
+        const bool set = rank <= c1;
+        cand = set ? one : cand & ~one;
+        rank = set ? rank : rank - c1;
+        r |= set ? 1u << b : 0u;
+    }
+    return r;
+}
+
 // One wave finishes a select on the cnt <= 64*NS keys of lst (all agreeing
 // above bit hi): bit by bit from bit hi-1 down, the bit of the need-th
 // largest key is 1 iff at least `need` of the remaining candidates have it
@@ -217,176 +283,223 @@ __device__ inline void ballot_finish(const uint32_t* lst, int cnt, int hi, int n
     }
 }
 
-// Token mode's candidate path: 16 keys per wave (256 in all) are a sample of
-// the row; the 12-bit key prefix of the sample key of rank sample_rank bounds
-// a candidate set (every key at or above that prefix) that holds the kept
-// keys whenever it has at least k members; it is then selected from in LDS.
-constexpr int kSamplePerWave = 16;
+// Token mode's fast select: wave 0 draws kSamples keys spread over the row
+// (two per lane) while the other waves form their keys; the 12-bit key prefix of the sample
+// key of rank sample_rank bounds a candidate set (every key at or above that
+// prefix) that holds the kept keys whenever it has at least k members; it is
+// then selected from in LDS.
+constexpr int kSamples = 128;
 constexpr int kSampleBits = 12;        // key prefix the sample decides
-constexpr int kCandCap = 8192;         // candidates held in LDS (keys and positions)
-constexpr int kCandCopies = 16;        // histogram copies of the candidate passes
+constexpr int kRegion = 832;           // (key, position) pairs each wave holds in LDS
+constexpr int kCandWord0 = 4352;       // first word of the waves' regions in sm_raw
+constexpr int kTokBinBits = 12;        // digit width of the candidates' histogram
+constexpr int kTokBins = 1 << kTokBinBits;
+constexpr int kSmallCap = 64;          // a bin this small is ranked by one wave
 
-// Exclusive block-wide sums of two per-thread counts (2 barriers).
-__device__ inline void block_excl_scan2(int& a, int& b, int* sm_a, int* sm_b, int lane, int wave) {
-    int ia = a, ib = b;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int ua = __shfl_up(ia, off), ub = __shfl_up(ib, off);
-        if (lane >= off) {
-            ia += ua;
-            ib += ub;
-        }
-    }
-    if (lane == 63) {
-        sm_a[wave] = ia;
-        sm_b[wave] = ib;
-    }
-    __syncthreads();
-    int pa = 0, pb = 0;
-    for (int w = 0; w < wave; ++w) {
-        pa += sm_a[w];
-        pb += sm_b[w];
-    }
-    __syncthreads();
-    a = pa + ia - a;
-    b = pb + ib - b;
-}
+// LDS word of histogram bin b: the low 5 bits are XORed with the next 5, a
+// bijection on [0, 4096) that spreads bins at power-of-two strides (scores
+// with few mantissa bits fill every 8th or 16th bin) over the LDS banks.
+__device__ inline int hist_word(uint32_t b) { return (int)(b ^ ((b >> 5) & 31u)); }
+// Word 3 of a buffer resource on this GPU family: 32-bit raw data, no swizzle.
+constexpr int kBufferWord3 = 0x00020000;
+
 
 // Token mode, register-resident row of KPT keys per thread, kk < competing
-// keys.  The sample's prefix of rank `rank` (one wave, bit by bit) gives the
-// bound pv; if between kk and kCandCap keys reach it, they are copied to LDS
-// in position order with their positions, the kk-th largest is found among
-// them alone (8-bit digit passes, then one wave bit by bit), and the kept
-// positions are written in ascending order.  Returns false, having written
-// nothing, when the count misses (then the full select runs); the decision
-// is uniform over the workgroup.  The row's counts and -1 padding are the
-// caller's.  Uses sm_raw: [0, 4096) histogram, [4096, 4352) small bucket,
-// [16384, 16384 + kCandCap) keys, then positions.
+// keys.  The per-step cost of this one-workgroup select is set by the issue
+// rate of its one compute unit (16 waves share 4 SIMDs, one scalar unit and
+// the LDS), so every step below is a few instructions per wave between
+// barriers:
+//  1. The bound pv (taken by the caller from a 64-key sample) splits off
+//     the candidates, every key >= pv: each wave copies its own to its LDS
+//     region as (key, position) pairs, in position order.  If fewer than kk
+//     keys reach pv in all, or some wave has more than its region holds,
+//     false is returned (uniformly) and the full select runs instead.
+//  2. A 4096-bin histogram of the candidates' top 12 bits above pv
+//     (key - pv >> sh, sh = bits of kmax - pv beyond 12) and a block-wide
+//     suffix scan find the bin of the kk-th largest candidate.  A bin that
+//     holds a single value (width 1, or every candidate's bits below the bin
+//     width equal to pv's) decides v* outright; a bin of at most 64 keys is
+//     gathered and finished by one wave, bit by bit; a larger bin is
+//     histogrammed again on its next 12 bits.
+//  3. Ordered compaction: candidates > v*, and the first `keep` candidates
+//     equal to v* in position order.  Waves cover the row in position order,
+//     so one exclusive scan of per-wave counts places all outputs in
+//     ascending position order.
+// The row's counts and -1 padding are the caller's.  The histogram's 4096
+// words at the start of sm_raw must be zero on entry.  Uses sm_raw: [0,
+// 4096) histogram (bin b at word hist_word(b)), [4096, 4160) small bucket,
+// from kCandWord0 the waves' regions of kRegion pairs.
 template <int KPT>
-__device__ __forceinline__ bool tokens_candidate_select(const uint32_t (&key)[KPT], int kk, uint32_t kmax, int rank, int wbase,
-                                        int tid, int lane, int wave, const uint32_t* sm_sample, uint32_t* sm_raw,
-                                        int* sm_i, int* sm_j, int* sm_tot, int* sm_pick, int32_t* dst) {
-    int* const hist = reinterpret_cast<int*>(sm_raw);           // [256][kCandCopies]
-    uint32_t* const small = sm_raw + kBins * kCandCopies;       // <= kBallotMax keys
-    uint32_t* const ckey = sm_raw + kBins * kLaneCopies;        // [kCandCap]
-    uint32_t* const cpos = ckey + kCandCap;                     // [kCandCap]
-    static_assert(kBins * kCandCopies + kBallotMax <= kBins * kLaneCopies, "histogram and bucket fit below the lists");
-    static_assert(kBins * kLaneCopies + 2 * kCandCap <= kBins * kLaneCopies + 2 * kListCap, "candidates fit the lists");
+__device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], int kk, uint32_t kmax, uint32_t pv,
+                                                   int wbase, int tid, int lane, int wave, uint32_t* sm_raw,
+                                                   int* sm_i, int* sm_j, int* sm_cnt, int* sm_pick, int32_t* dst) {
+    int* const hist = reinterpret_cast<int*>(sm_raw);   // [kTokBins]
+    uint32_t* const small = sm_raw + kTokBins;           // [kSmallCap]
+    uint2* const reg = reinterpret_cast<uint2*>(sm_raw + kCandWord0) + wave * kRegion;  // this wave's pairs
+    static_assert(kTokBins + kSmallCap <= kCandWord0 && kCandWord0 % 4 == 0, "histogram and bucket below the pairs");
+    static_assert(kCandWord0 + 2 * kWaves * kRegion <= kBins * kLaneCopies + 2 * kListCap, "regions fit sm_raw");
+    static_assert(kThreads * 4 == kTokBins && kRegion % 64 == 0, "scan layout: 4 bins per thread; whole runs");
 
-    // --- the bound: the 12-bit prefix of the sample key of rank `rank` ---
-    if (wave == 0) ballot_finish<kBallotSlots>(sm_sample, kWaves * kSamplePerWave, kSampleBits, rank, lane, sm_pick);
-    __syncthreads();
-    uint32_t pv = (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]) << (32 - kSampleBits);
-    pv = pv ? pv : 1u;  // key 0 does not compete
-    int n_w = 0;
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) n_w += __popcll(__ballot(key[e] >= pv));
-    if (lane == 0) sm_i[wave] = n_w;
-    __syncthreads();
-    int c = 0, before = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const int x = sm_i[w];
-        c += x;
-        before += w < wave ? x : 0;
-    }
-    c = __builtin_amdgcn_readfirstlane(c);
-    if (c < kk || c > kCandCap) return false;  // uniform
-
-    // --- the candidates, in position order ---
-    before = __builtin_amdgcn_readfirstlane(before);
+    // --- 1. the candidates ---
+    uint32_t n = 0;  // this wave's candidates so far
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const bool in = key[e] >= pv;
         const uint64_t m = __ballot(in);
-        if (in) {
-            const int at = before + lanes_below(m);
-            ckey[at] = key[e];
-            cpos[at] = (uint32_t)(wbase + 64 * e + lane);
-        }
-        before += __popcll(m);
+        // past the region (then the full select runs) every write lands on its last pair
+        const uint32_t at = min(__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, n)),
+                                (uint32_t)kRegion - 1u);
+        if (in) reg[at] = make_uint2(key[e], (uint32_t)(wbase + 64 * e + lane));
+        n += (uint32_t)__popcll(m);
     }
+    if (lane == 0) sm_i[wave] = (int)n;
+    if (tid == 0) sm_cnt[1] = 0;  // small bucket fill, used after later barriers
     __syncthreads();
+    const int cw = lane < kWaves ? sm_i[lane & (kWaves - 1)] : 0;
+    const int c = __builtin_amdgcn_readlane(wave_incl_sum(cw), 63);
+    if (c < kk || __ballot(cw > kRegion) != 0) return false;  // uniform
+    const int nw = (int)n, nruns = (nw + 63) / 64;  // this wave's pairs and runs of 64 (uniform)
 
-    // --- the kk-th largest candidate: digits of key - pv from the top ---
-    const uint32_t range = kmax - pv;
+    const uint32_t range = kmax - pv;  // kmax >= pv: some key reaches pv
     int hi = range == 0u ? 0 : 32 - __builtin_clz(range);
-    uint32_t rstar = 0;
-    int need = kk, cnt = c;
-    auto ub_of = [&](int h) {
-        const uint32_t span = h >= 32 ? 0xFFFFFFFFu : (1u << h) - 1u;
-        return min(span, range - rstar);
-    };
-    while (hi > 0) {
-        const uint32_t base = pv + rstar;
-        if (cnt <= kBallotMax) {
-            // the bucket's keys (relative to base) into a small list; one
-            // wave then decides the remaining bits
-            const uint32_t ub = ub_of(hi);
-            if (tid == 0) sm_tot[0] = 0;
-            __syncthreads();
-            for (int i0 = 0; i0 < c; i0 += kThreads) {
-                const int i = i0 + tid;
-                const uint32_t d = i < c ? ckey[i] - base : 0xFFFFFFFFu;
-                const bool in = i < c && d <= ub;
+    int sh = hi > kTokBinBits ? hi - kTokBinBits : 0;
+    // the histogram, and the OR of every candidate's bits below the bin
+    // width: 0 when each bin holds a single value (as for scores rounded to
+    // few mantissa bits)
+    // (plain loops over the wave's runs: every instruction a wave issues here
+    // costs the compute unit about 16 cycles, as all 16 waves issue it)
+    uint32_t below = 0;
+    {
+        const uint32_t low = (1u << sh) - 1u;
+#pragma unroll 1
+        for (int i = lane; i < nw; i += 64) {
+            const uint32_t x = reg[i].x - pv;
+            atomicAdd(&hist[hist_word(x >> sh)], 1);
+            below |= x & low;
+        }
+    }
+    below = wave_or(below);
+    if (lane == 0) sm_cnt[2 + wave] = (int)below;
+    __syncthreads();
+    below = wave_or(lane < kWaves ? (uint32_t)sm_cnt[2 + (lane & (kWaves - 1))] : 0u);
+
+    // --- 2. v* and how many keys equal to it are kept ---
+    uint32_t base = pv, vstar;
+    int need = kk, keep;
+    for (;;) {
+        // thread t holds bins 4095 - 4t down to 4092 - 4t: a prefix sum over
+        // threads is a suffix sum over bins
+        const int b0 = kTokBins - 1 - 4 * tid;
+        const int h3 = hist[hist_word(b0)], h2 = hist[hist_word(b0 - 1)], h1 = hist[hist_word(b0 - 2)],
+                  h0 = hist[hist_word(b0 - 3)];
+        const int sum = (h0 + h1) + (h2 + h3);
+        const int incl = wave_incl_sum(sum);
+        if (lane == 63) sm_j[wave] = incl;
+        __syncthreads();
+        const int excl = incl - sum + sum_below(sm_j, wave, lane);
+        if (excl < need && need <= excl + sum) {  // exactly one thread
+            int b = b0 - 3, nd = need - excl - h3 - h2 - h1, cb = h0;
+            if (excl + h3 >= need) {
+                b = b0; nd = need - excl; cb = h3;
+            } else if (excl + h3 + h2 >= need) {
+                b = b0 - 1; nd = need - excl - h3; cb = h2;
+            } else if (excl + h3 + h2 + h1 >= need) {
+                b = b0 - 2; nd = need - excl - h3 - h2; cb = h1;
+            }
+            sm_pick[0] = b;
+            sm_pick[1] = nd;
+            sm_pick[2] = cb;
+        }
+        __syncthreads();
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
+        need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
+        const int cb = __builtin_amdgcn_readfirstlane(sm_pick[2]);
+        if (sh == 0 || below == 0u) {  // the bin holds one value: base + (b << sh)
+            vstar = base + (b << sh);
+            keep = need;
+            break;
+        }
+        const uint32_t lo = base + (b << sh);  // the bin holds keys in [lo, lo + 2^sh)
+        if (cb <= kSmallCap) {
+            // gather the bin's keys (as offsets from lo), then one wave
+            // decides their need-th largest bit by bit
+#pragma unroll 1
+            for (int r = 0; r < nruns; ++r) {
+                const int i = 64 * r + lane;
+                const uint32_t x = reg[i].x - lo;
+                const bool in = i < nw && (x >> sh) == 0u;
                 const uint64_t m = __ballot(in);
-                int at = 0;
-                if (lane == 0 && m) at = atomicAdd(&sm_tot[0], __popcll(m));
-                at = __builtin_amdgcn_readfirstlane(at);
-                if (in) small[at + lanes_below(m)] = d;
+                if (m) {  // uniform
+                    int at = 0;
+                    if (lane == 0) at = atomicAdd(&sm_cnt[1], __popcll(m));
+                    at = __builtin_amdgcn_readfirstlane(at);
+                    if (in) small[at + lanes_below(m)] = x;
+                }
             }
             __syncthreads();
             if (wave == 0) {
-                if (cnt <= 64)
-                    ballot_finish<1>(small, cnt, hi, need, lane, sm_pick);
-                else
-                    ballot_finish<kBallotSlots>(small, cnt, hi, need, lane, sm_pick);
+                // lanes past the bin hold 0, below every offset that can be picked
+                const uint32_t di = lane < cb ? small[lane] : 0u;
+                const uint32_t dv = wave_rank_value(di, sh, need);
+                const int n_gt = __popcll(__ballot(lane < cb && di > dv));
+                if (lane == 0) {
+                    sm_pick[0] = (int)(lo + dv);
+                    sm_pick[1] = need - n_gt;
+                }
             }
             __syncthreads();
-            rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
-            need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
-            cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
+            vstar = (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]);
+            keep = __builtin_amdgcn_readfirstlane(sm_pick[1]);
             break;
         }
-        const int w = hi < kDigitBits ? hi : kDigitBits;
-        const int sh = hi - w;
-        const uint32_t ub = ub_of(hi);
-        for (int j = tid; j < kBins * kCandCopies / 4; j += kThreads)
-            reinterpret_cast<int4*>(hist)[j] = make_int4(0, 0, 0, 0);
-        __syncthreads();
-        for (int i = tid; i < c; i += kThreads) {
-            const uint32_t d = ckey[i] - base;
-            if (d <= ub) atomicAdd(&hist[(int)(d >> sh) * kCandCopies + (lane & (kCandCopies - 1))], 1);
-        }
-        __syncthreads();
-        pick_digit<kCandCopies>(hist, sm_tot, sm_pick, tid, lane, wave, need);
-        rstar |= (uint32_t)__builtin_amdgcn_readfirstlane(sm_pick[0]) << sh;
-        need = __builtin_amdgcn_readfirstlane(sm_pick[1]);
-        cnt = __builtin_amdgcn_readfirstlane(sm_pick[2]);
+        // a crowded bin: histogram its keys on their next bits
+        base = lo;
         hi = sh;
+        sh = hi > kTokBinBits ? hi - kTokBinBits : 0;
+        reinterpret_cast<int4*>(hist)[tid] = make_int4(0, 0, 0, 0);
+        __syncthreads();
+        below = 0u;
+        for (int i = lane; i < nw; i += 64) {
+            const uint32_t x = reg[i].x - base;
+            if ((x >> hi) == 0u) {
+                atomicAdd(&hist[hist_word(x >> sh)], 1);
+                below |= x & ((1u << sh) - 1u);
+            }
+        }
+        below = wave_or(below);
+        if (lane == 0) sm_cnt[2 + wave] = (int)below;
+        __syncthreads();
+        below = wave_or(lane < kWaves ? (uint32_t)sm_cnt[2 + (lane & (kWaves - 1))] : 0u);
     }
-    const uint32_t vstar = pv + rstar;
-    const bool all_eq = need == cnt;  // every key equal to v* is kept
 
-    // --- the kept positions, ascending: candidates > v*, and the first `need`
-    // equal to v* in position order; each thread a contiguous run ---
-    const int per = (c + kThreads - 1) / kThreads;
-    const int i0 = min(tid * per, c), i1 = min(i0 + per, c);
+    // --- 3. ordered compaction, each wave over its own region ---
     int n_gt = 0, n_eq = 0;
-    for (int i = i0; i < i1; ++i) {
-        n_gt += ckey[i] > vstar;
-        n_eq += ckey[i] == vstar;
+#pragma unroll 1
+    for (int r = 0; r < nruns; ++r) {  // uniform trip count: the ballots see every lane
+        const int i = 64 * r + lane;
+        const uint32_t k = i < nw ? reg[i].x : 0u;  // key 0 < pv <= v*: neither
+        n_gt += __popcll(__ballot(k > vstar));
+        n_eq += __popcll(__ballot(k == vstar));
     }
-    int gt_before = n_gt, eq_before = n_eq;
-    block_excl_scan2(gt_before, eq_before, sm_i, sm_j, lane, wave);
-    int out = gt_before + (all_eq ? eq_before : min(eq_before, need));
+    if (lane == 0) {
+        sm_i[wave] = n_gt;
+        sm_j[wave] = n_eq;
+    }
+    __syncthreads();
+    const int gt_before = sum_below(sm_i, wave, lane), eq_before = sum_below(sm_j, wave, lane);
+    int out = gt_before + min(eq_before, keep);
     int eq_seen = eq_before;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t v = ckey[i];
-        const bool eq = v == vstar;
-        const bool take = v > vstar || (eq && (all_eq || eq_seen < need));
-        eq_seen += eq;
-        if (take && out < kk) dst[out++] = (int32_t)cpos[i];
+#pragma unroll 1
+    for (int r = 0; r < nruns; ++r) {
+        const int i = 64 * r + lane;
+        const uint2 p = i < nw ? reg[i] : make_uint2(0u, 0u);
+        const bool eq = p.x == vstar;
+        const uint64_t em = __ballot(eq);
+        const bool take = p.x > vstar || (eq && eq_seen + lanes_below(em) < keep);
+        const uint64_t tm = __ballot(take);
+        if (take) dst[out + lanes_below(tm)] = (int32_t)p.y;
+        out += __popcll(tm);
+        eq_seen += __popcll(em);
     }
     return true;
 }
@@ -407,8 +520,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     uint32_t* const sm_lists = sm_raw + kBins * kLaneCopies;  // list s: sm_lists + s * kListCap
     __shared__ int sm_tot[kBins];
     __shared__ int sm_pick[3];  // digit chosen by a pass, keys still needed, keys in the digit
-    __shared__ int sm_cnt[2];
-    __shared__ uint32_t sm_sample[MODE == kModeTokens ? kWaves * kSamplePerWave : 1];  // key prefixes
+    __shared__ int sm_cnt[2 + kWaves];  // list fills; token rows: small-bin fill, per-wave ORs
+    __shared__ uint32_t sm_pv;  // token rows: the fast select's bound
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int k = a.k;
@@ -430,6 +543,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     // before any is used; keys are formed without branches (a load whose
     // only use sits under a branch moves into it and waits there).
     uint32_t key[KPT];
+    int lim_l = 0;        // list rows: usable tokens of the wave's entry `lane` (lane < KPT)
     if constexpr (MODE == kModeTokens || MODE == kModeSlice) {
         // slot e of wave w is exactly list entry j = off/64 + w*KPT + e (64 tokens)
         const float* srow = a.scores + (int64_t)row * row_len;
@@ -448,22 +562,56 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         const int jend = C > 0 ? min(kb, j0 + C / kChunkTokens) : 0;
         // lane e < KPT loads the id of the wave's slot e (KPT <= 64)
         const int jl = j0 + wave * KPT + lane;
+        // Buffer loads with the row as the buffer: a position past the row's
+        // end reads 0 (it lies in no entry in use, so it never competes), and
+        // slot e's offset is an immediate: no address arithmetic per slot.
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, row_len * 4, kBufferWord3);
+        // The fast select's sample, drawn by wave 0 ahead of its own keys so
+        // that its rank is found while the row's loads are in flight: lane
+        // l takes token (29 l + 7) mod 64 of list entry l * n_list / 64, as a
+        // 12-bit key prefix (0 where the token is not usable).
+        const bool sampler = MODE == kModeTokens && wave == 0 && a.sample_rank > 0;  // uniform
+        // sample s = lane and lane + 64: token (29 s + 7) mod 64 of list entry s * n_list / 128
+        const int js0 = (int)(((int64_t)lane * a.n_list) / kSamples);
+        const int js1 = (int)(((int64_t)(lane + 64) * a.n_list) / kSamples);
+        const int ts0 = (29 * lane + 7) & (kChunkTokens - 1), ts1 = (29 * (lane + 64) + 7) & (kChunkTokens - 1);
+        uint32_t cs0 = 0, cs1 = 0;
+        float vs0 = 0.0f, vs1 = 0.0f;
+        if (sampler) {
+            cs0 = (uint32_t)ids[js0];
+            cs1 = (uint32_t)ids[js1];
+            vs0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (64 * js0 + ts0) * 4, 0, 0));
+            vs1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (64 * js1 + ts1) * 4, 0, 0));
+        }
         const int32_t cidv = ids[jl < a.n_list ? jl : a.n_list - 1];
+        const int vo = (off + wbase + lane) * 4;  // byte offset of slot 0
         float sc[KPT];
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int idx = wbase + 64 * e + lane;  // position off + idx of the row
-            sc[e] = srow[idx < C ? off + idx : row_len - 1];  // clamped into the row (never used then)
+        for (int e = 0; e < KPT; ++e)
+            sc[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * e, 0, 0));
+        if (sampler) {
+            auto prefix = [&](int js, int ts, uint32_t cs, float vs) {  // 0 where the token is not usable
+                const int lims = js < jend ? (cs < ctx_chunk ? kChunkTokens : cs == ctx_chunk ? ctx_rem : 0) : 0;
+                return ts < lims ? score_key(vs) >> (32 - kSampleBits) : 0u;
+            };
+            const uint32_t p = wave_rank_value2(prefix(js0, ts0, cs0, vs0), prefix(js1, ts1, cs1, vs1), kSampleBits,
+                                                a.sample_rank);
+            if (lane == 0) sm_pv = p << (32 - kSampleBits);
         }
+        // tokens of entry j below the context length: 64 below chunk ctx/64,
+        // ctx%64 in it, none above it or in an entry not in use
+        const uint32_t cidl = (uint32_t)cidv;
+        lim_l = lane < KPT && jl < jend ? (cidl < ctx_chunk ? kChunkTokens : cidl == ctx_chunk ? ctx_rem : 0) : 0;
+        if (__ballot(lane < KPT && lim_l != kChunkTokens) == 0) {  // uniform: every slot of the wave usable
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            // tokens of entry j below the context length, 0 for an entry not
-            // in use (scalar arithmetic: the entry and its chunk id are uniform)
-            const int j = j0 + wave * KPT + e;
-            const uint32_t cid = (uint32_t)__builtin_amdgcn_readlane(cidv, e);
-            const int lim = j >= jend ? 0 : cid < ctx_chunk ? kChunkTokens : cid == ctx_chunk ? ctx_rem : 0;
-            const uint32_t kv = score_key(sc[e]);
-            key[e] = lane < lim ? kv : 0u;
+            for (int e = 0; e < KPT; ++e) key[e] = score_key(sc[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int lim = __builtin_amdgcn_readlane(lim_l, e);
+                key[e] = lane < lim ? score_key(sc[e]) : 0u;
+            }
         }
     } else if constexpr (MODE == kModeCand) {
         const uint32_t* krow = a.cand_key + (int64_t)row * C;
@@ -497,11 +645,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     // competing) wraps to the top and drops out; 1 is added back below.
     const bool capped = kScoreKeys || a.counts != nullptr;
     const uint32_t tkey = kScoreKeys ? 0u : ((uint32_t)a.thr ^ 0x80000000u);
+    // List rows: the competing keys are exactly the usable positions (no
+    // score is NaN, so no usable position has key 0), counted from lim_l.
+    // Token rows take the minimum only if the full select runs (below).
+    constexpr bool kListRows = MODE == kModeTokens || MODE == kModeSlice;
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
     int avail = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        if constexpr (kScoreKeys) {
+        if constexpr (kListRows) {
+            if constexpr (MODE == kModeSlice) lmin = min(lmin, key[e] - 1u);
+            lmax = max(lmax, key[e]);
+        } else if constexpr (kScoreKeys) {
             lmin = min(lmin, key[e] - 1u);
             lmax = max(lmax, key[e]);
             avail += __popcll(__ballot(key[e] != 0u));
@@ -512,31 +667,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             if (capped) avail += __popcll(__ballot(o && key[e] > tkey));
         }
     }
-    lmin = wave_min(lmin);
+    if constexpr (kListRows) {
+#pragma unroll
+        for (int off2 = 32; off2 > 0; off2 >>= 1) lim_l += __shfl_xor(lim_l, off2);
+        avail = lim_l;
+    }
+    if constexpr (MODE != kModeTokens) lmin = wave_min(lmin);
     lmax = wave_max(lmax);
     if (lane == 0) {
-        sm_min[wave] = lmin;
+        if constexpr (MODE != kModeTokens) sm_min[wave] = lmin;
         sm_max[wave] = lmax;
         sm_avail[wave] = avail;
     }
     if (tid == 0) sm_cnt[0] = 0;
     if constexpr (MODE == kModeTokens) {
-        // the sample: lane l < 16 of each wave gives its slot l % KPT, a
-        // position in list entry l % KPT of the wave's range (key 0: not
-        // competing, the smallest)
-        if (lane < kSamplePerWave) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) v = (e == lane % KPT) ? key[e] : v;
-            sm_sample[wave * kSamplePerWave + lane] = v >> (32 - kSampleBits);
-        }
+        // the fast select's histogram starts at zero
+        if (a.sample_rank > 0) reinterpret_cast<int4*>(sm_raw)[tid] = make_int4(0, 0, 0, 0);
     }
     __syncthreads();
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     avail = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        kmin = min(kmin, sm_min[w]);
+        if constexpr (MODE != kModeTokens) kmin = min(kmin, sm_min[w]);
         kmax = max(kmax, sm_max[w]);
         avail += sm_avail[w];
     }
@@ -562,9 +715,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
     if constexpr (MODE == kModeTokens) {
         if (a.sample_rank > 0 && kk < n_ok &&
-            tokens_candidate_select<KPT>(key, kk, kmax, a.sample_rank, wbase, tid, lane, wave, sm_sample, sm_raw,
-                                         sm_i, sm_j, sm_tot, sm_pick, dst))
+            tokens_fast_select<KPT>(key, kk, kmax, sm_pv ? sm_pv : 1u, wbase, tid, lane, wave, sm_raw, sm_i, sm_j,
+                                    sm_cnt, sm_pick, dst))
             return;
+        // the full select below works on key - (the smallest competing key)
+        uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) m = min(m, key[e] - 1u);
+        m = wave_min(m);
+        if (lane == 0) sm_min[wave] = m;
+        __syncthreads();
+        kmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) kmin = min(kmin, sm_min[w]);
+        kmin = __builtin_amdgcn_readfirstlane(kmin) + 1u;
     }
 
     // --- radix select ---
@@ -1030,14 +1194,14 @@ hipError_t launch_mode(const TopkArgs& a, int grid, int positions, hipStream_t s
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Rank, among the 256 sample keys, whose 12-bit prefix bounds the token
-// candidates: the expected rank of the k_tok-th largest key (256 k/n), plus
+// Rank, among the 128 sample keys, whose 12-bit prefix bounds the token
+// candidates: the expected rank of the k_tok-th largest key (128 k/n), plus
 // three binomial standard deviations and 4, so that fewer than k_tok keys
 // reach the bound only rarely (the full select then runs).  0 (no candidate
 // path) when the bound would keep most of the row anyway.
 int token_sample_rank(int n, int k_tok) {
     if (n <= 0 || k_tok >= n) return 0;
-    const double S = kWaves * kSamplePerWave, p = (double)k_tok / n;
+    const double S = kSamples, p = (double)k_tok / n;
     const double r = S * p + 3.0 * sqrt(S * p * (1.0 - p)) + 4.0;
     return r > 0.75 * S ? 0 : (int)ceil(r);
 }

@@ -125,22 +125,27 @@ def test_topk_tokens_random(lsa, oracle_lib, synth_lib, tune, case):
 # ---- the token select's candidate path and its fallbacks -----------------
 
 def _sample_positions(n_pos: int):
-    """Positions whose keys form the token select's sample: lanes 0-15 of
-    each of the 16 waves, slot (lane mod KPT) of the wave's KPT list entries."""
-    kpt = -(-n_pos // 1024)
-    pos = np.array([w * 64 * kpt + 64 * (l % kpt) + l for w in range(16) for l in range(16)])
-    return pos[pos < n_pos]  # the last wave's range runs past the row: those slots do not compete
+    """Positions whose keys form the token select's sample: for s = 0..127,
+    token (29 s + 7) mod 64 of list entry s * n_list / 128."""
+    n_list = n_pos // 64
+    return np.array([64 * (s * n_list // 128) + (29 * s + 7) % 64 for s in range(128)])
 
 
 @pytest.mark.parametrize("kind", ["normal", "quarters", "all_equal", "sample_high", "few_competing", "tiny_k",
-                                  "k_near_n", "negative"])
+                                  "k_near_n", "negative", "narrow", "cluster", "full_precision", "ascending"])
 def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
     """Rows that take the candidate path (a sample bound, then a select
     among the keys at or above it) and rows that miss it on purpose and run
     the full select: all keys equal (more candidates than LDS holds), the
     largest scores placed exactly on the sample (too few candidates), fewer
-    competing positions than k_tok, and extreme k_tok.  Bit-exact with the
-    oracle either way."""
+    competing positions than k_tok, and extreme k_tok.  Scores within a few
+    thousand ulps of each other ("narrow") make the candidates' histogram
+    exact at once; a dense cluster of values 4 ulps apart holding the k-th
+    largest ("cluster") sends it through three histogram levels; unrounded
+    fp32 normals ("full_precision") leave several values in the k-th key's
+    bin, which one wave then finishes; scores ascending along the row
+    ("ascending") give some waves more candidates than their LDS region
+    holds, so the full select runs.  Bit-exact with the oracle either way."""
     B, C, k = 3, 2048, 276
     n = k * 64
     s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), 31, synth_lib.stream(synth_lib.TAG_MISC, 6500)))
@@ -165,6 +170,17 @@ def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
         k_tok = n - 5
     elif kind == "negative":
         s = -np.abs(s) - 1.0
+    elif kind == "narrow":
+        r = np.random.default_rng(65)
+        s = (np.float32(1.0) + r.integers(0, 3000, s.shape) * np.float32(2.0 ** -23)).astype(np.float32)
+    elif kind == "ascending":  # the candidates crowd the last waves' ranges: more than a wave's LDS region holds
+        s = np.sort(s, axis=1)
+    elif kind == "full_precision":  # all 23 mantissa bits: the k-th largest key's bin holds several values
+        s = np.random.default_rng(67).standard_normal(s.shape).astype(np.float32)
+    elif kind == "cluster":
+        r = np.random.default_rng(66)
+        inside = r.random(s.shape) < 0.4
+        s = np.where(inside, np.float32(2.0) + r.integers(0, 64, s.shape) * np.float32(2.0 ** -20), s)
     s = np.ascontiguousarray(s, dtype=np.float32)
     ref, rc = oracle_lib.topk_tokens(s, ids, ctx, k_tok, counts=counts)
     tok, tc = lsa.lsa_topk_tokens(to_dev(s), to_dev(ids), to_dev(ctx), k_tok,
