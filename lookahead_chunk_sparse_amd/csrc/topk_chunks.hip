@@ -290,7 +290,8 @@ __device__ inline void ballot_finish(const uint32_t* lst, int cnt, int hi, int n
 // then selected from in LDS.
 constexpr int kSamples = 128;
 constexpr int kSampleBits = 12;        // key prefix the sample decides
-constexpr int kRegion = 832;           // (key, position) pairs each wave holds in LDS
+constexpr int kRegion = 768;           // (key, position) pairs each wave holds in LDS
+constexpr int kRegionStride = kRegion + 64;  // and one spare pair per lane: the writes need no branch
 constexpr int kCandWord0 = 4352;       // first word of the waves' regions in sm_raw
 constexpr int kTokBinBits = 12;        // digit width of the candidates' histogram
 constexpr int kTokBins = 1 << kTokBinBits;
@@ -335,21 +336,23 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], i
                                                    int* sm_i, int* sm_j, int* sm_cnt, int* sm_pick, int32_t* dst) {
     int* const hist = reinterpret_cast<int*>(sm_raw);   // [kTokBins]
     uint32_t* const small = sm_raw + kTokBins;           // [kSmallCap]
-    uint2* const reg = reinterpret_cast<uint2*>(sm_raw + kCandWord0) + wave * kRegion;  // this wave's pairs
+    uint2* const reg = reinterpret_cast<uint2*>(sm_raw + kCandWord0) + wave * kRegionStride;  // this wave's pairs
     static_assert(kTokBins + kSmallCap <= kCandWord0 && kCandWord0 % 4 == 0, "histogram and bucket below the pairs");
-    static_assert(kCandWord0 + 2 * kWaves * kRegion <= kBins * kLaneCopies + 2 * kListCap, "regions fit sm_raw");
+    static_assert(kCandWord0 + 2 * kWaves * kRegionStride <= kBins * kLaneCopies + 2 * kListCap, "regions fit sm_raw");
     static_assert(kThreads * 4 == kTokBins && kRegion % 64 == 0, "scan layout: 4 bins per thread; whole runs");
 
     // --- 1. the candidates ---
+    // Every lane writes at every slot, a key that is not a candidate to the
+    // lane's spare pair (a select instead of a branch around the store); past
+    // the region (then the full select runs) writes land among the spares.
     uint32_t n = 0;  // this wave's candidates so far
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         const bool in = key[e] >= pv;
         const uint64_t m = __ballot(in);
-        // past the region (then the full select runs) every write lands on its last pair
-        const uint32_t at = min(__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, n)),
-                                (uint32_t)kRegion - 1u);
-        if (in) reg[at] = make_uint2(key[e], (uint32_t)(wbase + 64 * e + lane));
+        const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, n));
+        reg[min(in ? at : (uint32_t)(kRegion + lane), (uint32_t)(kRegion + 63))] =
+            make_uint2(key[e], (uint32_t)(wbase + 64 * e + lane));
         n += (uint32_t)__popcll(m);
     }
     if (lane == 0) sm_i[wave] = (int)n;
