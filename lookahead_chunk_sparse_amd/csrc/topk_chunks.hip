@@ -443,7 +443,19 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], i
             if (wave == 0) {
                 // lanes past the bin hold 0, below every offset that can be picked
                 const uint32_t di = lane < cb ? small[lane] : 0u;
-                const uint32_t dv = wave_rank_value(di, sh, need);
+                uint32_t dv;
+                if (cb <= 16) {  // few keys: count, for every lane's key, the keys above it and at or above it
+                    int gt = 0, ge = 0;
+                    for (int j = 0; j < cb; ++j) {
+                        const uint32_t dj = (uint32_t)__builtin_amdgcn_readlane((int)di, j);
+                        gt += dj > di;
+                        ge += dj >= di;
+                    }
+                    const uint64_t hm = __ballot(lane < cb && gt < need && need <= ge);  // the lanes holding v*
+                    dv = (uint32_t)__builtin_amdgcn_readlane((int)di, __builtin_ctzll(hm | (1ull << 63)));
+                } else {
+                    dv = wave_rank_value(di, sh, need);
+                }
                 const int n_gt = __popcll(__ballot(lane < cb && di > dv));
                 if (lane == 0) {
                     sm_pick[0] = (int)(lo + dv);

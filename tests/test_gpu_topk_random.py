@@ -132,7 +132,8 @@ def _sample_positions(n_pos: int):
 
 
 @pytest.mark.parametrize("kind", ["normal", "quarters", "all_equal", "sample_high", "few_competing", "tiny_k",
-                                  "k_near_n", "negative", "narrow", "cluster", "full_precision", "ascending"])
+                                  "k_near_n", "negative", "narrow", "cluster", "full_precision", "ascending",
+                                  "band_at_boundary"])
 def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
     """Rows that take the candidate path (a sample bound, then a select
     among the keys at or above it) and rows that miss it on purpose and run
@@ -143,7 +144,9 @@ def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
     exact at once; a dense cluster of values 4 ulps apart holding the k-th
     largest ("cluster") sends it through three histogram levels; unrounded
     fp32 normals ("full_precision") leave several values in the k-th key's
-    bin, which one wave then finishes; scores ascending along the row
+    bin, which one wave then finishes (by pairwise counts; 40 distinct
+    keys in one bin at the boundary, "band_at_boundary", bit by bit); scores
+    ascending along the row
     ("ascending") give some waves more candidates than their LDS region
     holds, so the full select runs.  Bit-exact with the oracle either way."""
     B, C, k = 3, 2048, 276
@@ -173,6 +176,13 @@ def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
     elif kind == "narrow":
         r = np.random.default_rng(65)
         s = (np.float32(1.0) + r.integers(0, 3000, s.shape) * np.float32(2.0 ** -23)).astype(np.float32)
+    elif kind == "band_at_boundary":  # 2,038 large keys, then 40 distinct keys in [1, 1 + 2^-12): k-th in the band
+        r = np.random.default_rng(68)
+        for b in range(B):
+            perm = r.permutation(n)
+            s[b] = -50.0 + r.standard_normal(n)
+            s[b, perm[:2038]] = 50.0 + r.standard_normal(2038)
+            s[b, perm[2038:2078]] = 1.0 + r.random(40) * 2.0 ** -12
     elif kind == "ascending":  # the candidates crowd the last waves' ranges: more than a wave's LDS region holds
         s = np.sort(s, axis=1)
     elif kind == "full_precision":  # all 23 mantissa bits: the k-th largest key's bin holds several values
