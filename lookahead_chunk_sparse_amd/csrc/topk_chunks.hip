@@ -34,7 +34,10 @@
 // The same select serves the token-level stage: after the chunk recall the
 // model's own token scores pick a fine-grained top-k among the recalled
 // tokens only (same summary, 2.1 Architecture); there the keys are float
-// scores over the list positions of the recalled chunks.
+// scores over the list positions of the recalled chunks.  Token rows held in
+// registers first try a fast select (tokens_fast_select): a sampled bound,
+// the keys above it copied to LDS, a 12-bit histogram and an ordered
+// compaction of those keys only; the radix select above is its fallback.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
