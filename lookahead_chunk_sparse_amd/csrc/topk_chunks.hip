@@ -333,10 +333,11 @@ constexpr int kBufferWord3 = 0x00020000;
 // words at the start of sm_raw must be zero on entry.  Uses sm_raw: [0,
 // 4096) histogram (bin b at word hist_word(b)), [4096, 4160) small bucket,
 // from kCandWord0 the waves' regions of kRegion pairs.
-template <int KPT>
-__device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], int kk, uint32_t kmax, uint32_t pv,
-                                                   int wbase, int tid, int lane, int wave, uint32_t* sm_raw,
-                                                   int* sm_i, int* sm_j, int* sm_cnt, int* sm_pick, int32_t* dst) {
+template <int KPT, class PosOf>
+__device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], PosOf pos_of, int kk, uint32_t kmax,
+                                                   uint32_t pv, int tid, int lane, int wave, uint32_t* sm_raw,
+                                                   int* sm_i, int* sm_j, int* sm_cnt, int* sm_pick, int32_t* dst,
+                                                   uint32_t* dst_key) {
     int* const hist = reinterpret_cast<int*>(sm_raw);   // [kTokBins]
     uint32_t* const small = sm_raw + kTokBins;           // [kSmallCap]
     uint2* const reg = reinterpret_cast<uint2*>(sm_raw + kCandWord0) + wave * kRegionStride;  // this wave's pairs
@@ -354,8 +355,7 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], i
         const bool in = key[e] >= pv;
         const uint64_t m = __ballot(in);
         const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, n));
-        reg[min(in ? at : (uint32_t)(kRegion + lane), (uint32_t)(kRegion + 63))] =
-            make_uint2(key[e], (uint32_t)(wbase + 64 * e + lane));
+        reg[min(in ? at : (uint32_t)(kRegion + lane), (uint32_t)(kRegion + 63))] = make_uint2(key[e], pos_of(e));
         n += (uint32_t)__popcll(m);
     }
     if (lane == 0) sm_i[wave] = (int)n;
@@ -515,7 +515,10 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], i
         const uint64_t em = __ballot(eq);
         const bool take = p.x > vstar || (eq && eq_seen + lanes_below(em) < keep);
         const uint64_t tm = __ballot(take);
-        if (take) dst[out + lanes_below(tm)] = (int32_t)p.y;
+        if (take) {
+            dst[out + lanes_below(tm)] = (int32_t)p.y;
+            if (dst_key) dst_key[out + lanes_below(tm)] = p.x;  // slices hand their keys to the candidates pass
+        }
         out += __popcll(tm);
         eq_seen += __popcll(em);
     }
@@ -561,6 +564,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     // before any is used; keys are formed without branches (a load whose
     // only use sits under a branch moves into it and waits there).
     uint32_t key[KPT];
+    uint32_t cpos_e[MODE == kModeCand ? KPT : 1];  // candidates: row position of each slot's key
     int lim_l = 0;        // list rows: usable tokens of the wave's entry `lane` (lane < KPT)
     if constexpr (MODE == kModeTokens || MODE == kModeSlice) {
         // slot e of wave w is exactly list entry j = off/64 + w*KPT + e (64 tokens)
@@ -589,14 +593,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         // that its rank is found while the row's loads are in flight: lane
         // l takes token (29 l + 7) mod 64 of list entry l * n_list / 64, as a
         // 12-bit key prefix (0 where the token is not usable).
-        const bool sampler = MODE == kModeTokens && wave == 0 && a.sample_rank > 0;  // uniform
-        // sample s = lane and lane + 64: token (29 s + 7) mod 64 of list entry s * n_list / 128
-        const int js0 = (int)(((int64_t)lane * a.n_list) / kSamples);
-        const int js1 = (int)(((int64_t)(lane + 64) * a.n_list) / kSamples);
+        const bool sampler = wave == 0 && a.sample_rank > 0;  // uniform
+        // sample s = lane and lane + 64: token (29 s + 7) mod 64 of list entry
+        // j0 + s * E / 128 of the workgroup's E = C / 64 entries
+        const int n_ent = C > 0 ? C / kChunkTokens : 0;
+        const int js0 = j0 + (int)(((int64_t)lane * n_ent) / kSamples);
+        const int js1 = j0 + (int)(((int64_t)(lane + 64) * n_ent) / kSamples);
         const int ts0 = (29 * lane + 7) & (kChunkTokens - 1), ts1 = (29 * (lane + 64) + 7) & (kChunkTokens - 1);
         uint32_t cs0 = 0, cs1 = 0;
         float vs0 = 0.0f, vs1 = 0.0f;
-        if (sampler) {
+        if (sampler && n_ent > 0) {
             cs0 = (uint32_t)ids[js0];
             cs1 = (uint32_t)ids[js1];
             vs0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (64 * js0 + ts0) * 4, 0, 0));
@@ -633,10 +639,30 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         }
     } else if constexpr (MODE == kModeCand) {
         const uint32_t* krow = a.cand_key + (int64_t)row * C;
+        const int32_t* prow = a.cand_pos + (int64_t)row * C;
+        // the fast select's sample: keys s * C / 128 for s = lane, lane + 64
+        const bool sampler = wave == 0 && a.sample_rank > 0;  // uniform
+        uint32_t ks0 = 0, ks1 = 0;
+        if (sampler) {
+            ks0 = krow[(int)(((int64_t)lane * C) / kSamples)];
+            ks1 = krow[(int)(((int64_t)(lane + 64) * C) / kSamples)];
+        }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int idx = wbase + 64 * e + lane;
             key[e] = krow[idx < C ? idx : C - 1];
+        }
+        if (a.sample_rank > 0) {  // the fast select keeps each key's row position with it
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int idx = wbase + 64 * e + lane;
+                cpos_e[e] = (uint32_t)prow[idx < C ? idx : C - 1];
+            }
+        }
+        if (sampler) {
+            const uint32_t p = wave_rank_value2(ks0 >> (32 - kSampleBits), ks1 >> (32 - kSampleBits), kSampleBits,
+                                                a.sample_rank);
+            if (lane == 0) sm_pv = p << (32 - kSampleBits);
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) key[e] &= 0u - (uint32_t)(wbase + 64 * e + lane < C);
@@ -698,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
         sm_avail[wave] = avail;
     }
     if (tid == 0) sm_cnt[0] = 0;
-    if constexpr (MODE == kModeTokens) {
+    if constexpr (MODE != kModeLogits) {
         // the fast select's histogram starts at zero
         if (a.sample_rank > 0) reinterpret_cast<int4*>(sm_raw)[tid] = make_int4(0, 0, 0, 0);
     }
@@ -731,11 +757,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     }
     const int n_ok = kScoreKeys ? avail : C;  // competing keys
 
-    if constexpr (MODE == kModeTokens) {
+    if constexpr (MODE != kModeLogits) {
+        // the position a kept key is written as
+        auto pos_of = [&](int e) -> uint32_t {
+            if constexpr (MODE == kModeCand) return cpos_e[e];
+            else return (uint32_t)(off + wbase + 64 * e + lane);
+        };
         if (a.sample_rank > 0 && kk < n_ok &&
-            tokens_fast_select<KPT>(key, kk, kmax, sm_pv ? sm_pv : 1u, wbase, tid, lane, wave, sm_raw, sm_i, sm_j,
-                                    sm_cnt, sm_pick, dst))
+            tokens_fast_select<KPT>(key, pos_of, kk, kmax, sm_pv ? sm_pv : 1u, tid, lane, wave, sm_raw, sm_i, sm_j,
+                                    sm_cnt, sm_pick, dst, dst_key))
             return;
+    }
+    if constexpr (MODE == kModeTokens) {
         // the full select below works on key - (the smallest competing key)
         uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
@@ -1301,8 +1334,10 @@ hipError_t launch_topk_tokens(const float* scores, const int32_t* list_ids, cons
         a.cand_key = reinterpret_cast<uint32_t*>(w + round256(n * sizeof(int32_t)));
         a.n_slices = sp.slices;
         a.C = sp.slice_len;
+        a.sample_rank = token_sample_rank(sp.slice_len, k_tok);
         hipError_t e = launch_mode<kModeSlice>(a, R * sp.slices, sp.slice_len, stream);
         if (e != hipSuccess) return e;
+        a.sample_rank = token_sample_rank(sp.slices * k_tok, k_tok);
         return launch_mode<kModeCand>(a, R, sp.slices * k_tok, stream);
     }
     if (a.C >= stream_min_c()) {

@@ -134,7 +134,8 @@ def _sample_positions(n_pos: int):
 @pytest.mark.parametrize("kind", ["normal", "quarters", "all_equal", "sample_high", "few_competing", "tiny_k",
                                   "k_near_n", "negative", "narrow", "cluster", "full_precision", "ascending",
                                   "band_at_boundary"])
-def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
+@pytest.mark.parametrize("split", [False, True], ids=["one_workgroup", "slices"])
+def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, tune, kind, split):
     """Rows that take the candidate path (a sample bound, then a select
     among the keys at or above it) and rows that miss it on purpose and run
     the full select: all keys equal (more candidates than LDS holds), the
@@ -148,7 +149,9 @@ def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
     keys in one bin at the boundary, "band_at_boundary", bit by bit); scores
     ascending along the row
     ("ascending") give some waves more candidates than their LDS region
-    holds, so the full select runs.  Bit-exact with the oracle either way."""
+    holds, so the full select runs.  With `split` the row is cut into two
+    slices (the slice + candidates path, whose two kernels take the same
+    fast select); bit-exact with the oracle either way."""
     B, C, k = 3, 2048, 276
     n = k * 64
     s = synth_lib.bf16_bits_to_f32(synth_lib.normal_bf16((B, n), 31, synth_lib.stream(synth_lib.TAG_MISC, 6500)))
@@ -192,8 +195,11 @@ def test_topk_tokens_candidate_path(lsa, oracle_lib, synth_lib, kind):
         inside = r.random(s.shape) < 0.4
         s = np.where(inside, np.float32(2.0) + r.integers(0, 64, s.shape) * np.float32(2.0 ** -20), s)
     s = np.ascontiguousarray(s, dtype=np.float32)
+    if split:
+        tune(topk_split_min_n=1)
     ref, rc = oracle_lib.topk_tokens(s, ids, ctx, k_tok, counts=counts)
     tok, tc = lsa.lsa_topk_tokens(to_dev(s), to_dev(ids), to_dev(ctx), k_tok,
-                                  counts=None if counts is None else to_dev(counts), workspace=None)
-    assert np.array_equal(tc.cpu().numpy(), rc), kind
-    assert np.array_equal(tok.cpu().numpy(), ref), kind
+                                  counts=None if counts is None else to_dev(counts),
+                                  workspace="auto" if split else None)
+    assert np.array_equal(tc.cpu().numpy(), rc), (kind, split)
+    assert np.array_equal(tok.cpu().numpy(), ref), (kind, split)
