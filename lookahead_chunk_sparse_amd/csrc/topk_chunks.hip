@@ -286,11 +286,12 @@ __device__ inline void ballot_finish(const uint32_t* lst, int cnt, int hi, int n
     }
 }
 
-// Token mode's fast select: wave 0 draws kSamples keys spread over the row
-// (two per lane) while the other waves form their keys; the 12-bit key prefix of the sample
-// key of rank sample_rank bounds a candidate set (every key at or above that
-// prefix) that holds the kept keys whenever it has at least k members; it is
-// then selected from in LDS.
+// The fast select of score rows (token rows, their slices and their
+// candidates): wave 0 draws kSamples keys spread over the workgroup's
+// positions (two per lane) while the other waves form their keys; the 12-bit
+// key prefix of the sample key of rank sample_rank bounds a candidate set
+// (every key at or above that prefix) that holds the kept keys whenever it
+// has at least k members; it is then selected from in LDS.
 constexpr int kSamples = 128;
 constexpr int kSampleBits = 12;        // key prefix the sample decides
 constexpr int kRegion = 768;           // (key, position) pairs each wave holds in LDS
@@ -307,13 +308,13 @@ __device__ inline int hist_word(uint32_t b) { return (int)(b ^ ((b >> 5) & 31u))
 // Word 3 of a buffer resource on this GPU family: 32-bit raw data, no swizzle.
 constexpr int kBufferWord3 = 0x00020000;
 
-
-// Token mode, register-resident row of KPT keys per thread, kk < competing
-// keys.  The per-step cost of this one-workgroup select is set by the issue
-// rate of its one compute unit (16 waves share 4 SIMDs, one scalar unit and
-// the LDS), so every step below is a few instructions per wave between
-// barriers:
-//  1. The bound pv (taken by the caller from a 64-key sample) splits off
+// Score row (token, slice or candidates mode), register-resident, KPT keys
+// per thread, kk < competing keys; pos_of(e) is the position slot e's key is
+// written as, dst_key (slices only) receives the kept keys too.  The cost of
+// this one-workgroup select is set by the issue rate of its one compute unit
+// (16 waves share 4 SIMDs, one scalar unit and the LDS), so every step below
+// is a few instructions per wave between barriers:
+//  1. The bound pv (taken by the caller from the 128-key sample) splits off
 //     the candidates, every key >= pv: each wave copies its own to its LDS
 //     region as (key, position) pairs, in position order.  If fewer than kk
 //     keys reach pv in all, or some wave has more than its region holds,
