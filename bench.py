@@ -653,7 +653,8 @@ def main():
     ap.add_argument("--segment", type=int, default=0, metavar="S",
                     help="resident tokens per request (local window, decoded tokens, compressed entries) "
                          "attended in the same softmax as the recalled chunks (HBM-resident, one layer)")
-    ap.add_argument("--fetch", default="pull", choices=("pull", "memcpy"), help="host-tier fetch method")
+    ap.add_argument("--fetch", default="memcpy", choices=("pull", "memcpy"),
+                    help="host-tier fetch: DMA copies over the library's copy streams (memcpy) or the device gather (pull)")
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
     ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
     ap.add_argument("--drift", action="store_true", help="host tier: a fresh indexer query every interval")

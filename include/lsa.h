@@ -75,12 +75,15 @@ typedef enum lsa_tuning {
                                        lsa_topk_tokens splits a row over workgroups */
     LSA_TUNE_TOPK_SPLIT_SLICES = 4, /* LSA_TOPK_SPLIT_SLICES: slices of such a split
                                        (default: chosen from the sizes) */
-    LSA_TUNE_COUNT = 5
+    LSA_TUNE_FETCH_LANES = 5,       /* LSA_FETCH_LANES: copy streams lsa_fetch_chunks
+                                       spreads its copies over, 1-16 (4) */
+    LSA_TUNE_COUNT = 6
 } lsa_tuning;
 
 /* Override a knob (an lsa_tuning value) for the calling thread; value 0
  * drops the override.  LSA_ERR_INVALID_ARGUMENT for an unknown knob or a
- * value out of range (negative; ring depth other than 2-4).  The knob is
+ * value out of range (negative; ring depth other than 2-4; more than 16
+ * fetch streams).  The knob is
  * passed as int32_t so that any integer a caller passes is well defined. */
 lsa_status lsa_set_tuning(int32_t knob, int32_t value);
 
@@ -380,16 +383,26 @@ lsa_status lsa_check_ids(const int32_t* chunk_ids, const int32_t* slots, const i
  * Indexer, item 3).  For every request b and entry j:
  *     pool_kv[b][slot] := host_kv[b][chunk_ids[b][j]]   (K and V, all heads)
  * with slot = host_slots[b][j] (NULL: slot j), as host-to-device copies
- * enqueued on `side_stream`; entries whose chunk ids and slots both run on
- * consecutively are merged into one copy.  If `done` is not NULL it is
- * recorded on `side_stream` after the last copy, so a compute stream can
- * wait on it (hipStreamWaitEvent) before attending over the pool.
+ * ordered on `side_stream`; entries whose chunk ids and slots both run on
+ * consecutively are merged into one copy, and an entry with a negative slot
+ * is not copied (its id is not read): the fetch_slots of lsa_pool_assign
+ * (-1 for a chunk already in the pool, or an entry not in use) give a delta
+ * fetch.  The copies are spread round-robin over LSA_TUNE_FETCH_LANES (4)
+ * streams of the library's own (created for the current device at the first
+ * call, default priority, kept until the process ends) that start after the
+ * work already on
+ * `side_stream` and that `side_stream` waits for again, so several DMA copies
+ * are in flight at once; under graph capture they stay on `side_stream`.  If
+ * `done` is not NULL it is recorded on `side_stream` after the last copy, so
+ * a compute stream can wait on it (hipStreamWaitEvent) before attending over
+ * the pool.
  *
  *  host_kv         host bf16 [B][C][2][Hkv][64][d], pinned (hipHostMalloc);
  *                  pageable memory is rejected with LSA_ERR_INVALID_ARGUMENT
  *  C               chunks per request in host_kv
- *  host_chunk_ids  host int32 [B][k], each in [0, C) (checked)
- *  host_slots      host int32 [B][k], each in [0, P) (checked), or NULL
+ *  host_chunk_ids  host int32 [B][k], each in [0, C) (checked) where copied
+ *  host_slots      host int32 [B][k], each < P (checked; negative: not
+ *                  copied), or NULL
  *  pool_kv         device bf16 [B][P][2][Hkv][64][d]
  *  P               chunk slots per request in the pool (k <= P when slots is NULL)
  *  B, Hkv, d, k    >= 1

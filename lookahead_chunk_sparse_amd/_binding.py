@@ -37,9 +37,10 @@ TUNE_SCORE_MFMA_MIN_NQ = 1
 TUNE_TOPK_STREAM_MIN_C = 2
 TUNE_TOPK_SPLIT_MIN_N = 3
 TUNE_TOPK_SPLIT_SLICES = 4
+TUNE_FETCH_LANES = 5
 TUNE_KNOBS = {"attend_depth": TUNE_ATTEND_DEPTH, "score_mfma_min_nq": TUNE_SCORE_MFMA_MIN_NQ,
               "topk_stream_min_c": TUNE_TOPK_STREAM_MIN_C, "topk_split_min_n": TUNE_TOPK_SPLIT_MIN_N,
-              "topk_split_slices": TUNE_TOPK_SPLIT_SLICES}
+              "topk_split_slices": TUNE_TOPK_SPLIT_SLICES, "fetch_lanes": TUNE_FETCH_LANES}
 
 
 class LsaError(RuntimeError):

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/lsa.h"
@@ -58,20 +59,67 @@ lsa_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// ---- the DMA fetch's streams ----
+constexpr int kFetchLanes = 16;  // library streams one lsa_fetch_chunks call may spread its copies over
+constexpr int kMaxDevices = 64;
+struct FetchLanes {
+    std::mutex mu;  // one call at a time records and waits on the fork and join events
+    hipStream_t s[kFetchLanes] = {};
+    hipEvent_t fork = nullptr, join[kFetchLanes] = {};
+};
+
+// The current device's fetch streams and events (default priority, no
+// timing; all kFetchLanes, of which a call uses LSA_TUNE_FETCH_LANES),
+// created at the first use and kept until the process ends;
+// nullptr if they cannot be created (the copies then stay on the caller's
+// stream).
+FetchLanes* fetch_lanes() {
+    static std::mutex init_mu;
+    static FetchLanes* per_dev[kMaxDevices] = {};
+    static bool failed[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> g(init_mu);
+    if (per_dev[dev] || failed[dev]) return per_dev[dev];
+    auto* f = new FetchLanes();
+    bool good = hipEventCreateWithFlags(&f->fork, hipEventDisableTiming) == hipSuccess;
+    for (int l = 0; l < kFetchLanes && good; ++l)
+        good = hipStreamCreateWithFlags(&f->s[l], hipStreamNonBlocking) == hipSuccess &&
+               hipEventCreateWithFlags(&f->join[l], hipEventDisableTiming) == hipSuccess;
+    if (!good) {
+        (void)hipGetLastError();
+        for (int l = 0; l < kFetchLanes; ++l) {
+            if (f->s[l]) (void)hipStreamDestroy(f->s[l]);
+            if (f->join[l]) (void)hipEventDestroy(f->join[l]);
+        }
+        if (f->fork) (void)hipEventDestroy(f->fork);
+        delete f;
+        failed[dev] = true;
+        return nullptr;
+    }
+    per_dev[dev] = f;
+    return f;
+}
+
 // A launch counts its work-items (workgroups x threads) in 32 bits: these
 // bound the workgroups of the launches whose count follows the arguments.
 constexpr int64_t kMaxRowGroups = (int64_t)1 << 22;    // 1024-thread top-k / pool workgroups
 constexpr int64_t kMaxSplitGroups = (int64_t)1 << 24;  // 256-thread attention workgroups
 
 // ---- tuning knobs (include/lsa.h, lsa_tuning) ----
-constexpr const char* kTuneEnv[LSA_TUNE_COUNT] = {"LSA_ATTEND_DEPTH", "LSA_SCORE_MFMA_MIN_NQ", "LSA_TOPK_STREAM_MIN_C",
-                                                  "LSA_TOPK_SPLIT_MIN_N", "LSA_TOPK_SPLIT_SLICES"};
+constexpr const char* kTuneEnv[LSA_TUNE_COUNT] = {"LSA_ATTEND_DEPTH",     "LSA_SCORE_MFMA_MIN_NQ",
+                                                  "LSA_TOPK_STREAM_MIN_C", "LSA_TOPK_SPLIT_MIN_N",
+                                                  "LSA_TOPK_SPLIT_SLICES", "LSA_FETCH_LANES"};
 // the library's own choice where it is a constant (0: chosen per call)
-constexpr int32_t kTuneDefault[LSA_TUNE_COUNT] = {2, 16, lsa::kTopkRegisterMaxC + 1, 32769, 0};
+constexpr int32_t kTuneDefault[LSA_TUNE_COUNT] = {2, 16, lsa::kTopkRegisterMaxC + 1, 32769, 0, 4};
 
 bool tune_value_ok(int knob, int32_t v) {
     if (v < 0) return false;
     if (knob == LSA_TUNE_ATTEND_DEPTH) return v == 0 || (v >= 2 && v <= 4);
+    if (knob == LSA_TUNE_FETCH_LANES) return v <= 16;
     return true;
 }
 
@@ -345,10 +393,11 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
         return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, d, k must all be >= 1");
     if (!host_slots && k > P) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d > P=%lld with default slots", k, (long long)P);
     for (int64_t e = 0; e < (int64_t)B * k; ++e) {
+        if (host_slots && host_slots[e] < 0) continue;  // not copied: its id is not read
         if (host_chunk_ids[e] < 0 || host_chunk_ids[e] >= C)
             return fail(LSA_ERR_INVALID_ARGUMENT, "chunk id %d at entry %lld outside [0, %lld)", host_chunk_ids[e],
                         (long long)e, (long long)C);
-        if (host_slots && (host_slots[e] < 0 || host_slots[e] >= P))
+        if (host_slots && host_slots[e] >= P)
             return fail(LSA_ERR_INVALID_ARGUMENT, "slot %d at entry %lld outside [0, %lld)", host_slots[e],
                         (long long)e, (long long)P);
     }
@@ -361,13 +410,39 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
         return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv is not pinned host memory (allocate it with hipHostMalloc)");
     }
     const size_t chunk_bytes = (size_t)2 * Hkv * lsa::kChunkTokens * d * sizeof(uint16_t);
+    // The copies go round-robin onto kFetchLanes library streams that start
+    // after, and rejoin, side_stream: one stream's copies run one after the
+    // other with a fixed cost each (about 20 GB/s in 256 KB copies), several
+    // streams overlap it.  Under graph capture they stay on side_stream.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(side_stream, &cap);
+    if (ce != hipSuccess) return hip_fail(ce, "capture status");
+    const int n_lanes = lsa::tuning(LSA_TUNE_FETCH_LANES);
+    FetchLanes* lanes = cap == hipStreamCaptureStatusNone && n_lanes > 1 ? fetch_lanes() : nullptr;
+    std::unique_lock<std::mutex> hold;
+    if (lanes) {
+        hold = std::unique_lock<std::mutex>(lanes->mu);
+        hipError_t e = hipEventRecord(lanes->fork, side_stream);
+        for (int l = 0; l < n_lanes && e == hipSuccess; ++l) e = hipStreamWaitEvent(lanes->s[l], lanes->fork, 0);
+        if (e != hipSuccess) return hip_fail(e, "fetch fork");
+    }
     hipError_t copy_err = hipSuccess;
+    int n_run = 0;
     lsa::coalesce_fetch_runs(host_chunk_ids, host_slots, B, k, [&](int32_t b, int64_t c0, int64_t p0, int32_t run) {
         const char* src = reinterpret_cast<const char*>(host_kv) + ((int64_t)b * C + c0) * chunk_bytes;
         char* dst = reinterpret_cast<char*>(pool_kv) + ((int64_t)b * P + p0) * chunk_bytes;
-        copy_err = hipMemcpyAsync(dst, src, run * chunk_bytes, hipMemcpyHostToDevice, side_stream);
+        copy_err = hipMemcpyAsync(dst, src, run * chunk_bytes, hipMemcpyHostToDevice,
+                                  lanes ? lanes->s[n_run++ % n_lanes] : side_stream);
         return copy_err == hipSuccess;
     });
+    if (lanes) {  // rejoin, also after a failed copy, so side_stream never runs ahead of what was issued
+        hipError_t e = hipSuccess;
+        for (int l = 0; l < n_lanes && e == hipSuccess; ++l) {
+            e = hipEventRecord(lanes->join[l], lanes->s[l]);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side_stream, lanes->join[l], 0);
+        }
+        if (e != hipSuccess && copy_err == hipSuccess) copy_err = e;
+    }
     if (copy_err != hipSuccess) return hip_fail(copy_err, "fetch copy");
     if (done) {
         hipError_t e = hipEventRecord(done, side_stream);

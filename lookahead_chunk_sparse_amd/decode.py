@@ -17,11 +17,12 @@ Two placements of the K/V:
     overlaps attention.  Two pool buffers alternate; the first interval waits
     for its own fetch.  The copy is either a device-side gather that reads
     the selected ids on the GPU (fetch="pull", the default: no host round
-    trip, graph-capturable) or one DMA copy per run of chunks issued from the
-    host (fetch="memcpy": the ids are copied to the host first).
-    With delta=True (pull only, the default) one pool of 2k slots replaces the
-    two buffers: chunks selected again keep their slot and only new chunks
-    are copied, into slots the selection being attended over does not hold.
+    trip, graph-capturable) or DMA copies issued from the host, spread over
+    several copy streams (fetch="memcpy": the ids, and the slots, are copied
+    to the host first; the copies use no compute unit).
+    With delta=True (the default) one pool of 2k slots replaces the two
+    buffers: chunks selected again keep their slot and only new chunks are
+    copied, into slots the selection being attended over does not hold.
 
 Two selection rules: a fixed budget of k chunks (selection="topk"), or the
 pages' sigmoid gating (selection="threshold": chunks whose score passes 0.5,
@@ -115,12 +116,11 @@ class LsaDecoder:
         self.fetch, self.fetch_grid = fetch, fetch_grid
         if selection not in ("topk", "threshold"):
             raise ValueError("selection must be 'topk' or 'threshold'")
-        if selection == "threshold" and host_kv is not None and fetch == "memcpy":
-            raise NotImplementedError("threshold selection on the host tier uses the pull fetch (ids stay on the GPU)")
         self.selection, self.logit_threshold = selection, int(logit_threshold)
-        self.delta = (fetch == "pull") if delta is None else bool(delta)
-        if self.delta and fetch != "pull":
-            raise ValueError("the delta fetch needs fetch='pull' (slots are assigned on the device)")
+        self.delta = True if delta is None else bool(delta)
+        if selection == "threshold" and host_kv is not None and fetch == "memcpy" and not self.delta:
+            # the -1 padding past a request's count is skipped through its slot (-1)
+            raise NotImplementedError("threshold selection with fetch='memcpy' on the host tier needs delta=True")
         self.sm_scale = 1.0 / math.sqrt(self.d) if sm_scale is None else sm_scale
         dev = torch.device(device)
         B = self.B
@@ -156,6 +156,8 @@ class LsaDecoder:
                 self.fetch_slots = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
             self.slots = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
             self.host_ids = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)]
+            self.host_slots = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)] \
+                if self.delta and fetch == "memcpy" else None
             self.side = torch.cuda.Stream(device=dev)
             self.ev_ids = torch.cuda.Event()
             self.ev_sel = torch.cuda.Event()
@@ -230,6 +232,8 @@ class LsaDecoder:
                             fetch_slots=self.fetch_slots[i % 2])
         if self.fetch == "memcpy":
             self.host_ids[i % 2].copy_(self.sel_ids[i % 2], non_blocking=True)
+            if self.delta:
+                self.host_slots[i % 2].copy_(self.fetch_slots[i % 2], non_blocking=True)
             self.ev_ids.record(main)
         else:
             self.ev_sel.record(main)
@@ -260,9 +264,10 @@ class LsaDecoder:
             ev0 = torch.cuda.Event(enable_timing=True)
             ev0.record(self.side)
         if self.fetch == "memcpy":
-            self.ev_ids.synchronize()  # the ids must be on the host before the copies are issued
+            self.ev_ids.synchronize()  # the ids (and slots) must be on the host before the copies are issued
             for host, pool in zip(self.host_layers or [self.host_kv], self.pools):
-                lsa_fetch_chunks(host, self.host_ids[i % 2], pool[i % 2], host_slots=None, stream=self.side,
+                lsa_fetch_chunks(host, self.host_ids[i % 2], pool[i % 2],
+                                 host_slots=self.host_slots[i % 2] if self.delta else None, stream=self.side,
                                  done=None)
         else:
             self.side.wait_event(self.ev_sel)  # selection i (and its slots) are on the device

@@ -74,9 +74,17 @@ static void rejected_calls() {
           LSA_ERR_INVALID_ARGUMENT);
     CHECK(strstr(lsa_last_error(), "99") != nullptr);
     ids[5] = 5;
-    slots[4] = -1;
+    slots[4] = 3;  // a slot past the pool
     CHECK(lsa_fetch_chunks(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, nullptr, nullptr) ==
           LSA_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(lsa_last_error(), "slot 3") != nullptr);
+    // a negative slot is not copied, so its id is not checked: the call gets as
+    // far as the pinned-memory test, which this (pageable) buffer fails
+    slots[4] = -1;
+    ids[4] = 99;
+    CHECK(lsa_fetch_chunks(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, nullptr, nullptr) ==
+          LSA_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(lsa_last_error(), "99") == nullptr);
     CHECK(lsa_fetch_chunks(host.data(), 10, ids.data(), nullptr, pool, 2, 2, 1, 64, 3, nullptr, nullptr) ==
           LSA_ERR_INVALID_ARGUMENT);
     for (int32_t s : {0, 1, 2, 3, 4, 5, -1, 99, INT32_MIN}) CHECK(lsa_status_string(s) != nullptr);
@@ -121,6 +129,7 @@ static void run_coalescing() {
         std::vector<int32_t> ids((size_t)B * k), slots((size_t)B * k);
         for (auto& x : ids) x = (int32_t)(rng() % 60);
         for (auto& x : slots) x = (int32_t)(rng() % 60);
+        const bool with_skips = with_slots && rng() % 2;  // negative slots: entries not copied
         if (trial % 3 == 0)  // long runs
             for (int32_t b = 0; b < B; ++b)
                 for (int32_t j = 1; j < k; ++j)
@@ -128,7 +137,11 @@ static void run_coalescing() {
                         ids[(size_t)b * k + j] = ids[(size_t)b * k + j - 1] + 1;
                         slots[(size_t)b * k + j] = slots[(size_t)b * k + j - 1] + 1;
                     }
-        // expanding the runs gives back every entry, in order, exactly once
+        if (with_skips)
+            for (auto& x : slots)
+                if (rng() % 4 == 0) x = -1 - (int32_t)(rng() % 3);
+        // expanding the runs gives back every entry with a slot >= 0 (all of
+        // them without slots), in order, exactly once
         std::vector<int64_t> got_c, got_p, got_b;
         int calls = 0;
         const bool done = lsa::coalesce_fetch_runs(ids.data(), with_slots ? slots.data() : nullptr, B, k,
@@ -143,14 +156,19 @@ static void run_coalescing() {
                                                        return true;
                                                    });
         CHECK(done);
-        CHECK(got_c.size() == ids.size());
+        size_t n_copied = 0;
+        for (size_t e = 0; e < ids.size(); ++e) n_copied += !(with_slots && slots[e] < 0);
+        CHECK(got_c.size() == n_copied);
         int expected_runs = 0;
-        for (int32_t b = 0; b < B && got_c.size() == ids.size(); ++b)
+        size_t g = 0;  // next expanded entry
+        for (int32_t b = 0; b < B && got_c.size() == n_copied; ++b)
             for (int32_t j = 0; j < k; ++j) {
                 const size_t e = (size_t)b * k + j;
+                if (with_slots && slots[e] < 0) continue;
                 const int64_t p = with_slots ? slots[e] : j;
-                CHECK(got_b[e] == b && got_c[e] == ids[e] && got_p[e] == p);
-                const bool cont = j > 0 && ids[e] == ids[e - 1] + 1 &&
+                CHECK(got_b[g] == b && got_c[g] == ids[e] && got_p[g] == p);
+                ++g;
+                const bool cont = j > 0 && !(with_slots && slots[e - 1] < 0) && ids[e] == ids[e - 1] + 1 &&
                                   p == (with_slots ? (int64_t)slots[e - 1] : (int64_t)j - 1) + 1;
                 expected_runs += !cont;
             }

@@ -165,7 +165,7 @@ def test_tuning_defaults_and_overrides(lsa):
 
 
 @pytest.mark.parametrize("knob,value", [("attend_depth", 1), ("attend_depth", 5), ("score_mfma_min_nq", -1),
-                                        (99, 1)])
+                                        ("fetch_lanes", 17), (99, 1)])
 def test_tuning_rejects_bad_values(lsa, knob, value):
     with pytest.raises(lsa.LsaError):
         lsa.lsa_set_tuning(knob, value)

@@ -50,7 +50,9 @@ def oracle_output(oracle, W, w, t, b, ids_b):
 @pytest.mark.parametrize("name,fetch,delta", [("tiny", None, None), ("32k", None, None), ("128k", None, None),
                                               ("500k", None, None), ("1m_host", "pull", True),
                                               ("1m_host", "pull", False), ("1m_host", "memcpy", False),
-                                              ("128k_host", "pull", True), ("32k_churn", "pull", True)])
+                                              ("1m_host", "memcpy", True), ("128k_host", "pull", True),
+                                              ("128k_host", "memcpy", True), ("32k_churn", "pull", True),
+                                              ("32k_churn", "memcpy", True)])
 def test_decode_workload(oracle_lib, name, fetch, delta):
     import torch
 

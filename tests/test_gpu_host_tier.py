@@ -6,8 +6,9 @@ selection made at interval i-1 while interval i's chunks are fetched):
     each request keeps its own number of chunks per interval (paperlayer.ai
     summary of FlashMemory-DeepSeek-V4, 2.1 Architecture: threshold
     selection; non-recalled entries are evicted to CPU memory), through the
-    delta fetch (pool slots assigned on the GPU from -1-padded lists) and the
-    two-buffer pull fetch, at the 32K shape and at the full 1M size;
+    delta fetch (pool slots assigned on the GPU from -1-padded lists; pull and
+    DMA copies) and the two-buffer pull fetch, at the 32K shape and at the
+    full 1M size;
   * several layers sharing one selection, each with its own host store and
     HBM pool (the lightning-indexer listing's cross-layer index reuse).
 
@@ -54,7 +55,8 @@ def calibrated_indexer(synth, w, n_intervals, n_rel, seed):
     return qs, K.astype(np.int8)
 
 
-def _run_threshold_host(oracle_lib, w, n_intervals, n_rel, steps_per_interval, check_reqs, delta, max_rel_rms):
+def _run_threshold_host(oracle_lib, w, n_intervals, n_rel, steps_per_interval, check_reqs, delta, max_rel_rms,
+                        fetch="pull"):
     import torch
 
     import synth
@@ -63,9 +65,9 @@ def _run_threshold_host(oracle_lib, w, n_intervals, n_rel, steps_per_interval, c
 
     dev = torch.device("cuda")
     qs, K = calibrated_indexer(synth, w, n_intervals, n_rel, seed=11)
-    say(f"  host store: B={w.B} C={w.C} k={w.k}, delta={delta}")
+    say(f"  host store: B={w.B} C={w.C} k={w.k}, delta={delta}, fetch={fetch}")
     dec = LsaDecoder(k_idx=to_dev(K), ctx_len=to_dev(W.ctx_lens(w)), Hq=w.Hq, k=w.k, alpha=w.alpha,
-                     host_kv=W.pinned_kv_store(w), selection="threshold", fetch="pull", delta=delta)
+                     host_kv=W.pinned_kv_store(w), selection="threshold", fetch=fetch, delta=delta)
     outs, sels = {}, {}
     for i in range(n_intervals):
         ts = [i * w.tau + j for j in range(steps_per_interval)]
@@ -111,13 +113,15 @@ def _run_threshold_host(oracle_lib, w, n_intervals, n_rel, steps_per_interval, c
         assert np.array_equal(pool[b][slots[b, :n]], W.kv_chunks(w, b, ids[b, :n])), f"pool of request {b}"
 
 
-@pytest.mark.parametrize("delta", [True, False])
-def test_threshold_selection_host_tier_32k(oracle_lib, delta):
+@pytest.mark.parametrize("delta,fetch", [(True, "pull"), (False, "pull"), (True, "memcpy")])
+def test_threshold_selection_host_tier_32k(oracle_lib, delta, fetch):
+    """With fetch='memcpy' the DMA copies skip the -1 padding through its
+    slot (-1) and spread over the library's copy streams."""
     from synth import workloads as W
     w = W.WORKLOADS["32k"].replace(B=4, k=64, host_tier=True)
     table = [[5, 20, 90, 0], [0, 40, 3, 90], [64, 1, 0, 30], [12, 0, 70, 64]]  # 90 > k: capped
-    say(f"threshold host tier 32k, delta={delta}")
-    _run_threshold_host(oracle_lib, w, 4, lambda i, b: table[i][b], 2, range(w.B), delta, 1e-3)
+    say(f"threshold host tier 32k, delta={delta}, fetch={fetch}")
+    _run_threshold_host(oracle_lib, w, 4, lambda i, b: table[i][b], 2, range(w.B), delta, 1e-3, fetch=fetch)
 
 
 @pytest.mark.slow
@@ -180,14 +184,15 @@ def test_layers_share_one_selection_on_host_tier(oracle_lib):
             assert np.array_equal(pool[b][slots[b]], W.kv_chunks(layer_w[l], b, sels[-1][b])), (l, b)
 
 
-def test_threshold_host_tier_memcpy_is_refused():
-    """The DMA fetch copies from host-side ids; variable-size selections stay
-    on the GPU with the pull fetch, and asking for the DMA fetch says so."""
+def test_threshold_host_tier_memcpy_needs_delta():
+    """The DMA fetch skips the -1 padding of a variable-size selection through
+    its slot; without the delta fetch's slots there is none, and asking for
+    that combination says so."""
     import torch
 
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
     host = torch.empty((1, 4, 2, 1, 64, 64), dtype=torch.bfloat16, pin_memory=True)
-    with pytest.raises(NotImplementedError, match="pull"):
+    with pytest.raises(NotImplementedError, match="delta=True"):
         LsaDecoder(k_idx=torch.zeros((1, 4, 64), dtype=torch.int8, device="cuda"),
                    ctx_len=torch.full((1,), 256, dtype=torch.int32, device="cuda"), Hq=8, k=2, alpha=0.01,
                    host_kv=host, selection="threshold", fetch="memcpy", delta=False)
