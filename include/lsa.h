@@ -390,9 +390,10 @@ lsa_status lsa_check_ids(const int32_t* chunk_ids, const int32_t* slots, const i
  * fetch.  The copies are spread round-robin over LSA_TUNE_FETCH_LANES (4)
  * streams of the library's own (created for the current device at the first
  * call, default priority, kept until the process ends) that start after the
- * work already on
- * `side_stream` and that `side_stream` waits for again, so several DMA copies
- * are in flight at once; under graph capture they stay on `side_stream`.  If
+ * work already on `side_stream` and that `side_stream` waits for again, so
+ * several DMA copies are in flight at once; under graph capture, or when
+ * `side_stream` belongs to another device than the current one, they stay
+ * on `side_stream`.  If
  * `done` is not NULL it is recorded on `side_stream` after the last copy, so
  * a compute stream can wait on it (hipStreamWaitEvent) before attending over
  * the pool.

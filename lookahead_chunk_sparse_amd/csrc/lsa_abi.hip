@@ -417,8 +417,21 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     const hipError_t ce = hipStreamIsCapturing(side_stream, &cap);
     if (ce != hipSuccess) return hip_fail(ce, "capture status");
+    // The library's streams belong to the current device: a side_stream of
+    // another device keeps its copies.
     const int n_lanes = lsa::tuning(LSA_TUNE_FETCH_LANES);
-    FetchLanes* lanes = cap == hipStreamCaptureStatusNone && n_lanes > 1 ? fetch_lanes() : nullptr;
+    bool fan_out = cap == hipStreamCaptureStatusNone && n_lanes > 1;
+    if (fan_out) {
+        int cur_dev = -1;
+        hipDevice_t stream_dev = -1;
+        if (hipGetDevice(&cur_dev) != hipSuccess || hipStreamGetDevice(side_stream, &stream_dev) != hipSuccess) {
+            (void)hipGetLastError();  // a failed query only keeps the copies on side_stream
+            fan_out = false;
+        } else {
+            fan_out = stream_dev == cur_dev;
+        }
+    }
+    FetchLanes* lanes = fan_out ? fetch_lanes() : nullptr;
     std::unique_lock<std::mutex> hold;
     if (lanes) {
         hold = std::unique_lock<std::mutex>(lanes->mu);
