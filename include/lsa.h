@@ -28,8 +28,11 @@
  *    range and distinct); lsa_check_ids checks a list on request.
  *  - A chunk is LSA_CHUNK_TOKENS = 64 consecutive tokens.
  *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
- *  - Calls keep no mutable global state (the tuning overrides below are per
- *    thread) and may be issued from several host threads on different
+ *  - Calls keep no mutable global state that a result depends on: per
+ *    device the library holds only the copy streams of lsa_fetch_chunks and
+ *    the scratch array of lsa_gather_attend_noalloc, set up at their first
+ *    use and kept until the process ends; the tuning overrides below are per
+ *    thread.  Calls may be issued from several host threads on different
  *    streams.
  *  - Tuning knobs (lsa_tuning below) choose among kernels and launch shapes;
  *    none changes a result.
@@ -83,8 +86,8 @@ typedef enum lsa_tuning {
 /* Override a knob (an lsa_tuning value) for the calling thread; value 0
  * drops the override.  LSA_ERR_INVALID_ARGUMENT for an unknown knob or a
  * value out of range (negative; ring depth other than 2-4; more than 16
- * fetch streams).  The knob is
- * passed as int32_t so that any integer a caller passes is well defined. */
+ * fetch streams).  The knob is passed as int32_t so that any integer a
+ * caller passes is well defined. */
 lsa_status lsa_set_tuning(int32_t knob, int32_t value);
 
 /* The value in effect for the calling thread (0: chosen per call from the
