@@ -359,17 +359,28 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], P
     static_assert(kThreads * 4 == kTokBins && kRegion % 64 == 0, "scan layout: 4 bins per thread; whole runs");
 
     // --- 1. the candidates ---
-    // Every lane writes at every slot, a key that is not a candidate to the
-    // lane's spare pair (a select instead of a branch around the store); past
-    // the region (then the full select runs) writes land among the spares.
-    uint32_t n = 0;  // this wave's candidates so far
+    // The wave's count comes first (ballots and scalar counts only); if it
+    // fits the region, every lane writes at every slot, a key that is not a
+    // candidate to the lane's spare pair (a select instead of a branch around
+    // the store).  A wave whose candidates overflow writes nothing (the full
+    // select then runs).
+    uint64_t in_m[KPT];
+    uint32_t n_before[KPT];
+    uint32_t n = 0;  // this wave's candidates
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
-        const bool in = key[e] >= pv;
-        const uint64_t m = __ballot(in);
-        const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, n));
-        reg[min(in ? at : (uint32_t)(kRegion + lane), (uint32_t)(kRegion + 63))] = make_uint2(key[e], pos_of(e));
-        n += (uint32_t)__popcll(m);
+        in_m[e] = __ballot(key[e] >= pv);
+        n_before[e] = n;
+        n += (uint32_t)__popcll(in_m[e]);
+    }
+    if (n <= (uint32_t)kRegion) {  // uniform
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            // the lane's bit of the kept mask selects, without a second compare
+            const uint32_t at = n_before[e] + (uint32_t)lanes_below(in_m[e]);
+            reg[__builtin_amdgcn_inverse_ballot_w64(in_m[e]) ? at : (uint32_t)(kRegion + lane)] =
+                make_uint2(key[e], pos_of(e));
+        }
     }
     if (lane == 0) sm_i[wave] = (int)n;
     if (tid == 0) sm_cnt[1] = 0;  // small bucket fill, used after later barriers
@@ -504,13 +515,18 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], P
     }
 
     // --- 3. ordered compaction, each wave over its own region ---
+    // Two runs per trip with both loads issued first; the loads are
+    // unconditional (a run past nw reads stale words of the wave's stride,
+    // masked by i < nw), so no load waits behind a branch.
+    static_assert(kRegion + 64 <= kRegionStride, "a run past the region stays in the wave's stride");
     int n_gt = 0, n_eq = 0;
 #pragma unroll 1
-    for (int r = 0; r < nruns; ++r) {  // uniform trip count: the ballots see every lane
-        const int i = 64 * r + lane;
-        const uint32_t k = i < nw ? reg[i].x : 0u;  // key 0 < pv <= v*: neither
-        n_gt += __popcll(__ballot(k > vstar));
-        n_eq += __popcll(__ballot(k == vstar));
+    for (int r = 0; r < nruns; r += 2) {  // uniform trip count: the ballots see every lane
+        const int i0 = 64 * r + lane, i1 = i0 + 64;
+        const uint32_t x0 = reg[i0].x, x1 = reg[i1].x;
+        const uint32_t k0 = i0 < nw ? x0 : 0u, k1 = i1 < nw ? x1 : 0u;  // key 0 < pv <= v*: neither
+        n_gt += __popcll(__ballot(k0 > vstar)) + __popcll(__ballot(k1 > vstar));
+        n_eq += __popcll(__ballot(k0 == vstar)) + __popcll(__ballot(k1 == vstar));
     }
     if (lane == 0) {
         sm_i[wave] = n_gt;
@@ -520,20 +536,37 @@ __device__ __forceinline__ bool tokens_fast_select(const uint32_t (&key)[KPT], P
     const int gt_before = sum_below(sm_i, wave, lane), eq_before = sum_below(sm_j, wave, lane);
     int out = gt_before + min(eq_before, keep);
     int eq_seen = eq_before;
-#pragma unroll 1
-    for (int r = 0; r < nruns; ++r) {
-        const int i = 64 * r + lane;
-        const uint2 p = i < nw ? reg[i] : make_uint2(0u, 0u);
-        const bool eq = p.x == vstar;
-        const uint64_t em = __ballot(eq);
-        const bool take = p.x > vstar || (eq && eq_seen + lanes_below(em) < keep);
-        const uint64_t tm = __ballot(take);
-        if (take) {
-            dst[out + lanes_below(tm)] = (int32_t)p.y;
-            if (dst_key) dst_key[out + lanes_below(tm)] = p.x;  // slices hand their keys to the candidates pass
+    // the outputs as buffers of kk words: a store's offset is a lane's rank
+    // among the run's kept keys, its base the run's first output
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(dst, 0, kk * 4, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(dst_key ? dst_key : reinterpret_cast<uint32_t*>(dst), 0, kk * 4,
+                                          kBufferWord3);
+    // The masks are combined as lane masks (ballots of plain compares and
+    // scalar logic), so no bool is rebuilt from a mask and balloted again.
+    auto emit = [&](const uint2 p, const bool valid) {
+        const uint64_t vm = __ballot(valid);
+        const uint64_t em = vm & __ballot(p.x == vstar);
+        const uint64_t gm = vm & __ballot(p.x > vstar);
+        const uint64_t lm = __ballot(lanes_below(em) < keep - eq_seen);  // within the keys equal to v* kept
+        const uint64_t tm = gm | (em & lm);
+        if (__builtin_amdgcn_inverse_ballot_w64(tm)) {
+            const int at = 4 * lanes_below(tm);
+            __builtin_amdgcn_raw_buffer_store_b32(p.y, ors, at, 4 * out, 0);
+            if (dst_key) __builtin_amdgcn_raw_buffer_store_b32(p.x, krs, at, 4 * out, 0);  // slices hand their keys on
         }
         out += __popcll(tm);
         eq_seen += __popcll(em);
+    };
+#pragma unroll 1
+    for (int r = 0; r < nruns; r += 2) {
+        const int i0 = 64 * r + lane, i1 = i0 + 64;
+        const uint2 p0 = reg[i0], p1 = reg[i1];
+        // both pairs whole in registers here: a position used only under the
+        // store's branch would otherwise be loaded there and waited for
+        asm volatile("" ::"v"(p0.y), "v"(p1.y));
+        emit(p0, i0 < nw);
+        emit(p1, i1 < nw);
     }
     return true;
 }
