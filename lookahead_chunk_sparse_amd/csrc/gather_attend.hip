@@ -129,6 +129,25 @@ __device__ inline void load_slice_rows(Slice<D>& s, const uint16_t* krow, const 
     for (int r = 0; r < 4; ++r) s.v[r] = load_vrow<D, false>(vrow[r] + DPL * n);
 }
 
+// Across the 4 rows of 16 lanes: every lane gets the maximum (sum) of its
+// column, lanes l, l^16, l^32 and l^48.  gfx950's row-swap moves exchange
+// rows between two registers, so a copy of v swapped with itself puts lane
+// l^16 (then l^32) beside lane l with no LDS round trip.  Each step combines
+// the same two values per lane as a butterfly over l^16 and l^32, so the
+// results are the same bits.
+__device__ inline float max_over_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_over_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ inline short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 __device__ inline float bf16_value(short b) { return (float)__builtin_bit_cast(__bf16, b); }
 
@@ -163,9 +182,7 @@ __device__ inline void process_slice(Slice<D>& sl, int nvalid, uint32_t vmask, i
         sv[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
         vrow_mask(sl.v[r], ok);
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = max_over_rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     if (__any(mx > m_run)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
@@ -446,8 +463,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(AttendArgs a) {
     __shared__ float sm_m[kWaves][16];
     __shared__ float sm_l[kWaves][16];
     __shared__ float sm_o[kWaves * 16 * D];
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_over_rows(l_run);
     if (n < G) {
         if (i == 0) {
             sm_m[wave][n] = m_run;

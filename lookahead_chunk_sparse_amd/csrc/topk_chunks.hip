@@ -51,15 +51,31 @@ namespace {
 constexpr int kThreads = kTopkThreads;
 constexpr int kWaves = kThreads / 64;
 
+// Minimum and maximum over the 64 lanes of a wave, the same in every lane:
+// the DPP steps of an inclusive scan (row shifts of 1, 2, 4, 8, then the
+// row broadcasts of lanes 15 and 31), where a lane with no source takes the
+// operation's identity, leave the whole wave's result in lane 63.  Register
+// moves only: no LDS round trip per step, as a shuffle would take.
 __device__ inline uint32_t wave_min(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off));
-    return v;
+    int x = (int)v;
+    const int id = -1;  // 0xFFFFFFFF, the identity of an unsigned minimum
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x111, 0xF, 0xF, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x112, 0xF, 0xF, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x114, 0xF, 0xF, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x118, 0xF, 0xF, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x142, 0xA, 0xF, false));
+    x = (int)min((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(id, x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
 }
 __device__ inline uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
-    return v;
+    int x = (int)v;  // identity 0
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));
+    x = (int)max((uint32_t)x, (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane(x, 63);
 }
 
 constexpr int kDigitBits = 8;
@@ -88,8 +104,9 @@ __device__ inline void pick_digit(const int* sm_hist, int* sm_tot, int* sm_pick,
             const int4 v = p[i];
             t += (v.x + v.y) + (v.z + v.w);
         }
-        t += __shfl_xor(t, 1);
-        t += __shfl_xor(t, 2);
+        // quad sums by DPP lane swaps (quad_perm [1,0,3,2], then [2,3,0,1])
+        t += __builtin_amdgcn_update_dpp(0, t, 0xB1, 0xF, 0xF, false);
+        t += __builtin_amdgcn_update_dpp(0, t, 0x4E, 0xF, 0xF, false);
         if ((tid & 3) == 0) sm_tot[tid >> 2] = t;
     }
     __syncthreads();
@@ -757,11 +774,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
             if (capped) avail += __popcll(__ballot(o && key[e] > tkey));
         }
     }
-    if constexpr (kListRows) {
-#pragma unroll
-        for (int off2 = 32; off2 > 0; off2 >>= 1) lim_l += __shfl_xor(lim_l, off2);
-        avail = lim_l;
-    }
+    if constexpr (kListRows) avail = __builtin_amdgcn_readlane(wave_incl_sum(lim_l), 63);
     if constexpr (MODE != kModeTokens) lmin = wave_min(lmin);
     lmax = wave_max(lmax);
     if (lane == 0) {
