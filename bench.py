@@ -154,26 +154,46 @@ def capture(dec, w, q_all, qidx, n_steps, out):
     return g
 
 
-def time_attention_launches(dec, w, q_all, n_launches: int):
-    """Mean duration of one attention launch, timed with HIP events recorded
-    on the stream the kernel runs on (torch's current stream).  A few
-    untimed launches go first, without a wait, so the stream already holds
-    work when the first timed pair is recorded: otherwise the first pair
-    also spans the host's time to issue the launch."""
+def graph_timed(fn, n: int, reps: int = 3):
+    """Mean duration of one call fn(j) on the current stream: n calls captured
+    in one hipGraph, replayed back to back, with HIP events on the replay
+    stream around each of `reps` timed replays (after one untimed replay, so
+    the stream is busy when each timed pair is recorded).  Returns (the
+    median over the replays of replay time / n, every replay's per-call
+    mean), in ms.  The GPU runs the captured calls one after the other, so
+    the host's time to issue a call never enters, and one disturbed replay
+    does not move the median."""
     import torch
-    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launches)]
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn(0)  # eager first call (library set-up outside the capture)
+    stream.wait_stream(side)
     torch.cuda.synchronize()
-    for j in range(3):
-        dec.attend(q_all[j % q_all.shape[0]], 0, out)
-    for j, (a, b) in enumerate(evs):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            fn(j)
+    g.replay()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
         a.record(stream)
-        dec.attend(q_all[j % q_all.shape[0]], 0, out)
+        g.replay()
         b.record(stream)
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return statistics.mean(ms), statistics.median(ms), ms
+    per_call = [a.elapsed_time(b) / n for a, b in evs]
+    return statistics.median(per_call), per_call
+
+
+def time_attention_launches(dec, w, q_all, n_launches: int):
+    """Mean duration of one attention call (split kernel + combine) on the
+    stream it runs on, over n_launches calls replayed as one graph
+    (graph_timed).  Returns (mean ms, min and max of the replays' means)."""
+    import torch
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda:0")
+    mean_ms, per = graph_timed(lambda j: dec.attend(q_all[j % q_all.shape[0]], 0, out), n_launches)
+    return mean_ms, min(per), max(per)
 
 
 def host_cores() -> int:
@@ -454,22 +474,12 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int, repe
     ms_per_step = statistics.median(ms_runs) / steps
     steps_s = 1000.0 / ms_per_step
 
-    # the two per-step kernels, event-timed on the stream they run on
-    stream = torch.cuda.current_stream()
+    # the two per-step calls, each timed as 100 calls replayed in one graph
     dec.reselect(qidx[0], 0)
     ids = dec.sel_ids[0]
 
     def timed(fn, n=100):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for j in range(5):
-            fn(j)
-        torch.cuda.synchronize()
-        for j, (a, b) in enumerate(evs):
-            a.record(stream)
-            fn(j)
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.mean(a.elapsed_time(b) for a, b in evs)
+        return graph_timed(fn, n)[0]
 
     topk_ms = timed(lambda j: lsa_topk_tokens(pool[j % n_pool], ids, dec.ctx_len, k_tok, tok=dec.tok,
                                               tok_counts=dec.tok_counts, workspace=dec.tok_workspace))
@@ -502,7 +512,9 @@ def token_stage_bench(w, steps: int, warmup: int, k_tok: int, n_split: int, repe
         "roofline": {"bound": "hbm", "kernel": "gather-attend over listed tokens (split kernel + combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": a_bytes,
-                     "mean_launch_us": round(att_ms * 1e3, 2)},
+                     "mean_launch_us": round(att_ms * 1e3, 2),
+                     "launch_timing": "HIP events on the launch stream around replays of one graph of 100 "
+                                      "attention calls; median of 3 replays' per-call means"},
     }), flush=True)
 
 
@@ -637,13 +649,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="128k")
     ap.add_argument("--n-split", type=int, default=0, help="attention splits per (request, KV head); 0 = library")
-    ap.add_argument("--kernel-launches", type=int, default=200, help="event-timed attention launches")
+    ap.add_argument("--kernel-launches", type=int, default=200,
+                    help="attention calls per timed graph replay (the dominant kernel's timing)")
     ap.add_argument("--repeats", type=int, default=5, help="timed runs of exactly --steps steps (median reported)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the all-core cpu_baseline (the 1-thread one gets 0.6x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
-    ap.add_argument("--kernel-only", action="store_true", help="only the event-timed attention launches")
+    ap.add_argument("--kernel-only", action="store_true", help="only the timed attention calls")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--token-topk", type=int, default=0, metavar="K_TOK",
                     help="two-stage selection: attend over the K_TOK best tokens of the recalled chunks")
@@ -719,10 +732,10 @@ def main():
 
     if args.kernel_only:
         dec.reselect(qidx[0], 0)
-        mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
+        mean_ms, lo_ms, hi_ms = time_attention_launches(dec, w, q_all, args.kernel_launches)
         gbs = attend_bytes_per_launch(w, args.segment) / (mean_ms * 1e-3) / 1e9
         print(json.dumps({"kernel": "attend_split_kernel<128>+combine", "workload": w.name, "n_split": splits,
-                          "launches": args.kernel_launches, "mean_ms": mean_ms, "median_ms": med_ms,
+                          "launches": args.kernel_launches, "mean_ms": mean_ms, "replay_means_ms": [lo_ms, hi_ms],
                           "achieved_GBs": gbs}))
         return
 
@@ -753,13 +766,13 @@ def main():
     gating = gating_stats(dec, w, qidx[:(args.steps + w.tau - 1) // w.tau]) if args.selection == "threshold" else None
     k_step = gating["kept_mean"] if gating else None  # chunks attended per request and step, on average
 
-    # ---- the dominant kernel, event-timed on its own stream (interval 0's selection) ----
+    # ---- the dominant kernel, timed with events on its own stream (interval 0's selection) ----
     dec.reselect(qidx[0], 0)
-    mean_ms, med_ms, _ = time_attention_launches(dec, w, q_all, args.kernel_launches)
+    mean_ms, lo_ms, hi_ms = time_attention_launches(dec, w, q_all, args.kernel_launches)
     a_bytes = attend_bytes_per_launch(w, args.segment, gating["kept_mean_first_interval"] if gating else None)
     achieved = a_bytes / (mean_ms * 1e-3) / 1e9
-    log(f"[bench] attention launch: mean {mean_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
-        f"{achieved:.0f} GB/s algorithmic")
+    log(f"[bench] attention call, {args.kernel_launches} calls replayed as one graph: mean {mean_ms * 1e3:.1f} us "
+        f"(replays {lo_ms * 1e3:.1f}-{hi_ms * 1e3:.1f}), {achieved:.0f} GB/s algorithmic")
     traffic = traffic_for_current_kernel(w) if not args.segment else None  # counters: no segment
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy (torch, 1 GiB, read + write bytes): {copy_gbs:.0f} GB/s")
@@ -818,6 +831,8 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": a_bytes,
             "mean_launch_us": round(mean_ms * 1e3, 2),
+            "launch_timing": f"HIP events on the launch stream around replays of one graph of "
+                             f"{args.kernel_launches} attention calls; median of 3 replays' per-call means",
         },
     }
     if args.selection == "threshold":
