@@ -1,6 +1,8 @@
-"""The measurement-only tile-read kernel (the read ceiling bench.py reports)
-reads exactly the tiles it is given: every thread's XOR-fold of the 16-byte
-words it loaded matches numpy's."""
+"""bench.py's measurement helpers.  The measurement-only tile-read kernel
+(the read ceiling bench.py reports) reads exactly the tiles it is given:
+every thread's XOR-fold of the 16-byte words it loaded matches numpy's.  The
+graph timer that gives the dominant kernel's mean launch duration runs every
+call it claims to time."""
 import ctypes
 import os
 
@@ -35,3 +37,19 @@ def test_tile_read_reads_the_listed_tiles(unroll):
     # thread t reads words t, t + 256, t + 512, t + 768 of every tile
     want = np.bitwise_xor.reduce(words[tiles].reshape(n_tiles, 4, 256), axis=(0, 1))
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+def test_graph_timed_runs_every_call():
+    """graph_timed(fn, n, reps) makes one eager call, captures n calls in a
+    graph and replays it once untimed and reps times timed: a counter that
+    every call increments ends at 1 + n * (1 + reps), and the reported mean is
+    the median of the reps per-call means."""
+    import torch
+
+    import bench
+    x = torch.zeros(1, dtype=torch.int64, device="cuda")
+    mean_ms, per_call = bench.graph_timed(lambda j: x.add_(1 + 0 * j), 10, reps=3)
+    torch.cuda.synchronize()
+    assert int(x.item()) == 1 + 10 * 4
+    assert len(per_call) == 3 and all(p > 0 for p in per_call)
+    assert mean_ms == sorted(per_call)[1]
