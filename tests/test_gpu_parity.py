@@ -526,8 +526,14 @@ def test_attend_tokens_all_listed_equals_chunk_attention(lsa, synth_lib):
 
 # ------------------------------------------------------------------ fetch
 
-def test_fetch_byte_exact(lsa, oracle_lib, synth_lib):
+@pytest.mark.parametrize("lanes", [0, 1, 3, 16])
+def test_fetch_byte_exact(lsa, oracle_lib, synth_lib, tune, lanes):
+    """The DMA fetch with its copies on 1 stream (the caller's), on the
+    library's default of 4 copy streams, and on 3 and 16 of them: the same pool
+    bytes as the oracle's copy."""
     import torch
+    if lanes:
+        tune(fetch_lanes=lanes)
     B, C, Hkv, d, k, P = 2, 12, 2, 64, 5, 7
     host = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), 9, synth_lib.stream(synth_lib.TAG_MISC, 950))
     ids = np.array([[0, 1, 2, 7, 11], [3, 4, 6, 8, 9]], dtype=np.int32)
@@ -548,6 +554,53 @@ def test_fetch_byte_exact(lsa, oracle_lib, synth_lib):
     lsa.lsa_fetch_chunks(host_t, torch.from_numpy(ids), pool2, stream=side, done=ev)
     ev.synchronize()
     assert np.array_equal(pool2.cpu().view(torch.int16).numpy().view(np.uint16), oracle_lib.fetch_chunks(host, ids, k))
+
+
+def test_fetch_concurrent_threads_byte_exact(lsa, oracle_lib, synth_lib):
+    """Two host threads fetch at once, each on its own stream into its own
+    pool, both through the library's shared copy streams (each call holds the
+    fork and join events for its own use): every pool gets exactly its chunks
+    at their slots, and an entry with a negative slot (a chunk already in the
+    pool, as the delta fetch passes it) leaves the pool as it was."""
+    import threading
+
+    import torch
+    B, C, Hkv, d, k, P = 2, 64, 2, 64, 24, 48
+    host = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), 23, synth_lib.stream(synth_lib.TAG_MISC, 970))
+    host_t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(970)
+    jobs = []
+    for _ in range(2):
+        ids = np.stack([np.sort(rng.choice(C, k, replace=False)) for _ in range(B)]).astype(np.int32)
+        slots = np.stack([rng.choice(P, k, replace=False) for _ in range(B)]).astype(np.int32)
+        slots[:, ::5] = -1  # not copied
+        jobs.append((ids, slots))
+    one = np.uint16(0x3F80)  # bf16 1.0
+    pools = [torch.full((B, P, 2, Hkv, 64, d), 1.0, dtype=torch.bfloat16, device="cuda") for _ in jobs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            side = torch.cuda.Stream()
+            for _ in range(5):
+                lsa.lsa_fetch_chunks(host_t, torch.from_numpy(jobs[t][0]), pools[t],
+                                     host_slots=torch.from_numpy(jobs[t][1]), stream=side)
+            side.synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(len(jobs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (ids, slots), pool in zip(jobs, pools):
+        want = np.full((B, P, 2, Hkv, 64, d), one, dtype=np.uint16)
+        want = oracle_lib.fetch_chunks(host, ids, P, slots=slots, pool=want, skip_negative_slots=True)
+        assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
 def test_fetch_pull_byte_exact(lsa, oracle_lib, synth_lib):
