@@ -281,7 +281,8 @@ def spread(ms: list) -> dict:
             "max_ms": round(max(ms), 5), "spread": round(max(ms) / min(ms) - 1.0, 4)}
 
 
-def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_split: int = 0, delta=None):
+def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_split: int = 0, delta=None,
+                    stage_chunks: int = 1024):
     """The host-tier workload: the whole K/V in pinned host memory, selected
     chunks fetched into an HBM pool on a side stream every tau steps (lag 1,
     two pool buffers), attention on the pool.  Eager launches.  The timed
@@ -291,7 +292,8 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
     host-to-HBM bandwidth, PCIe-inclusive."""
     import torch
 
-    from lookahead_chunk_sparse_amd import lsa_fetch_chunks, lsa_fetch_chunks_pull
+    from lookahead_chunk_sparse_amd import (alloc_fetch_staging, lsa_fetch_chunks, lsa_fetch_chunks_pull,
+                                            lsa_fetch_chunks_staged)
     from lookahead_chunk_sparse_amd.decode import LsaDecoder
     from synth import workloads as W
 
@@ -301,7 +303,7 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
     ctx = torch.from_numpy(W.ctx_lens(w)).to(dev)
     host_kv = W.pinned_kv_store(w)
     dec = LsaDecoder(k_idx=K, ctx_len=ctx, Hq=w.Hq, k=w.k, alpha=w.alpha, host_kv=host_kv, fetch=fetch,
-                     fetch_grid=fetch_grid, n_split=n_split, delta=delta, device=dev)
+                     fetch_grid=fetch_grid, n_split=n_split, delta=delta, stage_chunks=stage_chunks, device=dev)
     log(f"[bench] pinned host K/V {host_kv.numel() * 2 / 1e9:.2f} GB placed in {time.time() - t0:.1f}s")
     n_warm_int = max(1, (warmup + w.tau - 1) // w.tau)
     n_time_int = max(1, steps // w.tau)
@@ -331,6 +333,9 @@ def host_tier_bench(w, steps: int, warmup: int, fetch: str, fetch_grid: int, n_s
 
     pool0 = pool0.contiguous() if not pool0.is_contiguous() else pool0
     alone = {"memcpy": timed(lambda: lsa_fetch_chunks(host_kv, ids_h, pool0, stream=dec.side))}
+    staging = dec.staging if dec.staging is not None else alloc_fetch_staging(host_kv, stage_chunks, device=dev)
+    alone["staged"] = timed(lambda: lsa_fetch_chunks_staged(host_kv, ids_h, pool0, *staging, stream=dec.side))
+    del staging
     for g in (8, 16, 64):
         alone[f"pull_grid{g}"] = timed(lambda: lsa_fetch_chunks_pull(host_kv, ids_d, pool0, grid=g,
                                                                      stream=dec.side))
@@ -666,9 +671,12 @@ def main():
     ap.add_argument("--segment", type=int, default=0, metavar="S",
                     help="resident tokens per request (local window, decoded tokens, compressed entries) "
                          "attended in the same softmax as the recalled chunks (HBM-resident, one layer)")
-    ap.add_argument("--fetch", default="memcpy", choices=("pull", "memcpy"),
-                    help="host-tier fetch: DMA copies over the library's copy streams (memcpy) or the device gather (pull)")
+    ap.add_argument("--fetch", default="staged", choices=("pull", "memcpy", "staged"),
+                    help="host-tier fetch: DMA copies over the library's copy streams (memcpy), the same through a "
+                         "host-gathered staging buffer (staged), or the device gather (pull)")
     ap.add_argument("--fetch-grid", type=int, default=0, help="workgroups of the pull fetch (0 = 16)")
+    ap.add_argument("--stage-chunks", type=int, default=1024,
+                    help="staged fetch: chunks of each staging buffer (two halves, one copy each)")
     ap.add_argument("--no-delta", action="store_true", help="host tier: re-fetch every selected chunk")
     ap.add_argument("--drift", action="store_true", help="host tier: a fresh indexer query every interval")
     ap.add_argument("--churn", type=float, default=0.0,
@@ -712,7 +720,7 @@ def main():
         return
     if w.host_tier:
         host_tier_bench(w, args.steps, args.warmup, args.fetch, args.fetch_grid, args.n_split,
-                        False if args.no_delta else None)
+                        False if args.no_delta else None, stage_chunks=args.stage_chunks)
         return
     dec = setup(w, args.n_split, args.layers, args.selection)
     if args.segment:

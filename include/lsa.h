@@ -30,7 +30,8 @@
  *  - bf16 values are passed as their raw 16-bit patterns (uint16_t).
  *  - Calls keep no mutable global state that a result depends on: per
  *    device the library holds only the copy streams of lsa_fetch_chunks and
- *    the scratch array of lsa_gather_attend_noalloc, set up at their first
+ *    the scratch array of lsa_gather_attend_noalloc, and per process the
+ *    host worker threads of lsa_fetch_chunks_staged, set up at their first
  *    use and kept until the process ends; the tuning overrides below are per
  *    thread.  Calls may be issued from several host threads on different
  *    streams.
@@ -417,6 +418,47 @@ lsa_status lsa_check_ids(const int32_t* chunk_ids, const int32_t* slots, const i
 lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,
                             const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
                             int32_t d, int32_t k, hipStream_t side_stream, hipEvent_t done);
+
+/*
+ * lsa_fetch_chunks_staged -- the fetch of lsa_fetch_chunks (the same
+ * definition, arguments and result in the pool), sent over the host link
+ * in large copies: the selected chunks lie scattered over the host store,
+ * and one copy per 256 KB chunk carries a fixed cost that keeps the link
+ * below half its rate.  Here the library's host worker threads gather the
+ * chunks to copy into consecutive places of a pinned staging buffer, each
+ * piece of up to stage_chunks / 2 chunks (at most 512) crosses the link as
+ * one hipMemcpyAsync on `side_stream`, and a kernel on `side_stream` moves
+ * the piece's chunks from the device staging buffer into their pool slots.
+ * Pieces alternate between the two halves of the staging buffers, so the
+ * host gathers one piece while the previous one is on the link.
+ *
+ * Defined by: as lsa_fetch_chunks (paperlayer.ai summary, 2.1 Architecture
+ * and 3 Experiments / Experimental Setup; sergiiob.dev handbook, The Neural
+ * Memory Indexer, item 3 and its closing paragraph on host-to-device
+ * bandwidth).
+ *
+ *  host_kv, C, host_chunk_ids, host_slots, pool_kv, P, B, Hkv, d, k, done:
+ *                 as for lsa_fetch_chunks (negative slots: not copied);
+ *                 also B*P < 2^31
+ *  host_staging   pinned host memory (hipHostMalloc) of stage_chunks chunks
+ *                 (2*Hkv*64*d bf16 each), owned by the caller
+ *  dev_staging    device memory of stage_chunks chunks, owned by the caller
+ *  stage_chunks   >= 2
+ *  side_stream    HIP stream the copies and the scatter kernels go on
+ * Unlike lsa_fetch_chunks the call waits on the host: before it refills a
+ * staging half for the copy out of it, and before it returns for every
+ * copy, so host_staging is the caller's again on return; side_stream must
+ * therefore not wait for work that is enqueued after the call.  dev_staging
+ * is read by the scatter kernels in side_stream's order: a later use on
+ * another stream waits for `done` or side_stream first.  Under graph
+ * capture it returns LSA_ERR_UNSUPPORTED.  Calls from several threads each
+ * need their own staging buffers; their gathers share the worker threads
+ * one call at a time.
+ */
+lsa_status lsa_fetch_chunks_staged(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,
+                                   const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
+                                   int32_t d, int32_t k, uint16_t* host_staging, uint16_t* dev_staging,
+                                   int64_t stage_chunks, hipStream_t side_stream, hipEvent_t done);
 
 /*
  * lsa_fetch_chunks_pull -- the same host-tier fetch as lsa_fetch_chunks, done

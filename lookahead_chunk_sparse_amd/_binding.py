@@ -25,7 +25,8 @@ CHUNK_TOKENS = 64
 # Every symbol include/lsa.h declares.
 EXPORTS = ("lsa_status_string", "lsa_last_error", "lsa_index_score", "lsa_topk_chunks", "lsa_threshold_chunks",
            "lsa_topk_tokens", "lsa_topk_tokens_workspace_size", "lsa_gather_attend_workspace_size", "lsa_gather_attend_default_splits",
-           "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_pull",
+           "lsa_gather_attend", "lsa_gather_attend_tokens", "lsa_fetch_chunks", "lsa_fetch_chunks_staged",
+           "lsa_fetch_chunks_pull",
            "lsa_pool_assign", "lsa_set_tuning", "lsa_get_tuning", "lsa_gather_attend_noalloc", "lsa_check_ids")
 
 # bytes of the static split-partials buffer of lsa_gather_attend_noalloc (LSA_NOALLOC_SCRATCH_BYTES)
@@ -88,6 +89,8 @@ def load_library(path: str = LIB_PATH):
     L.lsa_gather_attend_tokens.restype = ctypes.c_int
     L.lsa_fetch_chunks.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp]
     L.lsa_fetch_chunks.restype = ctypes.c_int
+    L.lsa_fetch_chunks_staged.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, i64, vp, vp]
+    L.lsa_fetch_chunks_staged.restype = ctypes.c_int
     L.lsa_fetch_chunks_pull.argtypes = [vp, i64, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp]
     L.lsa_fetch_chunks_pull.restype = ctypes.c_int
     L.lsa_pool_assign.argtypes = [vp, vp, i32, vp, i32, i32, i64, vp, vp, vp]
@@ -498,6 +501,53 @@ def lsa_fetch_chunks(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_k
         ev = done.cuda_event if hasattr(done, "cuda_event") else int(done)
     _check(load_library().lsa_fetch_chunks(_ptr(host_kv), C, _ptr(host_chunk_ids), _ptr(host_slots),
                                            _ptr(pool_kv), P, B, Hkv, d, k, _stream(stream), ev))
+
+
+def alloc_fetch_staging(host_kv: torch.Tensor, stage_chunks: int, device="cuda"):
+    """The two staging buffers of lsa_fetch_chunks_staged, each stage_chunks
+    chunks of host_kv's shape: (pinned host bf16, device bf16)
+    [stage_chunks][2][Hkv][64][d]."""
+    _, _, two, Hkv, T, d = host_kv.shape
+    shape = (int(stage_chunks), two, Hkv, T, d)
+    return (torch.empty(shape, dtype=torch.bfloat16, pin_memory=True),
+            torch.empty(shape, dtype=torch.bfloat16, device=device))
+
+
+def lsa_fetch_chunks_staged(host_kv: torch.Tensor, host_chunk_ids: torch.Tensor, pool_kv: torch.Tensor,
+                            host_staging: torch.Tensor, dev_staging: torch.Tensor,
+                            host_slots: torch.Tensor | None = None, stream=None, done=None):
+    """lsa_fetch_chunks through staging buffers (alloc_fetch_staging): the
+    host gathers the chunks to copy, which cross the link in large copies and
+    are scattered into the pool on the device.  Waits on the host for its
+    copies (so not under graph capture)."""
+    _need(host_kv, torch.bfloat16, "host_kv", 6)
+    _need(pool_kv, torch.bfloat16, "pool_kv", 6)
+    _need(host_chunk_ids, torch.int32, "host_chunk_ids", 2)
+    _need(host_staging, torch.bfloat16, "host_staging", 5)
+    _need(dev_staging, torch.bfloat16, "dev_staging", 5)
+    if host_chunk_ids.is_cuda or (host_slots is not None and host_slots.is_cuda):
+        raise ValueError("chunk ids and slots for the fetch must be host tensors")
+    B, C, _, Hkv, T, d = host_kv.shape
+    P = pool_kv.shape[1]
+    k = host_chunk_ids.shape[1]
+    n_stage = host_staging.shape[0]
+    if tuple(host_staging.shape[1:]) != tuple(host_kv.shape[2:]) or tuple(dev_staging.shape) != tuple(host_staging.shape):
+        raise ValueError("host_staging and dev_staging must both be [stage_chunks][2][Hkv][64][d] of host_kv's chunks")
+    _check_pool(host_kv, pool_kv)
+    if host_chunk_ids.shape[0] != B:
+        raise ValueError("host_chunk_ids batch size mismatch")
+    if host_slots is not None:
+        _need(host_slots, torch.int32, "host_slots", 2)
+        if tuple(host_slots.shape) != tuple(host_chunk_ids.shape):
+            raise ValueError("host_slots must have the shape of host_chunk_ids")
+    if host_staging.is_cuda or not dev_staging.is_cuda:
+        raise ValueError("host_staging must be pinned host memory and dev_staging device memory")
+    ev = 0
+    if done is not None:
+        ev = done.cuda_event if hasattr(done, "cuda_event") else int(done)
+    _check(load_library().lsa_fetch_chunks_staged(_ptr(host_kv), C, _ptr(host_chunk_ids), _ptr(host_slots),
+                                                  _ptr(pool_kv), P, B, Hkv, d, k, _ptr(host_staging),
+                                                  _ptr(dev_staging), n_stage, _stream(stream), ev))
 
 
 def lsa_fetch_chunks_pull(host_kv: torch.Tensor, chunk_ids: torch.Tensor, pool_kv: torch.Tensor,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblsa.so")
 SOURCES = ["lsa_abi.hip", "index_score.hip", "topk_chunks.hip", "gather_attend.hip", "fetch_pull.hip",
-           "pool_assign.hip", "noalloc.hip", "check_ids.hip"]
+           "pool_assign.hip", "noalloc.hip", "check_ids.hip", "fetch_staged.hip"]
 MEASURE_SOURCES = ["measure/tile_read.hip"]
 MEASURE_LIB_PATH = os.path.join(HERE, "libtileread.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,9 +9,12 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/lsa.h"
 #include "fetch_runs.h"
@@ -459,6 +462,115 @@ lsa_status lsa_fetch_chunks(const uint16_t* host_kv, int64_t C, const int32_t* h
     if (copy_err != hipSuccess) return hip_fail(copy_err, "fetch copy");
     if (done) {
         hipError_t e = hipEventRecord(done, side_stream);
+        if (e != hipSuccess) return hip_fail(e, "fetch event record");
+    }
+    return ok();
+}
+
+lsa_status lsa_fetch_chunks_staged(const uint16_t* host_kv, int64_t C, const int32_t* host_chunk_ids,
+                                   const int32_t* host_slots, uint16_t* pool_kv, int64_t P, int32_t B, int32_t Hkv,
+                                   int32_t d, int32_t k, uint16_t* host_staging, uint16_t* dev_staging,
+                                   int64_t stage_chunks, hipStream_t side_stream, hipEvent_t done) {
+    if (!host_kv || !host_chunk_ids || !pool_kv || !host_staging || !dev_staging)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv, host_chunk_ids, pool_kv and both staging buffers are required");
+    if (C < 1 || P < 1 || B < 1 || Hkv < 1 || d < 1 || k < 1)
+        return fail(LSA_ERR_INVALID_ARGUMENT, "C, P, B, Hkv, d, k must all be >= 1");
+    if (stage_chunks < 2) return fail(LSA_ERR_INVALID_ARGUMENT, "stage_chunks=%lld: at least 2", (long long)stage_chunks);
+    if (!host_slots && k > P) return fail(LSA_ERR_INVALID_ARGUMENT, "k=%d > P=%lld with default slots", k, (long long)P);
+    if ((int64_t)B * P >= ((int64_t)1 << 31) || (int64_t)B * C >= ((int64_t)1 << 40))
+        return fail(LSA_ERR_UNSUPPORTED, "B*P must be < 2^31 and B*C < 2^40");
+    if (!aligned(host_kv, 16) || !aligned(pool_kv, 16) || !aligned(host_staging, 16) || !aligned(dev_staging, 16))
+        return fail(LSA_ERR_INVALID_ARGUMENT, "host_kv, pool_kv and the staging buffers need 16-byte alignment");
+    for (int64_t e = 0; e < (int64_t)B * k; ++e) {
+        if (host_slots && host_slots[e] < 0) continue;  // not copied: its id is not read
+        if (host_chunk_ids[e] < 0 || host_chunk_ids[e] >= C)
+            return fail(LSA_ERR_INVALID_ARGUMENT, "chunk id %d at entry %lld outside [0, %lld)", host_chunk_ids[e],
+                        (long long)e, (long long)C);
+        if (host_slots && host_slots[e] >= P)
+            return fail(LSA_ERR_INVALID_ARGUMENT, "slot %d at entry %lld outside [0, %lld)", host_slots[e],
+                        (long long)e, (long long)P);
+    }
+    // both host buffers pinned (the staging buffer is read by asynchronous
+    // DMA, the store is read by the gather threads), the staging on the
+    // device in device memory
+    for (const void* hp : {(const void*)host_kv, (const void*)host_staging}) {
+        hipPointerAttribute_t attr;
+        memset(&attr, 0, sizeof attr);
+        const hipError_t pe = hipPointerGetAttributes(&attr, hp);
+        if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return fail(LSA_ERR_INVALID_ARGUMENT,
+                        "host_kv and host_staging must be pinned host memory (allocate them with hipHostMalloc)");
+        }
+    }
+    {
+        hipPointerAttribute_t attr;
+        memset(&attr, 0, sizeof attr);
+        const hipError_t pe = hipPointerGetAttributes(&attr, dev_staging);
+        if (pe != hipSuccess || attr.type != hipMemoryTypeDevice) {
+            (void)hipGetLastError();
+            return fail(LSA_ERR_INVALID_ARGUMENT, "dev_staging must be device memory");
+        }
+    }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    const hipError_t ce = hipStreamIsCapturing(side_stream, &cap);
+    if (ce != hipSuccess) return hip_fail(ce, "capture status");
+    if (cap != hipStreamCaptureStatusNone)
+        return fail(LSA_ERR_UNSUPPORTED, "the staged fetch waits on the host for its copies: not under graph capture");
+
+    const size_t chunk_bytes = (size_t)2 * Hkv * lsa::kChunkTokens * d * sizeof(uint16_t);
+    // the entries to copy: store chunk b * C + id into pool chunk b * P + slot
+    std::vector<int64_t> src;
+    std::vector<int32_t> dst;
+    src.reserve((size_t)B * k);
+    dst.reserve((size_t)B * k);
+    for (int32_t b = 0; b < B; ++b)
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t e = (int64_t)b * k + j;
+            const int32_t slot = host_slots ? host_slots[e] : j;
+            if (slot < 0) continue;
+            src.push_back((int64_t)b * C + host_chunk_ids[e]);
+            dst.push_back((int32_t)((int64_t)b * P + slot));
+        }
+    // Pieces of up to `piece` chunks alternate between the two halves of the
+    // staging buffers: the host gathers piece p + 1 while piece p crosses
+    // the link, and waits for the copy out of a half before filling it again.
+    const int64_t piece = std::min<int64_t>(stage_chunks / 2, lsa::kStagePiece);
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    bool used[2] = {false, false};
+    hipError_t err = hipSuccess;
+    for (int h = 0; h < 2 && err == hipSuccess; ++h) err = hipEventCreateWithFlags(&ev[h], hipEventDisableTiming);
+    int h = 0;
+    for (size_t p0 = 0; p0 < src.size() && err == hipSuccess; p0 += (size_t)piece, h ^= 1) {
+        const int n = (int)std::min<size_t>((size_t)piece, src.size() - p0);
+        if (used[h] && (err = hipEventSynchronize(ev[h])) != hipSuccess) break;
+        char* hs = reinterpret_cast<char*>(host_staging) + (size_t)h * piece * chunk_bytes;
+        char* ds = reinterpret_cast<char*>(dev_staging) + (size_t)h * piece * chunk_bytes;
+        lsa::host_gather_chunks(hs, reinterpret_cast<const char*>(host_kv), src.data() + p0, n, chunk_bytes);
+        if ((err = hipMemcpyAsync(ds, hs, (size_t)n * chunk_bytes, hipMemcpyHostToDevice, side_stream)) != hipSuccess)
+            break;
+        if ((err = hipEventRecord(ev[h], side_stream)) != hipSuccess) break;
+        used[h] = true;
+        lsa::StageScatterArgs sa{};
+        sa.src = reinterpret_cast<const uint16_t*>(ds);
+        sa.pool = pool_kv;
+        sa.chunk_u4 = (int64_t)(chunk_bytes / 16);
+        sa.n = n;
+        for (int i = 0; i < n; ++i) sa.dst[i] = dst[p0 + i];
+        err = lsa::launch_stage_scatter(sa, side_stream);
+    }
+    // the host staging buffer is the caller's again once every copy out of it
+    // has finished (also after a failure, so no copy still reads it)
+    for (int hh = 0; hh < 2; ++hh) {
+        if (used[hh]) {
+            const hipError_t e = hipEventSynchronize(ev[hh]);
+            if (err == hipSuccess) err = e;
+        }
+        if (ev[hh]) (void)hipEventDestroy(ev[hh]);
+    }
+    if (err != hipSuccess) return hip_fail(err, "staged fetch");
+    if (done) {
+        const hipError_t e = hipEventRecord(done, side_stream);
         if (e != hipSuccess) return hip_fail(e, "fetch event record");
     }
     return ok();

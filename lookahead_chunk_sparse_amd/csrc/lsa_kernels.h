@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <functional>
+
 #include "../../include/lsa.h"
 
 namespace lsa {
@@ -76,6 +78,25 @@ hipError_t launch_gather_attend(const AttendArgs& a, hipStream_t stream);
 // ---- host-tier fetch as a device-side gather over the host link ----
 hipError_t launch_fetch_pull(const uint16_t* host_kv_dev, int64_t C, const int32_t* ids, const int32_t* slots,
                              uint16_t* pool, int64_t P, int B, int Hkv, int d, int k, int grid, hipStream_t stream);
+
+// ---- host-tier fetch through a staging buffer ----
+// Chunks per staged copy: the scatter's destination list rides in its kernel
+// arguments (4 bytes a chunk).
+constexpr int kStagePiece = 512;
+struct StageScatterArgs {
+    const uint16_t* src;  // device staging: n consecutive chunks
+    uint16_t* pool;       // [B][P] chunks
+    int64_t chunk_u4;     // 16-byte words per chunk (16 * Hkv * d)
+    int n;                // chunks staged
+    int32_t dst[kStagePiece];  // pool chunk b * P + slot of staged chunk s
+};
+hipError_t launch_stage_scatter(const StageScatterArgs& a, hipStream_t stream);
+// Runs fn(i) for every i in [0, n) on the library's host worker threads and
+// the calling thread; returns when all have run.  One job at a time.
+void host_parallel_for(int n, const std::function<void(int)>& fn);
+// Copies host chunks src_chunks[0..n) of `store` (chunk_bytes each, a
+// multiple of 64) to consecutive places of dst, on those threads.
+void host_gather_chunks(char* dst, const char* store, const int64_t* src_chunks, int n, size_t chunk_bytes);
 
 // ---- opt-in validation of chunk lists ----
 constexpr int kCheckMaxEntries = 16384;  // entries per request the check sorts in LDS

@@ -19,7 +19,11 @@ Two placements of the K/V:
     the selected ids on the GPU (fetch="pull", the default: no host round
     trip, graph-capturable) or DMA copies issued from the host, spread over
     several copy streams (fetch="memcpy": the ids, and the slots, are copied
-    to the host first; the copies use no compute unit).
+    to the host first; the copies use no compute unit), or the same DMA
+    through a staging buffer (fetch="staged": the host gathers the chunks to
+    fetch, which cross the link in large copies and are scattered into the
+    pool on the device; the host waits for its copies, so not under graph
+    capture).
     With delta=True (the default) one pool of 2k slots replaces the two
     buffers: chunks selected again keep their slot and only new chunks are
     copied, into slots the selection being attended over does not hold.
@@ -53,9 +57,9 @@ import math
 
 import torch
 
-from ._binding import (CHUNK_TOKENS, alloc_topk_tokens_workspace, alloc_workspace, lsa_fetch_chunks,
-                       lsa_fetch_chunks_pull, lsa_gather_attend, lsa_index_score, lsa_pool_assign, lsa_threshold_chunks,
-                       lsa_topk_chunks, lsa_topk_tokens)
+from ._binding import (CHUNK_TOKENS, alloc_fetch_staging, alloc_topk_tokens_workspace, alloc_workspace,
+                       lsa_fetch_chunks, lsa_fetch_chunks_pull, lsa_fetch_chunks_staged, lsa_gather_attend,
+                       lsa_index_score, lsa_pool_assign, lsa_threshold_chunks, lsa_topk_chunks, lsa_topk_tokens)
 
 TAU = 64
 
@@ -81,7 +85,7 @@ class LsaDecoder:
                  n_split: int = 0, sm_scale: float | None = None, fetch: str = "pull", fetch_grid: int = 0,
                  delta: bool | None = None, selection: str = "topk", logit_threshold: int = 0,
                  seg_kv: torch.Tensor | None = None, seg_len: torch.Tensor | None = None, token_topk: int = 0,
-                 device="cuda"):
+                 stage_chunks: int = 1024, device="cuda"):
         if (kv is None) == (host_kv is None):
             raise ValueError("give exactly one of kv (HBM store) or host_kv (host tier)")
         self.k_idx = k_idx
@@ -111,16 +115,16 @@ class LsaDecoder:
         # busy all interval (a drifting query, or full re-fetches) 4x the
         # splits balance around the fetch workgroups only 1-2% better.
         self.n_split = n_split
-        if fetch not in ("pull", "memcpy"):
-            raise ValueError("fetch must be 'pull' or 'memcpy'")
+        if fetch not in ("pull", "memcpy", "staged"):
+            raise ValueError("fetch must be 'pull', 'memcpy' or 'staged'")
         self.fetch, self.fetch_grid = fetch, fetch_grid
         if selection not in ("topk", "threshold"):
             raise ValueError("selection must be 'topk' or 'threshold'")
         self.selection, self.logit_threshold = selection, int(logit_threshold)
         self.delta = True if delta is None else bool(delta)
-        if selection == "threshold" and host_kv is not None and fetch == "memcpy" and not self.delta:
+        if selection == "threshold" and host_kv is not None and fetch != "pull" and not self.delta:
             # the -1 padding past a request's count is skipped through its slot (-1)
-            raise NotImplementedError("threshold selection with fetch='memcpy' on the host tier needs delta=True")
+            raise NotImplementedError(f"threshold selection with fetch='{fetch}' on the host tier needs delta=True")
         self.sm_scale = 1.0 / math.sqrt(self.d) if sm_scale is None else sm_scale
         dev = torch.device(device)
         B = self.B
@@ -157,7 +161,11 @@ class LsaDecoder:
             self.slots = torch.arange(k, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
             self.host_ids = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)]
             self.host_slots = [torch.empty((B, k), dtype=torch.int32).pin_memory() for _ in range(2)] \
-                if self.delta and fetch == "memcpy" else None
+                if self.delta and fetch != "pull" else None
+            # the staged fetch's buffers (two halves of stage_chunks / 2 chunks
+            # each, the size of one copy over the link)
+            self.staging = alloc_fetch_staging(host_kv, max(2, min(int(stage_chunks), 2 * B * k)), device=dev) \
+                if fetch == "staged" else None
             self.side = torch.cuda.Stream(device=dev)
             self.ev_ids = torch.cuda.Event()
             self.ev_sel = torch.cuda.Event()
@@ -230,7 +238,7 @@ class LsaDecoder:
             prev = (self.sel_ids[(i - 1) % 2], self.sel_slots[(i - 1) % 2]) if i >= 1 else (None, None)
             lsa_pool_assign(prev[0], prev[1], self.sel_ids[i % 2], 2 * self.k, new_slots=self.sel_slots[i % 2],
                             fetch_slots=self.fetch_slots[i % 2])
-        if self.fetch == "memcpy":
+        if self.fetch != "pull":
             self.host_ids[i % 2].copy_(self.sel_ids[i % 2], non_blocking=True)
             if self.delta:
                 self.host_slots[i % 2].copy_(self.fetch_slots[i % 2], non_blocking=True)
@@ -263,12 +271,16 @@ class LsaDecoder:
         if timing:
             ev0 = torch.cuda.Event(enable_timing=True)
             ev0.record(self.side)
-        if self.fetch == "memcpy":
+        if self.fetch != "pull":
             self.ev_ids.synchronize()  # the ids (and slots) must be on the host before the copies are issued
+            slots = self.host_slots[i % 2] if self.delta else None
             for host, pool in zip(self.host_layers or [self.host_kv], self.pools):
-                lsa_fetch_chunks(host, self.host_ids[i % 2], pool[i % 2],
-                                 host_slots=self.host_slots[i % 2] if self.delta else None, stream=self.side,
-                                 done=None)
+                if self.fetch == "staged":
+                    lsa_fetch_chunks_staged(host, self.host_ids[i % 2], pool[i % 2], *self.staging,
+                                            host_slots=slots, stream=self.side)
+                else:
+                    lsa_fetch_chunks(host, self.host_ids[i % 2], pool[i % 2], host_slots=slots, stream=self.side,
+                                     done=None)
         else:
             self.side.wait_event(self.ev_sel)  # selection i (and its slots) are on the device
             for host, pool in zip(self.host_layers or [self.host_kv], self.pools):

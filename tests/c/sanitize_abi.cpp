@@ -87,6 +87,26 @@ static void rejected_calls() {
     CHECK(strstr(lsa_last_error(), "99") == nullptr);
     CHECK(lsa_fetch_chunks(host.data(), 10, ids.data(), nullptr, pool, 2, 2, 1, 64, 3, nullptr, nullptr) ==
           LSA_ERR_INVALID_ARGUMENT);
+    // the staged fetch: staging buffers required, at least 2 chunks of them,
+    // the same id and slot checks, and pageable host memory refused
+    uint16_t* stage = const_cast<uint16_t*>(U16);
+    CHECK(lsa_fetch_chunks_staged(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, nullptr, stage, 4,
+                                  nullptr, nullptr) == LSA_ERR_INVALID_ARGUMENT);
+    CHECK(lsa_fetch_chunks_staged(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, stage, stage, 1,
+                                  nullptr, nullptr) == LSA_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(lsa_last_error(), "stage_chunks") != nullptr);
+    CHECK(lsa_fetch_chunks_staged(host.data(), 10, ids.data(), slots.data(), pool, 1 << 30, 4, 1, 64, 1, stage, stage,
+                                  4, nullptr, nullptr) == LSA_ERR_UNSUPPORTED);
+    ids[4] = 4;
+    slots[4] = 3;  // a slot past the pool
+    CHECK(lsa_fetch_chunks_staged(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, stage, stage, 4,
+                                  nullptr, nullptr) == LSA_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(lsa_last_error(), "slot 3") != nullptr);
+    slots[4] = -1;  // not copied: its id 99 is not read; the pageable store is refused next
+    ids[4] = 99;
+    CHECK(lsa_fetch_chunks_staged(host.data(), 10, ids.data(), slots.data(), pool, 3, 2, 1, 64, 3, stage, stage, 4,
+                                  nullptr, nullptr) == LSA_ERR_INVALID_ARGUMENT);
+    CHECK(strstr(lsa_last_error(), "pinned") != nullptr);
     for (int32_t s : {0, 1, 2, 3, 4, 5, -1, 99, INT32_MIN}) CHECK(lsa_status_string(s) != nullptr);
     CHECK(strcmp(lsa_status_string(99), "LSA_ERR_UNKNOWN") == 0);
 }

@@ -149,6 +149,18 @@ def test_fetch_pool_must_match_host_store(lsa, no_lib, pool_shape):
         lsa.lsa_fetch_chunks_pull(host, _i32(2, 4), pool)
 
 
+def test_fetch_staged_checks_staging(lsa, no_lib):
+    """The staging buffers must hold chunks of the store's shape, the host one
+    on the host and the device one on the device."""
+    host, pool = _bf16(2, 9, 2, 2, 64, 64), _bf16(2, 6, 2, 2, 64, 64)
+    with pytest.raises(ValueError, match="staging"):
+        lsa.lsa_fetch_chunks_staged(host, _i32(2, 4), pool.to("meta"), _bf16(4, 2, 2, 64, 32), _bf16(4, 2, 2, 64, 32))
+    with pytest.raises(ValueError):
+        lsa.lsa_fetch_chunks_staged(host, _i32(2, 4), pool, _bf16(4, 2, 2, 64, 64), _bf16(4, 2, 2, 64, 64))
+    with pytest.raises(TypeError):
+        lsa.lsa_fetch_chunks_staged(host, _i32(2, 4), pool, _bf16(4, 2, 2, 64, 64), _i32(4, 2, 2, 64, 64))
+
+
 # ---- tuning knobs ---------------------------------------------------------
 
 def test_tuning_defaults_and_overrides(lsa):

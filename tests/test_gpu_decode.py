@@ -52,7 +52,8 @@ def oracle_output(oracle, W, w, t, b, ids_b):
                                               ("1m_host", "pull", False), ("1m_host", "memcpy", False),
                                               ("1m_host", "memcpy", True), ("128k_host", "pull", True),
                                               ("128k_host", "memcpy", True), ("32k_churn", "pull", True),
-                                              ("32k_churn", "memcpy", True)])
+                                              ("32k_churn", "memcpy", True), ("32k_churn", "staged", True),
+                                              ("1m_host", "staged", True), ("128k_host", "staged", False)])
 def test_decode_workload(oracle_lib, name, fetch, delta):
     import torch
 

@@ -113,10 +113,11 @@ def _run_threshold_host(oracle_lib, w, n_intervals, n_rel, steps_per_interval, c
         assert np.array_equal(pool[b][slots[b, :n]], W.kv_chunks(w, b, ids[b, :n])), f"pool of request {b}"
 
 
-@pytest.mark.parametrize("delta,fetch", [(True, "pull"), (False, "pull"), (True, "memcpy")])
+@pytest.mark.parametrize("delta,fetch", [(True, "pull"), (False, "pull"), (True, "memcpy"), (True, "staged")])
 def test_threshold_selection_host_tier_32k(oracle_lib, delta, fetch):
     """With fetch='memcpy' the DMA copies skip the -1 padding through its
-    slot (-1) and spread over the library's copy streams."""
+    slot (-1) and spread over the library's copy streams; with 'staged' the
+    host gathers only the entries with a slot."""
     from synth import workloads as W
     w = W.WORKLOADS["32k"].replace(B=4, k=64, host_tier=True)
     table = [[5, 20, 90, 0], [0, 40, 3, 90], [64, 1, 0, 30], [12, 0, 70, 64]]  # 90 > k: capped

@@ -603,6 +603,63 @@ def test_fetch_concurrent_threads_byte_exact(lsa, oracle_lib, synth_lib):
         assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("stage,Hkv,d", [(2, 2, 64), (5, 2, 64), (64, 2, 64), (8, 8, 128)])
+def test_fetch_staged_byte_exact(lsa, oracle_lib, synth_lib, stage, Hkv, d):
+    """The staged fetch (host gather into pinned staging, large copies,
+    scatter into the pool on the device) leaves the oracle's bytes in the
+    pool: pieces of stage // 2 chunks (one chunk at a time for stage 2 and
+    3), entries with a negative slot leave their slots as they were, two
+    calls in a row reuse the staging buffers, and default slots put entry j
+    at slot j."""
+    import torch
+    B, C, k, P = 2, 64, 24, 48
+    host = synth_lib.normal_bf16((B, C, 2, Hkv, 64, d), 29, synth_lib.stream(synth_lib.TAG_MISC, 980 + stage))
+    host_t = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).pin_memory()
+    staging = lsa.alloc_fetch_staging(host_t, stage)
+    rng = np.random.default_rng(980 + stage)
+    one = np.uint16(0x3F80)  # bf16 1.0
+    pool = torch.full((B, P, 2, Hkv, 64, d), 1.0, dtype=torch.bfloat16, device="cuda")
+    want = np.full(tuple(pool.shape), one, dtype=np.uint16)
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        ids = np.stack([np.sort(rng.choice(C, k, replace=False)) for _ in range(B)]).astype(np.int32)
+        slots = np.stack([rng.choice(P, k, replace=False) for _ in range(B)]).astype(np.int32)
+        slots[:, rep::4] = -1  # not copied
+        lsa.lsa_fetch_chunks_staged(host_t, torch.from_numpy(ids), pool, *staging,
+                                    host_slots=torch.from_numpy(slots), stream=side)
+        side.synchronize()
+        want = oracle_lib.fetch_chunks(host, ids, P, slots=slots, pool=want, skip_negative_slots=True)
+        assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), want), rep
+    pool2 = torch.zeros((B, k, 2, Hkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    ev = torch.cuda.Event()
+    ev.record(side)  # create the event before handing it to the library
+    lsa.lsa_fetch_chunks_staged(host_t, torch.from_numpy(ids), pool2, *staging, stream=side, done=ev)
+    ev.synchronize()
+    assert np.array_equal(pool2.cpu().view(torch.int16).numpy().view(np.uint16), oracle_lib.fetch_chunks(host, ids, k))
+
+
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
+def test_fetch_staged_rejects(lsa):
+    """Pageable staging memory and graph capture are refused before any copy
+    (the call waits on the host for its copies)."""
+    import torch
+    host = torch.zeros((1, 4, 2, 1, 64, 64), dtype=torch.bfloat16).pin_memory()
+    pool = torch.zeros((1, 2, 2, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.tensor([[0, 3]], dtype=torch.int32)
+    host_stage, dev_stage = lsa.alloc_fetch_staging(host, 4)
+    with pytest.raises(lsa.LsaError, match="pinned"):
+        lsa.lsa_fetch_chunks_staged(host, ids, pool, torch.zeros(tuple(host_stage.shape), dtype=torch.bfloat16),
+                                    dev_stage)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with pytest.raises(lsa.LsaError, match="capture"):
+            with torch.cuda.graph(g, stream=s):
+                lsa.lsa_fetch_chunks_staged(host, ids, pool, host_stage, dev_stage, stream=s)
+    torch.cuda.synchronize()
+
+
 def test_fetch_pull_byte_exact(lsa, oracle_lib, synth_lib):
     """The device-side gather: same pool bytes as the oracle's copy; entries
     with an id or slot out of range are skipped and leave their slot as it was."""
