@@ -510,6 +510,34 @@ def test_attend_tokens_parity(lsa, oracle_lib, synth_lib, B, Hq, Hkv, d, C, k, k
     say("  ", check_attention(out.cpu().numpy(), ref, "token attend"))
 
 
+@pytest.mark.parametrize("n_split,seg_n", [(2, 0), (4, 0), (7, 0), (3, 256), (5, 128)])
+def test_attend_tokens_counts_move_split_start(lsa, oracle_lib, synth_lib, n_split, seg_n):
+    """Token counts far below the list length (down to 0 and 1) and partly
+    filled segments, over several split counts: many splits start at another
+    block than a full list and a full segment would give them, and some hold
+    only segment blocks or nothing."""
+    B, Hq, Hkv, d, C, k, k_tok = 5, 64, 8, 128, 40, 16, 900
+    q, kv = _problem(synth_lib, B, Hq, Hkv, d, C, seed=90 + n_split, qscale=4.0)
+    ids = _ids(synth_lib, B, C, k, seed=91)
+    ctx = np.full(B, C * 64, dtype=np.int32)
+    rng = np.random.default_rng(92 + n_split)
+    tok = np.stack([rng.permutation(k * 64)[:k_tok] for _ in range(B)]).astype(np.int32)
+    # request 3 lists no token when its segment gives it some (the oracle's
+    # softmax needs at least one usable token per request)
+    tok_counts = np.array([k_tok, k_tok // 3, 1, 0 if seg_n else 2, 450], dtype=np.int32)
+    kw, seg, seg_len = {}, None, None
+    if seg_n:
+        seg = synth_lib.normal_bf16((B, 2, Hkv, seg_n, d), 93, synth_lib.stream(synth_lib.TAG_MISC, 4030))
+        seg_len = np.array([seg_n, seg_n // 2, 1, 17, 0], dtype=np.int32)
+        kw = dict(seg_kv=to_dev_bf16(seg), seg_len=to_dev(seg_len))
+    say("token attend counts", n_split, seg_n, tok_counts.tolist())
+    out = lsa.lsa_gather_attend_tokens(to_dev_bf16(q), to_dev_bf16(kv), to_dev(ids), to_dev(ctx), to_dev(tok),
+                                       to_dev(tok_counts), sm_scale=1 / math.sqrt(d), n_split=n_split, **kw)
+    ref = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 1 / math.sqrt(d), tok=tok, tok_counts=tok_counts,
+                                   seg_kv=seg, seg_len=seg_len)
+    say("  ", check_attention(out.cpu().numpy(), ref, "token attend counts"))
+
+
 def test_attend_tokens_all_listed_equals_chunk_attention(lsa, synth_lib):
     """Listing every token of the chunks reproduces chunk attention up to
     rounding order (same tokens, blocks of 64 listed rows instead of tiles)."""
