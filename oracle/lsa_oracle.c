@@ -96,18 +96,28 @@ void oracle_index_scores(const int64_t* logits, int64_t n, float alpha, double* 
  *    Returns 0, or -1 if k is out of [1, C]. */
 int oracle_topk_i64(const int64_t* keys, int64_t R, int64_t C, int64_t k, int32_t* ids) {
     if (k < 1 || k > C) return -1;
-    for (int64_t r = 0; r < R; ++r) {
+    unsigned char* keep = (unsigned char*)malloc((size_t)C);
+    int status = 0;
+    for (int64_t r = 0; r < R && status == 0; ++r) {
         const int64_t* row = keys + r * C;
-        int64_t n_out = 0;
+        /* each chunk's rank is counted on its own, so the counts run in
+         * parallel; the kept chunks are then listed in ascending order */
+#pragma omp parallel for schedule(dynamic, 64)
         for (int64_t c = 0; c < C; ++c) {
             int64_t before = 0;
             for (int64_t c2 = 0; c2 < C; ++c2)
                 if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;
-            if (before < k) ids[r * k + n_out++] = (int32_t)c;
+            keep[c] = before < k;
         }
-        if (n_out != k) return -2; /* cannot happen: the order is total */
+        int64_t n_out = 0;
+        for (int64_t c = 0; c < C; ++c) n_out += keep[c];
+        if (n_out != k) status = -2; /* cannot happen: the order is total */
+        n_out = 0;
+        for (int64_t c = 0; c < C && status == 0; ++c)
+            if (keep[c]) ids[r * k + n_out++] = (int32_t)c;
     }
-    return 0;
+    free(keep);
+    return status;
 }
 
 /* Same rule on double keys (used to compare selection by score with
@@ -353,33 +363,36 @@ int oracle_topk_tokens(const float* scores, const int32_t* chunk_ids, const int3
     if (B < 1 || k < 1 || T < 1 || k_tok < 1) return -1;
     const int64_t n = k * T;
     int status = 0;
-#pragma omp parallel for schedule(dynamic)
+    unsigned char* usable = (unsigned char*)malloc((size_t)n);
+    unsigned char* keep = (unsigned char*)malloc((size_t)n);
     for (int64_t b = 0; b < B; ++b) {
         const float* row = scores + b * n;
         const int64_t kb = counts ? (counts[b] < 0 ? 0 : counts[b] < k ? counts[b] : k) : k;
-        unsigned char* usable = (unsigned char*)malloc((size_t)n);
         int64_t n_use = 0;
         for (int64_t p = 0; p < n; ++p) {
             const int64_t j = p / T, t = p % T;
             usable[p] = j < kb && (int64_t)chunk_ids[b * k + j] * T + t < (int64_t)ctx_len[b];
-            if (usable[p] && isnan(row[p])) {
-#pragma omp atomic write
-                status = -1;
-            }
+            if (usable[p] && isnan(row[p])) status = -1;
             n_use += usable[p];
         }
         const int64_t kt = k_tok < n_use ? k_tok : n_use;
-        int64_t n_out = 0;
+        /* each usable position's rank is counted on its own, so the counts
+         * run in parallel; the kept positions are then listed in order */
+#pragma omp parallel for schedule(dynamic, 64)
         for (int64_t p = 0; p < n; ++p) {
-            if (!usable[p]) continue;
             int64_t before = 0;
-            for (int64_t p2 = 0; p2 < n; ++p2)
-                if (usable[p2] && (row[p2] > row[p] || (row[p2] == row[p] && p2 < p))) ++before;
-            if (before < kt) tok[b * k_tok + n_out++] = (int32_t)p;
+            if (usable[p])
+                for (int64_t p2 = 0; p2 < n; ++p2)
+                    if (usable[p2] && (row[p2] > row[p] || (row[p2] == row[p] && p2 < p))) ++before;
+            keep[p] = usable[p] && before < kt;
         }
+        int64_t n_out = 0;
+        for (int64_t p = 0; p < n; ++p)  /* at most kt, unless a NaN broke the order */
+            if (keep[p] && n_out < k_tok) tok[b * k_tok + n_out++] = (int32_t)p;
         for (int64_t u = n_out; u < k_tok; ++u) tok[b * k_tok + u] = -1;
         tok_counts[b] = (int32_t)n_out;
-        free(usable);
     }
+    free(usable);
+    free(keep);
     return status;
 }

@@ -175,6 +175,55 @@ def test_fetch_validation(lib):
     assert f(BOGUS, 8, ids.ctypes.data, 0, BOGUS, 1, 1, 1, 64, 2, 0, 0) == 1 and "k=2 > P=1" in _err(lib)
 
 
+def test_fetch_staged_validation(lib):
+    """Argument errors of the staged fetch are reported before any HIP call:
+    missing buffers, a staging buffer of fewer than 2 chunks, ids and slots
+    out of range (an entry with a negative slot is skipped, so its id is not
+    checked), k above P with default slots, misaligned buffers."""
+    import numpy as np
+    f = lib.lsa_fetch_chunks_staged
+    ids = np.array([[0, 5]], dtype=np.int32)
+    bad = np.array([[0, 9]], dtype=np.int32)
+    slots_bad = np.array([[0, 3]], dtype=np.int32)
+    # host_kv, C, ids, slots, pool, P, B, Hkv, d, k, host_staging, dev_staging, stage_chunks, stream, event
+    args = [BOGUS, 8, ids.ctypes.data, 0, BOGUS, 2, 1, 1, 64, 2, BOGUS, BOGUS, 4, 0, 0]
+
+    def call(**over):
+        a = list(args)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    for i in (0, 2, 4, 10, 11):  # a required pointer missing
+        assert call(**{f"a{i}": 0}) == 1 and "required" in _err(lib), i
+    assert call(a12=1) == 1 and "stage_chunks=1" in _err(lib)
+    assert call(a2=bad.ctypes.data) == 1 and "chunk id 9" in _err(lib)
+    assert call(a3=slots_bad.ctypes.data) == 1 and "slot 3" in _err(lib)
+    assert call(a5=1) == 1 and "k=2 > P=1" in _err(lib)
+    assert call(a10=BOGUS + 8) == 1 and "alignment" in _err(lib)
+    assert call(a7=0) == 1  # Hkv < 1
+    # the id past C sits at an entry whose slot is negative: not read, so the
+    # next check (pinned host memory) is the one that fails
+    skip = np.array([[0, -1]], dtype=np.int32)
+    assert call(a2=bad.ctypes.data, a3=skip.ctypes.data) == 1 and "chunk id" not in _err(lib)
+
+
+def test_fetch_pull_validation(lib):
+    """Argument errors of the pull fetch, reported before any HIP call."""
+    import numpy as np
+    f = lib.lsa_fetch_chunks_pull
+    ids = np.array([[0, 5]], dtype=np.int32)
+    # host_kv, C, ids, slots, pool, P, B, Hkv, d, k, grid, stream
+    assert f(0, 8, BOGUS, 0, BOGUS, 2, 1, 1, 64, 2, 0, 0) == 1 and "required" in _err(lib)
+    assert f(BOGUS, 8, BOGUS, 0, BOGUS, 2, 1, 1, 64, 2, -1, 0) == 1
+    assert f(BOGUS, 8, BOGUS, 0, BOGUS, 2, 1, 1, 64, 2, 1 << 24, 0) == 1
+    assert f(BOGUS, 8, BOGUS, 0, BOGUS, 2, 1, 1, 96, 2, 0, 0) == 2 and "d=96" in _err(lib)
+    assert f(BOGUS, 8, BOGUS, 0, BOGUS, 1, 1, 1, 64, 2, 0, 0) == 1 and "k=2 > P=1" in _err(lib)
+    assert f(BOGUS + 8, 8, BOGUS, 0, BOGUS, 2, 1, 1, 64, 2, 0, 0) == 1 and "alignment" in _err(lib)
+    assert f(BOGUS, 8, BOGUS + 2, 0, BOGUS, 2, 1, 1, 64, 2, 0, 0) == 1 and "alignment" in _err(lib)
+    del ids
+
+
 def test_python_binding_checks_dtypes(lsa):
     import torch
     with pytest.raises(TypeError):

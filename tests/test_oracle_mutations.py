@@ -25,11 +25,11 @@ MUTATIONS = [
      ["test_scores_closed_form_and_expit"]),
     ("sigmoid argument not fp32", "volatile float x = alpha * xl; /* one single-precision product */",
      "volatile double x = (double)alpha * (double)logits[j];", ["test_scores_argument_is_fp32_product"]),
-    ("top-k tie to higher index", "if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            if (before < k) ids[r * k + n_out++] = (int32_t)c;\n        }\n        if (n_out != k) return -2; /* cannot happen: the order is total */",
-     "if (row[c2] > row[c] || (row[c2] == row[c] && c2 > c)) ++before;\n            if (before < k) ids[r * k + n_out++] = (int32_t)c;\n        }\n        if (n_out != k) return -2; /* cannot happen: the order is total */",
+    ("top-k tie to higher index", "if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            keep[c] = before < k;",
+     "if (row[c2] > row[c] || (row[c2] == row[c] && c2 > c)) ++before;\n            keep[c] = before < k;",
      ["test_topk_vs_brute_force", "test_topk_closed_form"]),
-    ("top-k ascending order", "if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            if (before < k) ids[r * k + n_out++] = (int32_t)c;\n        }\n        if (n_out != k) return -2; /* cannot happen: the order is total */",
-     "if (row[c2] < row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            if (before < k) ids[r * k + n_out++] = (int32_t)c;\n        }\n        if (n_out != k) return -2; /* cannot happen: the order is total */",
+    ("top-k ascending order", "if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            keep[c] = before < k;",
+     "if (row[c2] < row[c] || (row[c2] == row[c] && c2 < c)) ++before;\n            keep[c] = before < k;",
      ["test_topk_vs_brute_force", "test_topk_closed_form"]),
     ("GQA head mapping", "const int64_t g = h / group;", "const int64_t g = h % Hkv;",
      ["test_all_chunks_equals_dense_sdpa", "test_convex_hull_and_gqa_as_mha"]),
