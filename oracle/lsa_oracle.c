@@ -330,23 +330,34 @@ int oracle_pool_assign(const int32_t* prev_ids, const int32_t* prev_slots, int64
 int oracle_threshold_i64(const int64_t* keys, int64_t R, int64_t C, int64_t thr, int64_t k_max, int32_t* ids,
                          int32_t* counts) {
     if (k_max < 1 || k_max > C) return -1;
-    for (int64_t r = 0; r < R; ++r) {
+    unsigned char* keep = (unsigned char*)malloc((size_t)C);
+    int status = 0;
+    for (int64_t r = 0; r < R && status == 0; ++r) {
         const int64_t* row = keys + r * C;
         int64_t above = 0;
         for (int64_t c = 0; c < C; ++c) above += row[c] > thr;
         const int64_t kk = above < k_max ? above : k_max;
-        int64_t n_out = 0;
+        /* ranks counted in parallel iterations, as in item 3 */
+#pragma omp parallel for schedule(dynamic, 64)
         for (int64_t c = 0; c < C; ++c) {
             int64_t before = 0;
             for (int64_t c2 = 0; c2 < C; ++c2)
                 if (row[c2] > row[c] || (row[c2] == row[c] && c2 < c)) ++before;
-            if (before < kk) ids[r * k_max + n_out++] = (int32_t)c;
+            keep[c] = before < kk;
         }
-        if (n_out != kk) return -2;
-        for (int64_t j = n_out; j < k_max; ++j) ids[r * k_max + j] = -1;
-        counts[r] = (int32_t)kk;
+        int64_t n_out = 0;
+        for (int64_t c = 0; c < C; ++c) n_out += keep[c];
+        if (n_out != kk) status = -2;
+        n_out = 0;
+        for (int64_t c = 0; c < C && status == 0; ++c)
+            if (keep[c]) ids[r * k_max + n_out++] = (int32_t)c;
+        if (status == 0) {
+            for (int64_t j = n_out; j < k_max; ++j) ids[r * k_max + j] = -1;
+            counts[r] = (int32_t)kk;
+        }
     }
-    return 0;
+    free(keep);
+    return status;
 }
 
 /* 8. Token selection inside the recalled chunks.  List position p = j*T + t
