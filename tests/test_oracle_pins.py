@@ -635,3 +635,41 @@ def test_token_attention_all_tokens_equals_chunk_attention(oracle_lib, synth_lib
     got, wgot = oracle_lib.gather_attend(q, kv, ids, ctx, Hkv, 0.125, want_weights=True, tok=perm)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(wgot, wref, rtol=1e-12, atol=1e-15)
+
+
+_THREADS_CHILD = r"""
+import sys
+sys.path.insert(0, {root!r})
+import numpy as np
+import oracle
+rng = np.random.default_rng(11)
+keys = rng.integers(-3, 4, size=(3, 3000)).astype(np.int64)
+sc = rng.integers(-2, 3, size=(2, 40 * 64)).astype(np.float32)
+ids = np.stack([np.sort(rng.choice(200, 40, replace=False)) for _ in range(2)]).astype(np.int32)
+ctx = np.array([200 * 64, int(ids[1, 30]) * 64 + 9], dtype=np.int32)
+t_ids, t_cnt = oracle.threshold_chunks(keys, 700, 1)
+tok, tc = oracle.topk_tokens(sc, ids, ctx, 900)
+np.savez({out!r}, topk=oracle.topk_chunks(keys, 1000), t_ids=t_ids, t_cnt=t_cnt, tok=tok, tc=tc)
+"""
+
+
+@pytest.mark.parametrize("threads", [1, 3])
+def test_selections_do_not_depend_on_thread_count(tmp_path, threads):
+    """The selections count ranks in parallel iterations: one thread, three
+    threads and the default give the same lists on tie-heavy rows."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = {}
+    for name, env_threads in (("default", None), ("set", str(threads))):
+        out = tmp_path / f"{name}.npz"
+        env = dict(os.environ)
+        env.pop("OMP_NUM_THREADS", None)
+        if env_threads:
+            env["OMP_NUM_THREADS"] = env_threads
+        r = subprocess.run([sys.executable, "-c", _THREADS_CHILD.format(root=root, out=str(out))], env=env,
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        outs[name] = np.load(out)
+    for key in ("topk", "t_ids", "t_cnt", "tok", "tc"):
+        assert np.array_equal(outs["default"][key], outs["set"][key]), key
