@@ -9,7 +9,12 @@
     pass only (hipcc -Xarch_host); the device code is built as usual but not
     run: no GPU is used.
 
-Any sanitizer report aborts the program (-fno-sanitize-recover=all)."""
+  * The staged fetch's host gather threads (fetch_staged.hip), driven by
+    tests/c/sanitize_host_pool.cpp under ThreadSanitizer and, separately,
+    AddressSanitizer with UndefinedBehaviorSanitizer.
+
+Any sanitizer report aborts the program (-fno-sanitize-recover=all;
+ThreadSanitizer: halt_on_error)."""
 import concurrent.futures
 import os
 import shutil
@@ -64,3 +69,31 @@ def test_abi_host_side_under_sanitizers(tmp_path):
     r = _run(exe, {"ASAN_OPTIONS": "detect_leaks=0"})
     assert r.returncode == 0, r.stdout + r.stderr[-4000:]
     assert "sanitize_abi: ok" in r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc")
+@pytest.mark.parametrize("kind", ["thread", "address"])
+def test_staged_fetch_host_threads_under_sanitizers(tmp_path, kind):
+    """The staged fetch's host gather threads (fetch_staged.hip: the worker
+    pool and its non-temporal chunk copies), driven by
+    tests/c/sanitize_host_pool.cpp: ThreadSanitizer for the pool's hand-off
+    and its callers on several threads; AddressSanitizer and
+    UndefinedBehaviorSanitizer for the copies.  No GPU is used."""
+    import lookahead_chunk_sparse_amd.build as B
+
+    san = ["-fsanitize=thread"] if kind == "thread" else SAN
+    host_san = [f for flag in san for f in ("-Xarch_host", flag)]
+    flags = [*B.DEVICE_FLAGS, "-O1", "-g", *host_san]
+    sources = [os.path.join(CSRC, "fetch_staged.hip"), os.path.join(ROOT, "tests", "c", "sanitize_host_pool.cpp")]
+    objs = [str(tmp_path / f"{i}.o") for i in range(len(sources))]
+    for src, obj in zip(sources, objs):
+        r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-4000:]
+    exe = tmp_path / f"sanitize_host_pool_{kind}"
+    r = subprocess.run([HIPCC, *flags, *objs, "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    env = {"TSAN_OPTIONS": "halt_on_error=1:second_deadlock_stack=1"} if kind == "thread" else \
+        {"ASAN_OPTIONS": "detect_leaks=0"}
+    r = _run(exe, env)
+    assert r.returncode == 0, r.stdout + r.stderr[-4000:]
+    assert "sanitize_host_pool: ok" in r.stdout
